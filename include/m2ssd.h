@@ -1,0 +1,232 @@
+/*
+ * m2ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 mixer-core prefill library.
+ *
+ * The library runs the prefill hot path of one Mamba-2 (SSD) layer of a
+ * Nemotron-H model on one GPU:
+ *   1. causal depthwise conv1d (width 4) + SiLU over the carried conv state
+ *      followed by the new rows ("add_short_conv_rows", page "perf(nemotron_h):
+ *      prefill single-GPU prompts in multi-token chunks", section
+ *      Implementation; "conv1d(xBC) -> SiLU", page "Nemotron-H", section 3);
+ *   2. the chunked selective scan with no sequential step inside a chunk:
+ *      a_t = dt_t * A_h, gamma = inclusive cumulative sum of a over the chunk,
+ *      chunk total gamma_S = the LAST element of that sum, every exponent
+ *      clamped at 0 (same page, section Implementation), with the recurrent
+ *      state carried across chunks and across calls (page "Nemotron-H",
+ *      section 4.1 "Mamba2 SSM layer" gives the token recurrence it equals);
+ *   3. the grouped gated RMSNorm with z (page "Nemotron-H", section 4.1:
+ *      GroupRMSNorm(y, ssm_norm.weight), then the SiLU(z) gate; the NemotronH
+ *      decode page names the op RmsNormGatedGroup(n_groups)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is DEVICE memory owned by the caller, except where
+ *   stated.  The library never frees or retains caller memory and performs no
+ *   allocation on the hot path; scratch memory is the caller's `workspace`.
+ * - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *   null stream).  A call returns after enqueueing.
+ * - Matrices are row-major.  `ld_*` arguments are row strides in ELEMENTS; the
+ *   inner (channel) stride is always 1.  Activations (x, B, C, z, xBC) are
+ *   M2_F32 or M2_BF16 as given by `act_dtype` / `*_dtype`; dt, A, D, weights
+ *   and both recurrent states are always fp32 (a state held in bf16 would be
+ *   silently halved; the ABI rejects nothing else because it takes no state
+ *   dtype argument).
+ * - Varlen batches are packed: sequence b owns rows cu_seqlens[b] ..
+ *   cu_seqlens[b+1]-1 of every token-indexed array.  cu_seqlens is int32
+ *   [batch+1] in device memory, non-decreasing, cu_seqlens[0] == 0,
+ *   cu_seqlens[batch] == total_tokens, and no sequence is longer than
+ *   max_seqlen (a host value).  Empty sequences are allowed.
+ * - Recurrent states live in caller pools indexed by slot:
+ *     conv_state [n_slots, width-1, conv_dim] fp32, row j = the raw xBC input
+ *       that is (width-1-j) steps older than the next new row (oldest first);
+ *     ssm_state  [n_slots, nheads, headdim, dstate] fp32 (dstate fastest).
+ *   Sequence b uses slot state_idx[b] (int32 device array; NULL = slot b).
+ *   Slots used in one call must be distinct.  has_init[b] (uint8 device
+ *   array; NULL = all 1) == 0 makes sequence b start from zero states.
+ *   States are ADVANCED IN PLACE: after the call slot state_idx[b] holds the
+ *   state after the last row of sequence b.  If a call fails after launch
+ *   (M2_ERR_HIP) the states are unspecified; callers that need retry keep a
+ *   copy (the recurrent state cannot be rewound).
+ * - Argument errors are detected on the host before any launch; the call then
+ *   returns a negative status and has no side effects.  m2_last_error()
+ *   returns a thread-local message for the last failing call on this thread.
+ * - Device-side contents (cu_seqlens, state_idx, has_init, dt >= 0, A <= 0)
+ *   are not read by the host; violating their contracts gives unspecified
+ *   results but never out-of-bounds access for cu_seqlens within
+ *   [0, total_tokens] and state_idx within [0, n_slots).
+ * - Results are deterministic: equal inputs give bitwise-equal outputs.
+ */
+#ifndef M2SSD_H
+#define M2SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (negative on failure). */
+#define M2_OK               0
+#define M2_ERR_NULL        -1   /* a required pointer is NULL */
+#define M2_ERR_SHAPE       -2   /* a dimension is non-positive or inconsistent */
+#define M2_ERR_DTYPE       -3   /* dtype code not in {M2_F32, M2_BF16} */
+#define M2_ERR_CHUNK       -4   /* chunk_size not a multiple of 16 in [16, 128] */
+#define M2_ERR_STRIDE      -5   /* a row stride is smaller than the row width */
+#define M2_ERR_ALIGN       -6   /* a pointer or stride breaks 16-byte row alignment */
+#define M2_ERR_UNSUPPORTED -7   /* (headdim, dstate) or width has no compiled kernel */
+#define M2_ERR_WORKSPACE   -8   /* workspace NULL or smaller than the query returned */
+#define M2_ERR_HIP         -9   /* a HIP runtime call or kernel launch failed */
+
+/* Activation / output element types. */
+#define M2_F32   0
+#define M2_BF16  1
+
+/* Thread-local message describing the last failing call on this thread ("" if none). */
+const char* m2_last_error(void);
+
+/* Library version string (static storage). */
+const char* m2_version(void);
+
+/*
+ * mamba2_conv_rows -- causal depthwise conv1d (+ optional SiLU) over the xBC
+ * stream of a packed varlen batch, advancing the conv state in place.
+ *
+ * For sequence b of length L with padded stream xpad = [conv_state[slot] (width-1
+ * rows, or zeros if has_init[b]==0) ; the L new rows]:
+ *   out[t, c]  = act(conv_b[c] + sum_{k<width} conv_w[c, k] * xpad[t + k, c])
+ *   new state  = the last width-1 rows of xpad (so for L < width-1 the old rows
+ *                shift and are kept).
+ * Weight column width-1 multiplies the current row.
+ *
+ * The conv_dim input channels come in three row-strided segments, in order:
+ *   x [T, d_x] (ld_x), B [T, d_b] (ld_B), C [T, d_b] (ld_C), conv_dim = d_x + 2*d_b.
+ * They may be views into one in-projection row (e.g. B == x + d_x, C == B + d_b).
+ * Pass d_b = 0 (B, C ignored) to convolve a single segment of d_x channels.
+ *
+ *   act_dtype    element type of x, B, C (M2_F32 / M2_BF16)
+ *   conv_w       [conv_dim, width] fp32;  conv_b [conv_dim] fp32 or NULL (0)
+ *   width        must be 4
+ *   conv_state   [n_slots, width-1, conv_dim] fp32, read and advanced in place
+ *   apply_silu   nonzero: act = SiLU, zero: identity
+ *   out          [T, conv_dim] with row stride ld_out, element type out_dtype;
+ *                must not overlap the inputs or the state.
+ * Alignment: every pointer 16-byte aligned; row strides times element size
+ * multiples of 16 bytes; d_x and d_b multiples of 8.
+ */
+int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
+                     const void* C, int64_t ld_C, int d_x, int d_b, int act_dtype,
+                     const float* conv_w, const float* conv_b, int width,
+                     float* conv_state, int n_slots,
+                     const int32_t* cu_seqlens, int batch, int64_t total_tokens,
+                     int max_seqlen, const int32_t* state_idx, const uint8_t* has_init,
+                     int apply_silu, void* out, int64_t ld_out, int out_dtype,
+                     void* stream);
+
+/*
+ * ssd_chunk_scan -- chunked selective scan (Mamba-2 SSD) of a packed varlen
+ * batch, from post-conv x, B, C; writes the pre-norm output and advances the
+ * SSM state in place.
+ *
+ * Per sequence, per head h (group g = h / (nheads/ngroups)), in chunks of
+ * chunk_size rows counted from the sequence's first row, with
+ * a_t = dt[t,h] * A[h], gamma_t the inclusive cumulative sum of a over the
+ * chunk, gamma_S its last element and e(v) = exp(min(v, 0)):
+ *   y[t,h,:] = e(gamma_t) * C_t . h_in
+ *              + sum_{i<=t} e(gamma_t - gamma_i) * (C_t . B_i) * dt_i * x_i
+ *              + D[h] * x_t
+ *   h_out    = e(gamma_S) * h_in + sum_i e(gamma_S - gamma_i) * dt_i * x_i (outer) B_i
+ * which equals the token recurrence h <- exp(dt*A) h + dt x (outer) B,
+ * y = h . C + D x up to rounding.
+ *
+ *   x   [T, nheads*headdim] (ld_x);  B, C [T, ngroups*dstate] (ld_B, ld_C);
+ *       element type act_dtype.
+ *   dt  [T, nheads] fp32 (ld_dt), the final step size (softplus and bias
+ *       already applied), expected >= 0;  A [nheads] fp32, expected <= 0;
+ *   D   [nheads] fp32 or NULL (0).
+ *   ssm_state [n_slots, nheads, headdim, dstate] fp32, read and advanced in place.
+ *   y   [T, nheads*headdim] fp32 (ld_y), must not overlap any input.
+ *   chunk_size: multiple of 16 in [16, 128].
+ * Supported (headdim, dstate): (16,16), (32,64), (64,64), (64,128).
+ * Arithmetic: fp32 inputs use fp32 matrix instructions; bf16 inputs use bf16
+ * matrix instructions on a two-term (high, low) bf16 split of every fp32
+ * operand (three products per tile), fp32 accumulation, fp64 cumulative sums
+ * and exponent differences.
+ */
+int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
+                   const void* C, int64_t ld_C, int act_dtype,
+                   const float* dt, int64_t ld_dt, const float* A, const float* D,
+                   float* ssm_state, int n_slots,
+                   const int32_t* cu_seqlens, int batch, int64_t total_tokens,
+                   int max_seqlen, const int32_t* state_idx, const uint8_t* has_init,
+                   int nheads, int headdim, int dstate, int ngroups, int chunk_size,
+                   float* y, int64_t ld_y, void* stream);
+
+/*
+ * gated_rmsnorm_group -- grouped RMSNorm with the SiLU(z) gate.
+ *
+ * Per token t and group j (channels j*d_inner/ngroups .. (j+1)*d_inner/ngroups-1):
+ *   norm_before_gate != 0:  out = y / sqrt(mean_j(y^2) + eps) * w * silu(z)
+ *   norm_before_gate == 0:  v = y * silu(z);  out = v / sqrt(mean_j(v^2) + eps) * w
+ *   y  [T, d_inner] fp32 (ld_y);  z [T, d_inner] (ld_z, z_dtype);
+ *   norm_w [d_inner] fp32;  out [T, d_inner] (ld_out, out_dtype).
+ * out may alias y exactly (same pointer and stride) for an in-place update.
+ * d_inner / ngroups must be a multiple of 64 and at most 2048.
+ */
+int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_z,
+                        int z_dtype, const float* norm_w, float eps, int ngroups,
+                        int norm_before_gate, int64_t total_tokens, int d_inner,
+                        void* out, int64_t ld_out, int out_dtype, void* stream);
+
+/*
+ * Bytes of device workspace mamba2_prefill needs for these sizes (0 on bad
+ * arguments).  The workspace holds the post-conv activations of the batch.
+ */
+size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
+                                     int nheads, int headdim, int dstate, int ngroups,
+                                     int chunk_size);
+
+/*
+ * mamba2_prefill -- the whole mixer core of one layer for a packed varlen batch:
+ * conv (+SiLU) over [conv_state ; rows] of x | B | C, the chunked scan with
+ * carried ssm_state, the D skip and the grouped gated RMSNorm with z.
+ * Arguments mean what they mean for the three calls above; additionally
+ *   z [T, nheads*headdim] (ld_z) of act_dtype;
+ *   conv_w [conv_dim, 4], conv_b [conv_dim] or NULL, norm_w [nheads*headdim];
+ *   y [T, nheads*headdim] (ld_y), element type y_dtype (fp32 recommended:
+ *     a bf16 output alone carries a relative rounding of 2^-9);
+ *   workspace: device memory of at least mamba2_prefill_workspace_size() bytes,
+ *     16-byte aligned (NULL allowed when that size is 0).
+ * Both states are advanced in place.
+ */
+int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
+                   const void* C, int64_t ld_C, const void* z, int64_t ld_z, int act_dtype,
+                   const float* dt, int64_t ld_dt, const float* A, const float* D,
+                   const float* conv_w, const float* conv_b, const float* norm_w,
+                   float eps, int norm_before_gate,
+                   float* conv_state, float* ssm_state, int n_slots,
+                   const int32_t* cu_seqlens, int batch, int64_t total_tokens,
+                   int max_seqlen, const int32_t* state_idx, const uint8_t* has_init,
+                   int nheads, int headdim, int dstate, int ngroups, int chunk_size,
+                   void* y, int64_t ld_y, int y_dtype,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Launch counters (process-wide, atomic): which kernels ran, per instantiation. */
+typedef struct {
+    uint64_t conv_launches;        /* conv kernel launches */
+    uint64_t conv_state_launches;  /* conv-state update launches */
+    uint64_t scan_f32_launches;    /* scan launches, fp32 matrix path */
+    uint64_t scan_bf16x3_launches; /* scan launches, split-bf16 matrix path */
+    uint64_t norm_launches;        /* gated norm launches */
+    uint64_t prefill_calls;        /* successful mamba2_prefill calls */
+} m2_counters;
+
+/* Copy the counters into *out (M2_ERR_NULL if out is NULL). */
+int m2_get_counters(m2_counters* out);
+/* Zero the counters. */
+void m2_reset_counters(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M2SSD_H */

@@ -1,0 +1,15 @@
+"""CPU oracle of the Mamba-2 mixer-core prefill (fp64, plain and slow).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__
+and the bench's CPU-baseline leg may import this package.  It shares no
+code with the HIP library (mamba_ssd_selective_amd) and never imports it.
+
+  recurrence  -- token-by-token definition: conv + SiLU, selective-state
+                 recurrence, grouped gated RMSNorm, varlen batch driver.
+  chunked     -- closed-form chunked evaluation (exponent checks, clamp) and
+                 the materialised quadratic form, used to pin the recurrence.
+
+Every function is pinned by a CPU test (tests/test_oracle_pins.py) against a
+closed form, an invariant, a library routine or a hand-derived fixture.
+"""
+from . import recurrence, chunked  # noqa: F401
