@@ -170,7 +170,7 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
  *   y  [T, d_inner] fp32 (ld_y);  z [T, d_inner] (ld_z, z_dtype);
  *   norm_w [d_inner] fp32;  out [T, d_inner] (ld_out, out_dtype).
  * out may alias y exactly (same pointer and stride) for an in-place update.
- * d_inner / ngroups must be a multiple of 64 and at most 2048.
+ * The group width d_inner / ngroups must be at most 2048.
  */
 int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_z,
                         int z_dtype, const float* norm_w, float eps, int ngroups,
@@ -224,6 +224,26 @@ typedef struct {
 int m2_get_counters(m2_counters* out);
 /* Zero the counters. */
 void m2_reset_counters(void);
+
+/*
+ * Kernel timing of mamba2_prefill with HIP events on the caller's stream.
+ * m2_timing_enable(n) with n > 0 creates n event sets (host-side HIP objects,
+ * no device allocation) and makes each following mamba2_prefill call record
+ * events between its kernel launches, up to n calls; n == 0 stops recording.
+ * m2_timing_read() waits for the recorded events, returns the summed kernel
+ * times and the number of recorded calls, and rewinds the recorder.
+ * Not thread-safe: one timing session per process.
+ */
+typedef struct {
+    double conv_ms;        /* conv kernel */
+    double conv_state_ms;  /* conv-state update */
+    double scan_ms;        /* chunked scan */
+    double norm_ms;        /* gated norm */
+    uint64_t calls;        /* recorded prefill calls */
+} m2_kernel_times;
+
+int m2_timing_enable(int max_calls);
+int m2_timing_read(m2_kernel_times* out);
 
 #ifdef __cplusplus
 }

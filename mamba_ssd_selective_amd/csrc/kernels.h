@@ -1,0 +1,77 @@
+// Internal host-side interface between the C ABI layer (m2ssd_api.cpp) and the
+// kernel translation units.  Argument validation happens in the API layer; the
+// launchers assume valid, supported arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// Matrix-core arithmetic of the scan: fp32 products, or bf16 products on a
+// (high, low) split of each fp32 operand.
+enum Policy : int { kPolicyF32 = 0, kPolicyBf16x3 = 1 };
+
+struct ConvArgs {
+    const void* seg_ptr[3];     // x, B, C segments
+    int64_t seg_ld[3];          // row strides (elements)
+    int seg_ch[3];              // channels per segment
+    int nseg;
+    int act_dtype;
+    const float* conv_w;        // [conv_dim, 4]
+    const float* conv_b;        // [conv_dim] or null
+    int conv_dim;
+    float* conv_state;          // [n_slots, 3, conv_dim]
+    const int32_t* cu_seqlens;  // [batch+1]
+    int batch;
+    int64_t total_tokens;
+    const int32_t* state_idx;   // [batch] or null
+    const uint8_t* has_init;    // [batch] or null
+    int apply_silu;
+    void* out;
+    int64_t ld_out;
+    int out_dtype;
+};
+
+struct ScanArgs {
+    const void* x; int64_t ld_x;
+    const void* B; int64_t ld_B;
+    const void* C; int64_t ld_C;
+    int act_dtype;              // storage type of x, B, C
+    int policy;                 // Policy
+    const float* dt; int64_t ld_dt;
+    const float* A;
+    const float* D;             // or null
+    float* ssm_state;           // [n_slots, H, P, N]
+    const int32_t* cu_seqlens;
+    int batch;
+    const int32_t* state_idx;
+    const uint8_t* has_init;
+    int nheads, headdim, dstate, ngroups, chunk;
+    float* y; int64_t ld_y;
+};
+
+struct NormArgs {
+    const float* y; int64_t ld_y;
+    const void* z; int64_t ld_z; int z_dtype;
+    const float* norm_w;
+    float eps;
+    int ngroups;
+    int norm_before_gate;
+    int64_t total_tokens;
+    int d_inner;
+    void* out; int64_t ld_out; int out_dtype;
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
+hipError_t launch_conv_rows(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_state_update(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_gated_norm(const NormArgs& a, hipStream_t stream);
+
+// True when a scan kernel is compiled for this (headdim, dstate).
+bool scan_supported(int headdim, int dstate);
+
+}  // namespace m2

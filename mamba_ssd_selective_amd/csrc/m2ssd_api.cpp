@@ -1,0 +1,420 @@
+// C ABI of the Mamba-2 mixer-core prefill library: argument validation (all of
+// it on the host, before any launch), dispatch to the kernel launchers, the
+// fused prefill chain, launch counters and the thread-local error message.
+// The operations are defined in include/m2ssd.h.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/m2ssd.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Counters {
+    std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f32{0}, scan_bf16x3{0}, norm{0}, prefill{0};
+} g_counters;
+
+// Event recorder for m2_timing_*: set k holds 5 events around the 4 launches of call k.
+struct Timing {
+    std::vector<hipEvent_t> ev;
+    int max_calls = 0;
+    int used = 0;
+    hipEvent_t* next() {  // event set for the next prefill call, or null when off / full
+        if (used >= max_calls) return nullptr;
+        return &ev[5 * used++];
+    }
+} g_timing;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return M2_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int elem_size(int dtype) { return dtype == M2_BF16 ? 2 : 4; }
+bool valid_dtype(int d) { return d == M2_F32 || d == M2_BF16; }
+
+// Debug checks of device-side index arrays, enabled per call by M2SSD_DEBUG=1.
+bool debug_enabled() {
+    const char* e = std::getenv("M2SSD_DEBUG");
+    return e && e[0] == '1';
+}
+
+int debug_check_indices(const int32_t* cu, int batch, int64_t total, int max_seqlen,
+                        const int32_t* idx, int n_slots) {
+    std::vector<int32_t> hcu(batch + 1), hidx;
+    if (hipMemcpy(hcu.data(), cu, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(M2_ERR_HIP, "debug: reading cu_seqlens failed");
+    if (hcu[0] != 0 || hcu[batch] != total)
+        return fail(M2_ERR_SHAPE, "debug: cu_seqlens must start at 0 and end at total_tokens=%lld",
+                    (long long)total);
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = (int64_t)hcu[b + 1] - hcu[b];
+        if (L < 0 || L > max_seqlen)
+            return fail(M2_ERR_SHAPE, "debug: sequence %d has length %lld (max_seqlen %d)", b,
+                        (long long)L, max_seqlen);
+    }
+    if (idx) {
+        hidx.resize(batch);
+        if (hipMemcpy(hidx.data(), idx, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
+            return fail(M2_ERR_HIP, "debug: reading state_idx failed");
+        std::vector<char> seen(n_slots, 0);
+        for (int b = 0; b < batch; ++b) {
+            if (hidx[b] < 0 || hidx[b] >= n_slots)
+                return fail(M2_ERR_SHAPE, "debug: state_idx[%d]=%d outside [0, %d)", b, hidx[b], n_slots);
+            if (seen[hidx[b]]++)
+                return fail(M2_ERR_SHAPE, "debug: state_idx[%d]=%d repeats a slot", b, hidx[b]);
+        }
+    }
+    return M2_OK;
+}
+
+int check_batch(const int32_t* cu, int batch, int64_t total, int max_seqlen, const int32_t* idx,
+                int n_slots) {
+    if (!cu) return fail(M2_ERR_NULL, "cu_seqlens is NULL");
+    if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive (got %d)", batch);
+    if (total < 0 || max_seqlen < 0) return fail(M2_ERR_SHAPE, "total_tokens and max_seqlen must be >= 0");
+    if ((int64_t)max_seqlen * batch < total)
+        return fail(M2_ERR_SHAPE, "total_tokens %lld exceeds batch * max_seqlen", (long long)total);
+    if (total > ((int64_t)1 << 31) - 1) return fail(M2_ERR_SHAPE, "total_tokens must fit in int32");
+    if (n_slots <= 0) return fail(M2_ERR_SHAPE, "n_slots must be positive");
+    if (!idx && n_slots < batch) return fail(M2_ERR_SHAPE, "state_idx NULL needs n_slots >= batch");
+    if (debug_enabled()) return debug_check_indices(cu, batch, total, max_seqlen, idx, n_slots);
+    return M2_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(M2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return M2_OK;
+}
+
+// ---- per-operation validation (no side effects) ----
+
+int validate_conv(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                  int64_t ld_C, int d_x, int d_b, int act_dtype, const float* conv_w,
+                  const float* conv_b, int width, float* conv_state, int n_slots,
+                  const int32_t* cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
+                  const int32_t* state_idx, const void* out, int64_t ld_out, int out_dtype) {
+    if (!x || !conv_w || !conv_state || !out) return fail(M2_ERR_NULL, "conv: x, conv_w, conv_state and out are required");
+    if (d_b > 0 && (!B || !C)) return fail(M2_ERR_NULL, "conv: B and C are required when d_b > 0");
+    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype)) return fail(M2_ERR_DTYPE, "conv: dtype must be M2_F32 or M2_BF16");
+    if (width != 4) return fail(M2_ERR_UNSUPPORTED, "conv: width must be 4 (got %d)", width);
+    if (d_x <= 0 || d_b < 0 || d_x % 8 || d_b % 8)
+        return fail(M2_ERR_SHAPE, "conv: d_x > 0 and d_b >= 0 must be multiples of 8 (got %d, %d)", d_x, d_b);
+    const int conv_dim = d_x + 2 * d_b;
+    if (ld_x < d_x || (d_b > 0 && (ld_B < d_b || ld_C < d_b)) || ld_out < conv_dim)
+        return fail(M2_ERR_STRIDE, "conv: a row stride is smaller than its row width");
+    const int es = elem_size(act_dtype);
+    if (!aligned16(x) || (d_b > 0 && (!aligned16(B) || !aligned16(C))) || !aligned16(out) ||
+        !aligned16(conv_w) || !aligned16(conv_state) || (conv_b && !aligned16(conv_b)))
+        return fail(M2_ERR_ALIGN, "conv: pointers must be 16-byte aligned");
+    if ((ld_x * es) % 16 || (d_b > 0 && ((ld_B * es) % 16 || (ld_C * es) % 16)) ||
+        (ld_out * elem_size(out_dtype)) % 16)
+        return fail(M2_ERR_ALIGN, "conv: row strides must be multiples of 16 bytes");
+    return check_batch(cu_seqlens, batch, total_tokens, max_seqlen, state_idx, n_slots);
+}
+
+int validate_scan_dims(int nheads, int headdim, int dstate, int ngroups, int chunk_size) {
+    if (nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return fail(M2_ERR_SHAPE, "scan: nheads, headdim, dstate, ngroups must be positive");
+    if (nheads % ngroups) return fail(M2_ERR_SHAPE, "scan: nheads %% ngroups != 0 (%d, %d)", nheads, ngroups);
+    if (chunk_size < 16 || chunk_size > 128 || chunk_size % 16)
+        return fail(M2_ERR_CHUNK, "chunk_size must be a multiple of 16 in [16, 128] (got %d)", chunk_size);
+    if (!m2::scan_supported(headdim, dstate))
+        return fail(M2_ERR_UNSUPPORTED, "no scan kernel for headdim=%d dstate=%d", headdim, dstate);
+    return M2_OK;
+}
+
+int validate_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                  int64_t ld_C, int act_dtype, const float* dt, int64_t ld_dt, const float* A,
+                  const float* D, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
+                  int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                  int nheads, int headdim, int dstate, int ngroups, int chunk_size,
+                  const float* y, int64_t ld_y) {
+    (void)D;
+    if (!x || !B || !C || !dt || !A || !ssm_state || !y)
+        return fail(M2_ERR_NULL, "scan: x, B, C, dt, A, ssm_state and y are required");
+    if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "scan: act_dtype must be M2_F32 or M2_BF16");
+    int st = validate_scan_dims(nheads, headdim, dstate, ngroups, chunk_size);
+    if (st) return st;
+    const int64_t di = (int64_t)nheads * headdim, gn = (int64_t)ngroups * dstate;
+    if (ld_x < di || ld_B < gn || ld_C < gn || ld_dt < nheads || ld_y < di)
+        return fail(M2_ERR_STRIDE, "scan: a row stride is smaller than its row width");
+    const int es = elem_size(act_dtype);
+    if (!aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(ssm_state))
+        return fail(M2_ERR_ALIGN, "scan: B, C, y and ssm_state must be 16-byte aligned");
+    if ((ld_B * es) % 16 || (ld_C * es) % 16 || (ld_y * 4) % 16)
+        return fail(M2_ERR_ALIGN, "scan: ld_B, ld_C and ld_y must be multiples of 16 bytes");
+    return check_batch(cu_seqlens, batch, total_tokens, max_seqlen, state_idx, n_slots);
+}
+
+int validate_norm(const float* y, int64_t ld_y, const void* z, int64_t ld_z, int z_dtype,
+                  const float* norm_w, int ngroups, int64_t total_tokens, int d_inner,
+                  const void* out, int64_t ld_out, int out_dtype) {
+    if (!y || !z || !norm_w || !out) return fail(M2_ERR_NULL, "norm: y, z, norm_w and out are required");
+    if (!valid_dtype(z_dtype) || !valid_dtype(out_dtype)) return fail(M2_ERR_DTYPE, "norm: dtype must be M2_F32 or M2_BF16");
+    if (d_inner <= 0 || ngroups <= 0 || d_inner % ngroups || total_tokens < 0)
+        return fail(M2_ERR_SHAPE, "norm: need d_inner > 0 divisible by ngroups > 0, total_tokens >= 0");
+    if (d_inner / ngroups > 2048) return fail(M2_ERR_UNSUPPORTED, "norm: group width above 2048");
+    if (ld_y < d_inner || ld_z < d_inner || ld_out < d_inner)
+        return fail(M2_ERR_STRIDE, "norm: a row stride is smaller than d_inner");
+    if (static_cast<const void*>(y) == out && (ld_out != ld_y || out_dtype != M2_F32))
+        return fail(M2_ERR_STRIDE, "norm: in-place use needs out == y with the same stride and fp32 output");
+    return M2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* m2_last_error(void) { return g_last_error.c_str(); }
+
+const char* m2_version(void) { return "m2ssd 0.1 (gfx950)"; }
+
+int m2_get_counters(m2_counters* out) {
+    if (!out) return fail(M2_ERR_NULL, "m2_get_counters: out is NULL");
+    out->conv_launches = g_counters.conv.load();
+    out->conv_state_launches = g_counters.conv_state.load();
+    out->scan_f32_launches = g_counters.scan_f32.load();
+    out->scan_bf16x3_launches = g_counters.scan_bf16x3.load();
+    out->norm_launches = g_counters.norm.load();
+    out->prefill_calls = g_counters.prefill.load();
+    return ok();
+}
+
+void m2_reset_counters(void) {
+    g_counters.conv = 0;
+    g_counters.conv_state = 0;
+    g_counters.scan_f32 = 0;
+    g_counters.scan_bf16x3 = 0;
+    g_counters.norm = 0;
+    g_counters.prefill = 0;
+}
+
+int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                     int64_t ld_C, int d_x, int d_b, int act_dtype, const float* conv_w,
+                     const float* conv_b, int width, float* conv_state, int n_slots,
+                     const int32_t* cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
+                     const int32_t* state_idx, const uint8_t* has_init, int apply_silu, void* out,
+                     int64_t ld_out, int out_dtype, void* stream) {
+    int st = validate_conv(x, ld_x, B, ld_B, C, ld_C, d_x, d_b, act_dtype, conv_w, conv_b, width,
+                           conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
+                           state_idx, out, ld_out, out_dtype);
+    if (st) return st;
+    m2::ConvArgs a{};
+    a.seg_ptr[0] = x; a.seg_ld[0] = ld_x; a.seg_ch[0] = d_x;
+    a.seg_ptr[1] = B; a.seg_ld[1] = ld_B; a.seg_ch[1] = d_b;
+    a.seg_ptr[2] = C; a.seg_ld[2] = ld_C; a.seg_ch[2] = d_b;
+    a.nseg = d_b > 0 ? 3 : 1;
+    a.act_dtype = act_dtype;
+    a.conv_w = conv_w; a.conv_b = conv_b;
+    a.conv_dim = d_x + 2 * d_b;
+    a.conv_state = conv_state;
+    a.cu_seqlens = cu_seqlens; a.batch = batch; a.total_tokens = total_tokens;
+    a.state_idx = state_idx; a.has_init = has_init;
+    a.apply_silu = apply_silu; a.out = out; a.ld_out = ld_out; a.out_dtype = out_dtype;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (total_tokens > 0) {
+        if ((st = hip_status(m2::launch_conv_rows(a, s), "conv launch"))) return st;
+        g_counters.conv++;
+    }
+    if ((st = hip_status(m2::launch_conv_state_update(a, s), "conv state launch"))) return st;
+    g_counters.conv_state++;
+    return ok();
+}
+
+int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                   int64_t ld_C, int act_dtype, const float* dt, int64_t ld_dt, const float* A,
+                   const float* D, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
+                   int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                   const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                   int chunk_size, float* y, int64_t ld_y, void* stream) {
+    int st = validate_scan(x, ld_x, B, ld_B, C, ld_C, act_dtype, dt, ld_dt, A, D, ssm_state,
+                           n_slots, cu_seqlens, batch, total_tokens, max_seqlen, state_idx, nheads,
+                           headdim, dstate, ngroups, chunk_size, y, ld_y);
+    if (st) return st;
+    m2::ScanArgs a{};
+    a.x = x; a.ld_x = ld_x; a.B = B; a.ld_B = ld_B; a.C = C; a.ld_C = ld_C;
+    a.act_dtype = act_dtype; a.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF32;
+    a.dt = dt; a.ld_dt = ld_dt; a.A = A; a.D = D; a.ssm_state = ssm_state;
+    a.cu_seqlens = cu_seqlens; a.batch = batch; a.state_idx = state_idx; a.has_init = has_init;
+    a.nheads = nheads; a.headdim = headdim; a.dstate = dstate; a.ngroups = ngroups;
+    a.chunk = chunk_size; a.y = y; a.ld_y = ld_y;
+    if ((st = hip_status(m2::launch_ssd_scan(a, static_cast<hipStream_t>(stream)), "scan launch"))) return st;
+    (a.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f32)++;
+    return ok();
+}
+
+int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_z, int z_dtype,
+                        const float* norm_w, float eps, int ngroups, int norm_before_gate,
+                        int64_t total_tokens, int d_inner, void* out, int64_t ld_out,
+                        int out_dtype, void* stream) {
+    int st = validate_norm(y, ld_y, z, ld_z, z_dtype, norm_w, ngroups, total_tokens, d_inner, out,
+                           ld_out, out_dtype);
+    if (st) return st;
+    if (total_tokens == 0) return ok();
+    m2::NormArgs a{};
+    a.y = y; a.ld_y = ld_y; a.z = z; a.ld_z = ld_z; a.z_dtype = z_dtype; a.norm_w = norm_w;
+    a.eps = eps; a.ngroups = ngroups; a.norm_before_gate = norm_before_gate;
+    a.total_tokens = total_tokens; a.d_inner = d_inner; a.out = out; a.ld_out = ld_out;
+    a.out_dtype = out_dtype;
+    if ((st = hip_status(m2::launch_gated_norm(a, static_cast<hipStream_t>(stream)), "norm launch"))) return st;
+    g_counters.norm++;
+    return ok();
+}
+
+size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen, int nheads,
+                                     int headdim, int dstate, int ngroups, int chunk_size) {
+    (void)batch; (void)max_seqlen; (void)chunk_size;
+    if (total_tokens < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0) return 0;
+    const int64_t conv_dim = (int64_t)nheads * headdim + 2 * (int64_t)ngroups * dstate;
+    const int64_t di = (int64_t)nheads * headdim;
+    auto round256 = [](int64_t v) { return (v + 255) / 256 * 256; };
+    // post-conv activations (fp32) + pre-norm output (fp32, used when y is not fp32)
+    return (size_t)(round256(total_tokens * conv_dim * 4) + round256(total_tokens * di * 4));
+}
+
+int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                   int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
+                   int64_t ld_dt, const float* A, const float* D, const float* conv_w,
+                   const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
+                   float* conv_state, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
+                   int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                   const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                   int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
+                   size_t ws_bytes, void* stream) {
+    int st = validate_scan_dims(nheads, headdim, dstate, ngroups, chunk_size);
+    if (st) return st;
+    const int d_x = nheads * headdim, d_b = ngroups * dstate;
+    const int conv_dim = d_x + 2 * d_b;
+    if (!z || !norm_w || !y) return fail(M2_ERR_NULL, "prefill: z, norm_w and y are required");
+    if (!valid_dtype(y_dtype)) return fail(M2_ERR_DTYPE, "prefill: y_dtype must be M2_F32 or M2_BF16");
+    const size_t need = mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads,
+                                                      headdim, dstate, ngroups, chunk_size);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(M2_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (workspace && !aligned16(workspace)) return fail(M2_ERR_ALIGN, "prefill: workspace must be 16-byte aligned");
+    float* u = static_cast<float*>(workspace);
+    float* ypre_ws = u ? u + ((int64_t)total_tokens * conv_dim * 4 + 255) / 256 * 64 : nullptr;
+    if ((st = validate_conv(x, ld_x, B, ld_B, C, ld_C, d_x, d_b, act_dtype, conv_w, conv_b, 4,
+                            conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
+                            state_idx, u ? u : y, conv_dim, M2_F32)))
+        return st;
+    if (!dt || !A || !ssm_state) return fail(M2_ERR_NULL, "prefill: dt, A and ssm_state are required");
+    if (ld_dt < nheads) return fail(M2_ERR_STRIDE, "prefill: ld_dt < nheads");
+    if (!aligned16(ssm_state)) return fail(M2_ERR_ALIGN, "prefill: ssm_state must be 16-byte aligned");
+    if ((st = validate_norm(u ? u : static_cast<const float*>(y), d_x, z, ld_z, act_dtype, norm_w,
+                            ngroups, total_tokens, d_x, y, ld_y, y_dtype)))
+        return st;
+    if (y_dtype == M2_F32 && (ld_y * 4) % 16) return fail(M2_ERR_ALIGN, "prefill: ld_y must be a multiple of 16 bytes");
+    if (!aligned16(y)) return fail(M2_ERR_ALIGN, "prefill: y must be 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t* tev = g_timing.next();
+    auto mark = [&](int k) { if (tev) (void)hipEventRecord(tev[k], s); };
+    mark(0);
+    m2::ConvArgs ca{};
+    ca.seg_ptr[0] = x; ca.seg_ld[0] = ld_x; ca.seg_ch[0] = d_x;
+    ca.seg_ptr[1] = B; ca.seg_ld[1] = ld_B; ca.seg_ch[1] = d_b;
+    ca.seg_ptr[2] = C; ca.seg_ld[2] = ld_C; ca.seg_ch[2] = d_b;
+    ca.nseg = 3; ca.act_dtype = act_dtype; ca.conv_w = conv_w; ca.conv_b = conv_b;
+    ca.conv_dim = conv_dim; ca.conv_state = conv_state; ca.cu_seqlens = cu_seqlens;
+    ca.batch = batch; ca.total_tokens = total_tokens; ca.state_idx = state_idx;
+    ca.has_init = has_init; ca.apply_silu = 1; ca.out = u; ca.ld_out = conv_dim;
+    ca.out_dtype = M2_F32;
+    if (total_tokens > 0) {
+        if ((st = hip_status(m2::launch_conv_rows(ca, s), "prefill conv launch"))) return st;
+        g_counters.conv++;
+    }
+    mark(1);
+    if ((st = hip_status(m2::launch_conv_state_update(ca, s), "prefill conv state launch"))) return st;
+    g_counters.conv_state++;
+    mark(2);
+
+    float* ypre = (y_dtype == M2_F32) ? static_cast<float*>(y) : ypre_ws;
+    const int64_t ld_pre = (y_dtype == M2_F32) ? ld_y : d_x;
+    m2::ScanArgs sa{};
+    sa.x = u; sa.ld_x = conv_dim; sa.B = u + d_x; sa.ld_B = conv_dim;
+    sa.C = u + d_x + d_b; sa.ld_C = conv_dim; sa.act_dtype = M2_F32;
+    sa.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF32;
+    sa.dt = dt; sa.ld_dt = ld_dt; sa.A = A; sa.D = D; sa.ssm_state = ssm_state;
+    sa.cu_seqlens = cu_seqlens; sa.batch = batch; sa.state_idx = state_idx; sa.has_init = has_init;
+    sa.nheads = nheads; sa.headdim = headdim; sa.dstate = dstate; sa.ngroups = ngroups;
+    sa.chunk = chunk_size; sa.y = ypre; sa.ld_y = ld_pre;
+    if ((st = hip_status(m2::launch_ssd_scan(sa, s), "prefill scan launch"))) return st;
+    (sa.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f32)++;
+    mark(3);
+
+    if (total_tokens > 0) {
+        m2::NormArgs na{};
+        na.y = ypre; na.ld_y = ld_pre; na.z = z; na.ld_z = ld_z; na.z_dtype = act_dtype;
+        na.norm_w = norm_w; na.eps = eps; na.ngroups = ngroups; na.norm_before_gate = norm_before_gate;
+        na.total_tokens = total_tokens; na.d_inner = d_x; na.out = y; na.ld_out = ld_y;
+        na.out_dtype = y_dtype;
+        if ((st = hip_status(m2::launch_gated_norm(na, s), "prefill norm launch"))) return st;
+        g_counters.norm++;
+    }
+    mark(4);
+    g_counters.prefill++;
+    return ok();
+}
+
+int m2_timing_enable(int max_calls) {
+    if (max_calls < 0) return fail(M2_ERR_SHAPE, "m2_timing_enable: max_calls < 0");
+    for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+    g_timing.ev.clear();
+    g_timing.used = 0;
+    g_timing.max_calls = 0;
+    if (max_calls == 0) return ok();
+    g_timing.ev.resize((size_t)5 * max_calls);
+    for (auto& e : g_timing.ev) {
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            g_timing.ev.clear();
+            return fail(M2_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(r));
+        }
+    }
+    g_timing.max_calls = max_calls;
+    return ok();
+}
+
+int m2_timing_read(m2_kernel_times* out) {
+    if (!out) return fail(M2_ERR_NULL, "m2_timing_read: out is NULL");
+    *out = m2_kernel_times{};
+    double* dst[4] = {&out->conv_ms, &out->conv_state_ms, &out->scan_ms, &out->norm_ms};
+    for (int c = 0; c < g_timing.used; ++c) {
+        hipEvent_t* e = &g_timing.ev[5 * c];
+        const hipError_t r = hipEventSynchronize(e[4]);
+        if (r != hipSuccess) return fail(M2_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(r));
+        for (int k = 0; k < 4; ++k) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, e[k], e[k + 1]) != hipSuccess) ms = 0.f;
+            *dst[k] += ms;
+        }
+    }
+    out->calls = (uint64_t)g_timing.used;
+    g_timing.used = 0;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+"""Host-side checks of the C ABI (CPU only, no kernel runs): the library loads,
+exports every function include/m2ssd.h declares, and rejects bad arguments
+with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_selective_amd as m2
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "m2ssd.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mamba2_conv_rows", "ssd_chunk_scan", "gated_rmsnorm_group", "mamba2_prefill",
+              "mamba2_prefill_workspace_size", "m2_last_error", "m2_get_counters"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m2.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libm2ssd.so does not export {n}"
+
+
+def test_version_and_counters():
+    assert "gfx950" in m2.version()
+    m2.reset_counters()
+    assert all(v == 0 for v in m2.get_counters().values())
+
+
+def _scan(lib, **kw):
+    a = dict(x=16, ld_x=64, B=32, ld_B=32, C=48, ld_C=32, act=0, dt=64, ld_dt=4, A=80, D=None,
+             ss=96, n_slots=1, cu=112, batch=1, T=8, maxlen=8, idx=None, init=None,
+             H=4, P=16, N=16, G=2, chunk=16, y=128, ld_y=64)
+    a.update(kw)
+    return lib.ssd_chunk_scan(a["x"], a["ld_x"], a["B"], a["ld_B"], a["C"], a["ld_C"], a["act"],
+                              a["dt"], a["ld_dt"], a["A"], a["D"], a["ss"], a["n_slots"], a["cu"],
+                              a["batch"], a["T"], a["maxlen"], a["idx"], a["init"], a["H"],
+                              a["P"], a["N"], a["G"], a["chunk"], a["y"], a["ld_y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(act=7), -3), (dict(chunk=144), -4), (dict(chunk=24), -4),
+    (dict(chunk=0), -4), (dict(P=24), -7), (dict(G=3), -2), (dict(ld_x=10), -5),
+    (dict(ld_y=60), -5), (dict(B=40), -6), (dict(ld_B=34), -6), (dict(batch=0), -2),
+    (dict(T=100, maxlen=8), -2), (dict(n_slots=0), -2),
+])
+def test_scan_rejects_bad_arguments(kw, code):
+    """Validation happens on the host: the fake (aligned, never dereferenced) pointers are not touched."""
+    lib = m2.load()
+    assert _scan(lib, **kw) == code
+    assert lib.m2_last_error().decode() != ""
+
+
+def test_conv_and_norm_reject_bad_arguments():
+    lib = m2.load()
+    # width 5 is unsupported
+    assert lib.mamba2_conv_rows(16, 8, 32, 8, 48, 8, 8, 8, 0, 64, None, 5, 128, 1, 256, 1, 0, 0,
+                                None, None, 1, 512, 24, 0, None) == -7
+    # d_x not a multiple of 8
+    assert lib.mamba2_conv_rows(16, 12, 32, 8, 48, 8, 12, 8, 0, 64, None, 4, 128, 1, 256, 1, 0, 0,
+                                None, None, 1, 512, 28, 0, None) == -2
+    # norm: group width above 2048
+    assert lib.gated_rmsnorm_group(16, 4096, 32, 4096, 0, 64, 1e-5, 1, 1, 4, 4096, 128, 4096, 0,
+                                   None) == -7
+    # norm: in place with a different stride
+    assert lib.gated_rmsnorm_group(16, 64, 32, 64, 0, 64, 1e-5, 2, 1, 4, 64, 16, 128, 0, None) == -5
+
+
+def test_workspace_query_and_prefill_workspace_error():
+    lib = m2.load()
+    n = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128)
+    assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4
+    assert lib.mamba2_prefill_workspace_size(-1, 1, 1, 64, 64, 128, 8, 128) == 0

@@ -220,3 +220,35 @@ def small_shape_inputs(shape: LayerShape, seqlens: List[int], seed: int, act: st
     """Inputs for an ad-hoc shape (tests of ragged tails, group maps, edge cases)."""
     w = Workload("adhoc", shape, tuple(seqlens), act, init, dt_mode=dt_mode, n_slots=n_slots)
     return make_inputs(w, seed)
+
+
+def group_channels(shape: LayerShape, g: int):
+    """Heads, x/z channels and conv channels (x | B | C order) owned by SSM group g."""
+    hpg = shape.nheads // shape.ngroups
+    P, N = shape.headdim, shape.dstate
+    di, gn = shape.d_inner, shape.ngroups * shape.dstate
+    heads = np.arange(g * hpg, (g + 1) * hpg)
+    xch = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
+    bch = di + g * N + np.arange(N)
+    cch = di + gn + g * N + np.arange(N)
+    return heads, xch, np.concatenate([xch, bch, cch])
+
+
+def slice_group(inp: Dict[str, np.ndarray], shape: LayerShape, g: int):
+    """Inputs of the one-group problem (ngroups = 1, nheads = heads per group) for group g.
+
+    Groups never interact in the mixer core (each owns its heads, its B/C, x, z
+    and conv channels and its norm group), so this is an exact sub-problem."""
+    heads, xch, ch = group_channels(shape, g)
+    out = dict(inp)
+    out["xbc"] = inp["xbc"][:, ch]
+    out["z"] = inp["z"][:, xch]
+    out["dt"] = inp["dt"][:, heads]
+    out["A"] = inp["A"][heads]
+    out["D"] = inp["D"][heads]
+    out["conv_w"] = inp["conv_w"][ch]
+    out["conv_b"] = inp["conv_b"][ch]
+    out["norm_w"] = inp["norm_w"][xch]
+    out["conv_state"] = inp["conv_state"][:, :, ch]
+    out["ssm_state"] = inp["ssm_state"][:, heads]
+    return out, LayerShape(len(heads), shape.headdim, shape.dstate, 1, shape.width)
