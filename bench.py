@@ -158,7 +158,7 @@ def main():
     x, B, C = xbc[:, :di], xbc[:, di:di + gn], xbc[:, di + gn:]
     maxlen = 4096
     ws = torch.empty(m2.mamba2_prefill_workspace_size(T, nseq, maxlen, s.nheads, s.headdim, s.dstate,
-                                                      s.ngroups, w.chunk_size),
+                                                      s.ngroups, w.chunk_size, at),
                      dtype=torch.uint8, device=dev)
     y = torch.empty((T, di), dtype=torch.float32, device=dev)
 

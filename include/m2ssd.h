@@ -147,10 +147,11 @@ int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
  *   y   [T, nheads*headdim] fp32 (ld_y), must not overlap any input.
  *   chunk_size: multiple of 16 in [16, 128].
  * Supported (headdim, dstate): (16,16), (32,64), (64,64), (64,128).
- * Arithmetic: fp32 inputs use fp32 matrix instructions; bf16 inputs use bf16
- * matrix instructions on a two-term (high, low) bf16 split of every fp32
- * operand (three products per tile), fp32 accumulation, fp64 cumulative sums
- * and exponent differences.
+ * Arithmetic: bf16 inputs use bf16 matrix instructions on a two-term (high,
+ * low) bf16 split of every fp32 operand (three products per tile) with fp32
+ * accumulation; fp32 inputs are computed in fp64 (fp64 matrix instructions,
+ * chunks evaluated 64 rows at a time -- the same function of the inputs).
+ * Cumulative sums and exponent differences are fp64 on both paths.
  */
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                    const void* C, int64_t ld_C, int act_dtype,
@@ -178,12 +179,13 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
                         void* out, int64_t ld_out, int out_dtype, void* stream);
 
 /*
- * Bytes of device workspace mamba2_prefill needs for these sizes (0 on bad
- * arguments).  The workspace holds the post-conv activations of the batch.
+ * Bytes of device workspace mamba2_prefill needs for these sizes and this
+ * activation dtype (0 on bad arguments).  The workspace holds the post-conv
+ * activations of the batch and, when y is bf16, the pre-norm output.
  */
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
                                      int nheads, int headdim, int dstate, int ngroups,
-                                     int chunk_size);
+                                     int chunk_size, int act_dtype);
 
 /*
  * mamba2_prefill -- the whole mixer core of one layer for a packed varlen batch:
@@ -214,8 +216,8 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
 typedef struct {
     uint64_t conv_launches;        /* conv kernel launches */
     uint64_t conv_state_launches;  /* conv-state update launches */
-    uint64_t scan_f32_launches;    /* scan launches, fp32 matrix path */
-    uint64_t scan_bf16x3_launches; /* scan launches, split-bf16 matrix path */
+    uint64_t scan_f64_launches;    /* scan launches, fp64 matrix path (fp32 inputs) */
+    uint64_t scan_bf16x3_launches; /* scan launches, split-bf16 matrix path (bf16 inputs) */
     uint64_t norm_launches;        /* gated norm launches */
     uint64_t prefill_calls;        /* successful mamba2_prefill calls */
 } m2_counters;

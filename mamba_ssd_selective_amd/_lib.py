@@ -31,7 +31,7 @@ class M2Error(RuntimeError):
 
 class Counters(ctypes.Structure):
     _fields_ = [("conv_launches", ctypes.c_uint64), ("conv_state_launches", ctypes.c_uint64),
-                ("scan_f32_launches", ctypes.c_uint64), ("scan_bf16x3_launches", ctypes.c_uint64),
+                ("scan_f64_launches", ctypes.c_uint64), ("scan_bf16x3_launches", ctypes.c_uint64),
                 ("norm_launches", ctypes.c_uint64), ("prefill_calls", ctypes.c_uint64)]
 
 
@@ -58,7 +58,7 @@ _SIGS = {
     "ssd_chunk_scan": (_I, [_P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _I,
                             _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I, _P, _L, _P]),
     "gated_rmsnorm_group": (_I, [_P, _L, _P, _L, _I, _P, _F, _I, _I, _L, _I, _P, _L, _I, _P]),
-    "mamba2_prefill_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I]),
+    "mamba2_prefill_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I, _I]),
     "mamba2_prefill": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
                             _F, _I, _P, _P, _I, _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I,
                             _P, _L, _I, _P, ctypes.c_size_t, _P]),
@@ -232,9 +232,10 @@ def gated_rmsnorm_group(y, z, norm_w, ngroups, eps=1e-5, norm_before_gate=True, 
 
 
 def mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim, dstate,
-                                  ngroups, chunk_size=128) -> int:
+                                  ngroups, chunk_size=128, act_dtype=torch.bfloat16) -> int:
+    code = M2_BF16 if act_dtype == torch.bfloat16 else M2_F32
     return int(load().mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads,
-                                                    headdim, dstate, ngroups, chunk_size))
+                                                    headdim, dstate, ngroups, chunk_size, code))
 
 
 def mamba2_prefill(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
@@ -252,7 +253,7 @@ def mamba2_prefill(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm
     if y is None:
         y = torch.empty((T, nheads * headdim), dtype=y_dtype, device=x.device)
     need = mamba2_prefill_workspace_size(T, batch, max_seqlen, nheads, headdim, dstate,
-                                         ngroups, chunk_size)
+                                         ngroups, chunk_size, x.dtype)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     for t, n in ((A, "A"), (D, "D"), (conv_w, "conv_w"), (conv_b, "conv_b"), (norm_w, "norm_w"),

@@ -14,6 +14,8 @@
 // from the slot's conv state (or zeros) whenever its run enters a new sequence.
 // Weights and bias of its 8 channels stay in registers for the whole run.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,8 +41,10 @@ __device__ __forceinline__ const Tin* seg_row(const ConvArgs& a, int seg, int64_
     return static_cast<const Tin*>(a.seg_ptr[seg]) + row * a.seg_ld[seg] + cs;
 }
 
+// Computes in fp64 when the output is fp64 (the fp32-input prefill path), else fp32.
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
+    using T = typename std::conditional<std::is_same<Tout, double>::value, double, float>::type;
     const int c0 = (blockIdx.y * BLOCK + threadIdx.x) * CPT;   // first channel of this thread
     if (c0 >= a.conv_dim) return;
     const int64_t t0 = (int64_t)blockIdx.x * TOK;
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     int seg = 0, cs = c0;
     while (seg + 1 < a.nseg && cs >= a.seg_ch[seg]) { cs -= a.seg_ch[seg]; ++seg; }
 
-    float w[CPT][4], bias[CPT];
+    T w[CPT][4], bias[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const float4 wv = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)(c0 + c) * 4);
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     int b = seq_of(a.cu_seqlens, a.batch, t0);
     int64_t s0 = a.cu_seqlens[b];
     int64_t s1 = a.cu_seqlens[b + 1];
-    float win[3][CPT];   // raw rows t-3, t-2, t-1
+    T win[3][CPT];   // raw rows t-3, t-2, t-1
 
     auto fill_window = [&](int64_t t) {
         // rows t-3..t-1 of sequence b: from the stream if inside it, else from the state
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
             const int64_t j = (t - s0) - 3 + d;     // position of the needed row in the sequence
-            float v[CPT];
+            T v[CPT];
             if (j >= 0) {
                 load8(seg_row<Tin>(a, seg, s0 + j, cs), v);
             } else if (init) {
@@ -94,17 +98,17 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
             s1 = a.cu_seqlens[b + 1];
             fill_window(t);
         }
-        float cur[CPT];
+        T cur[CPT];
         load8(seg_row<Tin>(a, seg, t, cs), cur);
-        float o[CPT];
+        T o[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            float acc = bias[c];
-            acc = fmaf(w[c][0], win[0][c], acc);
-            acc = fmaf(w[c][1], win[1][c], acc);
-            acc = fmaf(w[c][2], win[2][c], acc);
-            acc = fmaf(w[c][3], cur[c], acc);
-            o[c] = a.apply_silu ? silu_f32(acc) : acc;
+            T acc = bias[c];
+            acc = fma(w[c][0], win[0][c], acc);
+            acc = fma(w[c][1], win[1][c], acc);
+            acc = fma(w[c][2], win[2][c], acc);
+            acc = fma(w[c][3], cur[c], acc);
+            o[c] = a.apply_silu ? silu(acc) : acc;
             win[0][c] = win[1][c];
             win[1][c] = win[2][c];
             win[2][c] = cur[c];
@@ -151,11 +155,15 @@ hipError_t launch_conv_rows(const ConvArgs& a, hipStream_t stream) {
     if (a.act_dtype == kBF16) {
         if (a.out_dtype == kBF16)
             hipLaunchKernelGGL((conv_rows_kernel<uint16_t, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
+        else if (a.out_dtype == kF64)
+            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, double>), grid, dim3(BLOCK), 0, stream, a);
         else
             hipLaunchKernelGGL((conv_rows_kernel<uint16_t, float>), grid, dim3(BLOCK), 0, stream, a);
     } else {
         if (a.out_dtype == kBF16)
             hipLaunchKernelGGL((conv_rows_kernel<float, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
+        else if (a.out_dtype == kF64)
+            hipLaunchKernelGGL((conv_rows_kernel<float, double>), grid, dim3(BLOCK), 0, stream, a);
         else
             hipLaunchKernelGGL((conv_rows_kernel<float, float>), grid, dim3(BLOCK), 0, stream, a);
     }

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(BLOCK) void gated_norm_kernel(NormArgs a) {
             float yv = 0.f, g = 0.f;
             if (c < gs) {
                 yv = yr[c];
-                g = silu_f32(Act<Tz>::load(zr + c));
+                g = silu(Act<Tz>::load(zr + c));
             }
             const float u = a.norm_before_gate ? yv : yv * g;
             v[k] = u;

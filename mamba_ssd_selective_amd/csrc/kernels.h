@@ -8,11 +8,12 @@
 
 namespace m2 {
 
-enum DType : int { kF32 = 0, kBF16 = 1 };
+// Element types; kF64 is internal (the fp32 path's post-conv workspace).
+enum DType : int { kF32 = 0, kBF16 = 1, kF64 = 2 };
 
-// Matrix-core arithmetic of the scan: fp32 products, or bf16 products on a
-// (high, low) split of each fp32 operand.
-enum Policy : int { kPolicyF32 = 0, kPolicyBf16x3 = 1 };
+// Matrix-core arithmetic of the scan: fp64 products (fp32 inputs), or bf16
+// products on a (high, low) split of each fp32 operand (bf16 inputs).
+enum Policy : int { kPolicyF64 = 0, kPolicyBf16x3 = 1 };
 
 struct ConvArgs {
     const void* seg_ptr[3];     // x, B, C segments

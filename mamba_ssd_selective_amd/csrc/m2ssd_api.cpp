@@ -21,7 +21,7 @@ namespace {
 thread_local std::string g_last_error;
 
 struct Counters {
-    std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f32{0}, scan_bf16x3{0}, norm{0}, prefill{0};
+    std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f64{0}, scan_bf16x3{0}, norm{0}, prefill{0};
 } g_counters;
 
 // Event recorder for m2_timing_*: set k holds 5 events around the 4 launches of call k.
@@ -50,6 +50,7 @@ int ok() {
     return M2_OK;
 }
 
+int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int elem_size(int dtype) { return dtype == M2_BF16 ? 2 : 4; }
 bool valid_dtype(int d) { return d == M2_F32 || d == M2_BF16; }
@@ -195,7 +196,7 @@ int m2_get_counters(m2_counters* out) {
     if (!out) return fail(M2_ERR_NULL, "m2_get_counters: out is NULL");
     out->conv_launches = g_counters.conv.load();
     out->conv_state_launches = g_counters.conv_state.load();
-    out->scan_f32_launches = g_counters.scan_f32.load();
+    out->scan_f64_launches = g_counters.scan_f64.load();
     out->scan_bf16x3_launches = g_counters.scan_bf16x3.load();
     out->norm_launches = g_counters.norm.load();
     out->prefill_calls = g_counters.prefill.load();
@@ -205,7 +206,7 @@ int m2_get_counters(m2_counters* out) {
 void m2_reset_counters(void) {
     g_counters.conv = 0;
     g_counters.conv_state = 0;
-    g_counters.scan_f32 = 0;
+    g_counters.scan_f64 = 0;
     g_counters.scan_bf16x3 = 0;
     g_counters.norm = 0;
     g_counters.prefill = 0;
@@ -255,13 +256,13 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     if (st) return st;
     m2::ScanArgs a{};
     a.x = x; a.ld_x = ld_x; a.B = B; a.ld_B = ld_B; a.C = C; a.ld_C = ld_C;
-    a.act_dtype = act_dtype; a.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF32;
+    a.act_dtype = act_dtype; a.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
     a.dt = dt; a.ld_dt = ld_dt; a.A = A; a.D = D; a.ssm_state = ssm_state;
     a.cu_seqlens = cu_seqlens; a.batch = batch; a.state_idx = state_idx; a.has_init = has_init;
     a.nheads = nheads; a.headdim = headdim; a.dstate = dstate; a.ngroups = ngroups;
     a.chunk = chunk_size; a.y = y; a.ld_y = ld_y;
     if ((st = hip_status(m2::launch_ssd_scan(a, static_cast<hipStream_t>(stream)), "scan launch"))) return st;
-    (a.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f32)++;
+    (a.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f64)++;
     return ok();
 }
 
@@ -284,14 +285,18 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
 }
 
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen, int nheads,
-                                     int headdim, int dstate, int ngroups, int chunk_size) {
+                                     int headdim, int dstate, int ngroups, int chunk_size,
+                                     int act_dtype) {
     (void)batch; (void)max_seqlen; (void)chunk_size;
-    if (total_tokens < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0) return 0;
+    if (total_tokens < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        !valid_dtype(act_dtype))
+        return 0;
     const int64_t conv_dim = (int64_t)nheads * headdim + 2 * (int64_t)ngroups * dstate;
     const int64_t di = (int64_t)nheads * headdim;
-    auto round256 = [](int64_t v) { return (v + 255) / 256 * 256; };
-    // post-conv activations (fp32) + pre-norm output (fp32, used when y is not fp32)
-    return (size_t)(round256(total_tokens * conv_dim * 4) + round256(total_tokens * di * 4));
+    // post-conv activations (fp32 for bf16 inputs, fp64 for fp32 inputs) + the
+    // pre-norm output (fp32; used when y is not fp32)
+    const int64_t ues = act_dtype == M2_BF16 ? 4 : 8;
+    return (size_t)(round256(total_tokens * conv_dim * ues) + round256(total_tokens * di * 4));
 }
 
 int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -309,13 +314,19 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     const int conv_dim = d_x + 2 * d_b;
     if (!z || !norm_w || !y) return fail(M2_ERR_NULL, "prefill: z, norm_w and y are required");
     if (!valid_dtype(y_dtype)) return fail(M2_ERR_DTYPE, "prefill: y_dtype must be M2_F32 or M2_BF16");
+    if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "prefill: act_dtype must be M2_F32 or M2_BF16");
     const size_t need = mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads,
-                                                      headdim, dstate, ngroups, chunk_size);
+                                                      headdim, dstate, ngroups, chunk_size, act_dtype);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(M2_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (workspace && !aligned16(workspace)) return fail(M2_ERR_ALIGN, "prefill: workspace must be 16-byte aligned");
-    float* u = static_cast<float*>(workspace);
-    float* ypre_ws = u ? u + ((int64_t)total_tokens * conv_dim * 4 + 255) / 256 * 64 : nullptr;
+    // Post-conv activations: fp32 for bf16 inputs, fp64 for fp32 inputs (the
+    // fp64 scan path reads them without an fp32 rounding in between).
+    const int u_dtype = act_dtype == M2_BF16 ? m2::kF32 : m2::kF64;
+    const int64_t u_bytes = round256((int64_t)total_tokens * conv_dim * (u_dtype == m2::kF64 ? 8 : 4));
+    char* wsb = static_cast<char*>(workspace);
+    void* u = wsb;
+    float* ypre_ws = wsb ? reinterpret_cast<float*>(wsb + u_bytes) : nullptr;
     if ((st = validate_conv(x, ld_x, B, ld_B, C, ld_C, d_x, d_b, act_dtype, conv_w, conv_b, 4,
                             conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
                             state_idx, u ? u : y, conv_dim, M2_F32)))
@@ -323,7 +334,7 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     if (!dt || !A || !ssm_state) return fail(M2_ERR_NULL, "prefill: dt, A and ssm_state are required");
     if (ld_dt < nheads) return fail(M2_ERR_STRIDE, "prefill: ld_dt < nheads");
     if (!aligned16(ssm_state)) return fail(M2_ERR_ALIGN, "prefill: ssm_state must be 16-byte aligned");
-    if ((st = validate_norm(u ? u : static_cast<const float*>(y), d_x, z, ld_z, act_dtype, norm_w,
+    if ((st = validate_norm(static_cast<const float*>(u ? u : y), d_x, z, ld_z, act_dtype, norm_w,
                             ngroups, total_tokens, d_x, y, ld_y, y_dtype)))
         return st;
     if (y_dtype == M2_F32 && (ld_y * 4) % 16) return fail(M2_ERR_ALIGN, "prefill: ld_y must be a multiple of 16 bytes");
@@ -341,7 +352,7 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     ca.conv_dim = conv_dim; ca.conv_state = conv_state; ca.cu_seqlens = cu_seqlens;
     ca.batch = batch; ca.total_tokens = total_tokens; ca.state_idx = state_idx;
     ca.has_init = has_init; ca.apply_silu = 1; ca.out = u; ca.ld_out = conv_dim;
-    ca.out_dtype = M2_F32;
+    ca.out_dtype = u_dtype;
     if (total_tokens > 0) {
         if ((st = hip_status(m2::launch_conv_rows(ca, s), "prefill conv launch"))) return st;
         g_counters.conv++;
@@ -354,15 +365,18 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     float* ypre = (y_dtype == M2_F32) ? static_cast<float*>(y) : ypre_ws;
     const int64_t ld_pre = (y_dtype == M2_F32) ? ld_y : d_x;
     m2::ScanArgs sa{};
-    sa.x = u; sa.ld_x = conv_dim; sa.B = u + d_x; sa.ld_B = conv_dim;
-    sa.C = u + d_x + d_b; sa.ld_C = conv_dim; sa.act_dtype = M2_F32;
-    sa.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF32;
+    const int ues = u_dtype == m2::kF64 ? 8 : 4;
+    sa.x = u; sa.ld_x = conv_dim;
+    sa.B = static_cast<char*>(u) + (int64_t)d_x * ues; sa.ld_B = conv_dim;
+    sa.C = static_cast<char*>(u) + (int64_t)(d_x + d_b) * ues; sa.ld_C = conv_dim;
+    sa.act_dtype = u_dtype;
+    sa.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
     sa.dt = dt; sa.ld_dt = ld_dt; sa.A = A; sa.D = D; sa.ssm_state = ssm_state;
     sa.cu_seqlens = cu_seqlens; sa.batch = batch; sa.state_idx = state_idx; sa.has_init = has_init;
     sa.nheads = nheads; sa.headdim = headdim; sa.dstate = dstate; sa.ngroups = ngroups;
     sa.chunk = chunk_size; sa.y = ypre; sa.ld_y = ld_pre;
     if ((st = hip_status(m2::launch_ssd_scan(sa, s), "prefill scan launch"))) return st;
-    (sa.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f32)++;
+    (sa.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f64)++;
     mark(3);
 
     if (total_tokens > 0) {

@@ -27,16 +27,15 @@
 //      h <- e(gamma_S) h + B^T (x dt e(gamma_S - gamma_i)).
 //   5. M^T tiles go through LDS (reusing the B buffer) and y^T += X^T M^T.
 //   6. y rows of the chunk are stored; after the last chunk the state is stored.
-// Matrix products use PolicyBf16x3 (bf16 inputs) or PolicyF32 (fp32 inputs).
+// Matrix products use PolicyBf16x3 (bf16 inputs; fp32 values, 128-row chunks)
+// or PolicyF64 (fp32 inputs; fp64 values, chunks evaluated 64 rows at a time,
+// which is the same function of the inputs).
 
 #include "device_common.h"
 #include "kernels.h"
 
 namespace m2 {
 namespace {
-
-constexpr int QMAX = 128;          // largest chunk
-constexpr int NTQ = QMAX / 16;     // row tiles per chunk
 
 __device__ __forceinline__ void tile_of(int k, int& it, int& tt) {
     // causal tile k = tt*(tt+1)/2 + it, 0 <= it <= tt
@@ -48,19 +47,25 @@ __device__ __forceinline__ void tile_of(int k, int& it, int& tt) {
 
 template <int P, int N, class Pol, typename Tin>
 __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
+    using V = typename Pol::Val;
+    using Acc = typename Pol::Acc;
+    using Op = typename Pol::Op;
+    constexpr int QMAX = Pol::QMAX;      // rows staged per step
+    constexpr int NTQ = QMAX / 16;       // row tiles per step
+    constexpr int NKBQ = QMAX / 32;      // K blocks over rows
     constexpr int W = P / 16;
     constexpr int NTN = N / 16;          // 16-wide n tiles of the state
     constexpr int NKBN = (N + 31) / 32;  // K blocks over n
-    constexpr int LDS_ROW = N + 4;       // padded row of the staged B / C
+    constexpr int LDS_ROW = N + 16 / (int)sizeof(V);   // padded row of the staged B / C
+    constexpr int MAXT = NTQ * (NTQ + 1) / 2;           // causal 16x16 tiles of a full step
+    constexpr int BS_SIZE = (QMAX * LDS_ROW > MAXT * 64 * 4) ? QMAX * LDS_ROW : MAXT * 64 * 4;
 
-    constexpr int MAXT = NTQ * (NTQ + 1) / 2;   // causal 16x16 tiles of a full chunk
-    constexpr int BS_SIZE = (QMAX * LDS_ROW > MAXT * 256) ? QMAX * LDS_ROW : MAXT * 256;
-    __shared__ __align__(16) float Bs[BS_SIZE];         // B rows; later the M^T tiles
-    __shared__ __align__(16) float Cs[QMAX * LDS_ROW];
+    __shared__ __align__(16) V Bs[BS_SIZE];      // B rows; later the M^T tiles
+    __shared__ __align__(16) V Cs[QMAX * LDS_ROW];
     __shared__ __align__(16) double gam[QMAX];
-    __shared__ __align__(16) float dts[QMAX];
-    __shared__ __align__(16) float wout[QMAX];          // dt_i * e(gamma_S - gamma_i)
-    __shared__ __align__(16) float din[QMAX];           // e(gamma_t)
+    __shared__ __align__(16) V dts[QMAX];
+    __shared__ __align__(16) V wout[QMAX];       // dt_i * e(gamma_S - gamma_i)
+    __shared__ __align__(16) V din[QMAX];        // e(gamma_t)
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -82,117 +87,123 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
     const int64_t L = a.cu_seqlens[seq + 1] - s0;
     const int slot = a.state_idx ? a.state_idx[seq] : seq;
     const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
+    const int chunk = a.chunk < QMAX ? a.chunk : QMAX;
 
     const Tin* X = static_cast<const Tin*>(a.x);
     const Tin* Bg = static_cast<const Tin*>(a.B);
     const Tin* Cg = static_cast<const Tin*>(a.C);
-    const float Ah = a.A[head];
-    const float Dh = a.D ? a.D[head] : 0.0f;
+    const V Ah = a.A[head];
+    const V Dh = a.D ? a.D[head] : 0.0f;
     const int p = wave * 16 + l16;     // this lane's headdim column
 
     float* st = a.ssm_state + ((int64_t)slot * a.nheads + head) * (int64_t)(P * N);
 
-    // State accumulators: hacc[nt][r] = h[p][16 nt + 4 q + r].
-    f32x4_t hacc[NTN];
+    // State accumulators: hacc[nt][r] = h[p][16 nt + orow(q, r)].
+    Acc hacc[NTN];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt) {
-        if (init && L > 0) {
-            const float4 v = *reinterpret_cast<const float4*>(st + p * N + 16 * nt + 4 * q);
-            hacc[nt] = f32x4_t{v.x, v.y, v.z, v.w};
-        } else {
-            hacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            hacc[nt][r] = (init && L > 0) ? (V)st[p * N + 16 * nt + Pol::orow(q, r)] : (V)0;
     }
     if (L <= 0) {
         // Empty sequence: a fresh slot is still reset, a carried one is untouched.
         if (!init) {
 #pragma unroll
             for (int nt = 0; nt < NTN; ++nt)
-                *reinterpret_cast<float4*>(st + p * N + 16 * nt + 4 * q) = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[p * N + 16 * nt + Pol::orow(q, r)] = 0.f;
         }
         return;
     }
 
-    for (int64_t c0 = 0; c0 < L; c0 += a.chunk) {
-        const int S = (int)((L - c0) < a.chunk ? (L - c0) : a.chunk);
+    for (int64_t c0 = 0; c0 < L; c0 += chunk) {
+        const int S = (int)((L - c0) < chunk ? (L - c0) : chunk);
         const int nT = (S + 15) >> 4;            // row tiles in this chunk
-        const int rows = ((nT + 1) >> 1) * 32;   // staged rows: whole K blocks of 32
+        const int nkbi = (nT + 1) >> 1;          // K blocks over rows
+        const int rows = nkbi * 32;              // staged rows: whole K blocks
         const int64_t r0 = s0 + c0;              // first packed row of the chunk
 
         __syncthreads();  // previous chunk finished with the LDS buffers
 
-        // 1. stage B, C (fp32) and dt; rows >= S are zero
+        // 1. stage B, C and dt; rows >= S are zero
         {
-            constexpr int V = 8;                  // values per load
-            constexpr int PER_ROW = N / V;
+            constexpr int PER_ROW = N / 8;
             for (int e = tid; e < rows * PER_ROW; e += 64 * W) {
                 const int i = e / PER_ROW;
-                const int n0 = (e % PER_ROW) * V;
-                float vb[8], vc[8];
+                const int n0 = (e % PER_ROW) * 8;
+                V vb[8], vc[8];
                 if (i < S) {
                     load8(Bg + (r0 + i) * a.ld_B + grp * N + n0, vb);
                     load8(Cg + (r0 + i) * a.ld_C + grp * N + n0, vc);
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) { vb[j] = 0.f; vc[j] = 0.f; }
+                    for (int j = 0; j < 8; ++j) { vb[j] = 0; vc[j] = 0; }
                 }
-                float* bd = Bs + i * LDS_ROW + n0;
-                float* cd = Cs + i * LDS_ROW + n0;
-                *reinterpret_cast<float4*>(bd) = float4{vb[0], vb[1], vb[2], vb[3]};
-                *reinterpret_cast<float4*>(bd + 4) = float4{vb[4], vb[5], vb[6], vb[7]};
-                *reinterpret_cast<float4*>(cd) = float4{vc[0], vc[1], vc[2], vc[3]};
-                *reinterpret_cast<float4*>(cd + 4) = float4{vc[4], vc[5], vc[6], vc[7]};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    Bs[i * LDS_ROW + n0 + j] = vb[j];
+                    Cs[i * LDS_ROW + n0 + j] = vc[j];
+                }
             }
             for (int i = tid; i < QMAX; i += 64 * W)
-                dts[i] = (i < S) ? a.dt[(r0 + i) * a.ld_dt + head] : 0.f;
+                dts[i] = (i < S) ? (V)a.dt[(r0 + i) * a.ld_dt + head] : (V)0;
         }
 
-        // X operand values for this lane: xr[kb][j] = x[i][p], i = 32 kb + kslot(q, j).
-        float xr[QMAX / 32][8];
+        // X operand values for this lane: xr[kb][j] = x[i][p], i = 32 kb + kslot<Pol>(q, j).
+        V xr[NKBQ][8];
 #pragma unroll
-        for (int kb = 0; kb < QMAX / 32; ++kb) {
+        for (int kb = 0; kb < NKBQ; ++kb) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int i = 32 * kb + kslot(q, j);
-                xr[kb][j] = (i < S) ? Act<Tin>::load(X + (r0 + i) * a.ld_x + (int64_t)head * P + p) : 0.f;
+                const int i = 32 * kb + kslot<Pol>(q, j);
+                xr[kb][j] = (i < S) ? (V)Act<Tin>::load(X + (r0 + i) * a.ld_x + (int64_t)head * P + p) : (V)0;
             }
         }
         __syncthreads();
 
-        // 2. gamma: inclusive prefix sum of a = dt * A in fp64 (wave 0, 2 rows per lane)
+        // 2. gamma: inclusive prefix sum of a = dt * A in fp64 on wave 0, each
+        //    lane summing RPL consecutive rows before the wavefront scan.
         if (wave == 0) {
-            const double a0 = (double)dts[2 * lane] * (double)Ah;
-            const double a1 = (double)dts[2 * lane + 1] * (double)Ah;
-            double v = a0 + a1;
+            constexpr int RPL = QMAX / 64;
+            double av[RPL];
+            double v = 0.0;
+#pragma unroll
+            for (int k = 0; k < RPL; ++k) {
+                av[k] = (double)dts[RPL * lane + k] * (double)Ah;
+                v += av[k];
+            }
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
                 const double t = __shfl_up(v, d, 64);
                 if (lane >= d) v += t;
             }
-            double ex = __shfl_up(v, 1, 64);
-            if (lane == 0) ex = 0.0;
-            const double g0 = ex + a0;
-            gam[2 * lane] = g0;
-            gam[2 * lane + 1] = g0 + a1;
+            double run = __shfl_up(v, 1, 64);
+            if (lane == 0) run = 0.0;
+#pragma unroll
+            for (int k = 0; k < RPL; ++k) {
+                run += av[k];
+                gam[RPL * lane + k] = run;
+            }
         }
         __syncthreads();
         const double gS = gam[S - 1];
         for (int i = tid; i < QMAX; i += 64 * W) {
             const double gi = gam[i];
-            din[i] = __expf((float)fmin(gi, 0.0));
-            wout[i] = dts[i] * __expf((float)fmin(gS - gi, 0.0));
+            din[i] = Pol::expc(fmin(gi, 0.0));
+            wout[i] = dts[i] * Pol::expc(fmin(gS - gi, 0.0));
         }
-        const float chunk_decay = __expf((float)fmin(gS, 0.0));
+        const V chunk_decay = Pol::expc(fmin(gS, 0.0));
         __syncthreads();
 
         // 3. M^T tiles (causal), computed by wave (k mod W)
         constexpr int MYT = (MAXT + W - 1) / W;
         const int ntiles = nT * (nT + 1) / 2;
-        f32x4_t mt[MYT];
+        Acc mt[MYT];
 #pragma unroll
         for (int s = 0; s < MYT; ++s) {
             const int k = wave + s * W;
-            mt[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            mt[s] = Acc{0, 0, 0, 0};
             if (k < ntiles) {
                 int it, tt;
                 tile_of(k, it, tt);
@@ -200,12 +211,12 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
                 const int tb = 16 * tt + l16;    // B column (C row t)
 #pragma unroll
                 for (int kb = 0; kb < NKBN; ++kb) {
-                    float va[8], vb[8];
+                    V va[8], vb[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const int n = 32 * kb + kslot(q, j);
-                        va[j] = (n < N) ? Bs[ia * LDS_ROW + n] : 0.f;
-                        vb[j] = (n < N) ? Cs[tb * LDS_ROW + n] : 0.f;
+                        const int n = 32 * kb + kslot<Pol>(q, j);
+                        va[j] = (n < N) ? Bs[ia * LDS_ROW + n] : (V)0;
+                        vb[j] = (n < N) ? Cs[tb * LDS_ROW + n] : (V)0;
                     }
                     Pol::mma(mt[s], Pol::make(va), Pol::make(vb));
                 }
@@ -214,10 +225,10 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
                 const double gt = gam[t];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * it + 4 * q + r;
-                    float v = 0.f;
+                    const int i = 16 * it + Pol::orow(q, r);
+                    V v = 0;
                     if (i <= t) {
-                        v = mt[s][r] * dts[i] * __expf((float)fmin(gt - gam[i], 0.0));
+                        v = mt[s][r] * dts[i] * Pol::expc(fmin(gt - gam[i], 0.0));
                         if (i == t) v += Dh;
                     }
                     mt[s][r] = v;
@@ -226,28 +237,28 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
         }
 
         // 4a. y^T[p, t] = sum_n h_in[p, n] C[t, n] e(gamma_t)
-        f32x4_t yacc[NTQ];
+        Acc yacc[NTQ];
 #pragma unroll
-        for (int tt = 0; tt < NTQ; ++tt) yacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < NTQ; ++tt) yacc[tt] = Acc{0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < NKBN; ++kb) {
-            float va[8];
+            V va[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int nt = 2 * kb + (j >> 2);
-                va[j] = (nt < NTN) ? hacc[nt < NTN ? nt : 0][j & 3] : 0.f;
+                va[j] = (nt < NTN) ? (V)hacc[nt < NTN ? nt : 0][j & 3] : (V)0;
             }
-            const typename Pol::Op ha = Pol::make(va);
+            const Op ha = Pol::make(va);
 #pragma unroll
             for (int tt = 0; tt < NTQ; ++tt) {
                 if (tt < nT) {
                     const int t = 16 * tt + l16;
-                    const float dt_in = din[t];
-                    float vb[8];
+                    const V dt_in = din[t];
+                    V vb[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const int n = 32 * kb + kslot(q, j);
-                        vb[j] = (n < N) ? Cs[t * LDS_ROW + n] * dt_in : 0.f;
+                        const int n = 32 * kb + kslot<Pol>(q, j);
+                        vb[j] = (n < N) ? Cs[t * LDS_ROW + n] * dt_in : (V)0;
                     }
                     Pol::mma(yacc[tt], ha, Pol::make(vb));
                 }
@@ -257,20 +268,19 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
         // 4b. h <- e(gamma_S) h + B^T (x dt e(gamma_S - gamma_i))
 #pragma unroll
         for (int nt = 0; nt < NTN; ++nt) hacc[nt] *= chunk_decay;
-        const int nkbi = (nT + 1) >> 1;
 #pragma unroll
-        for (int kb = 0; kb < QMAX / 32; ++kb) {
+        for (int kb = 0; kb < NKBQ; ++kb) {
             if (kb < nkbi) {
-                float vb[8];
+                V vb[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) vb[j] = xr[kb][j] * wout[32 * kb + kslot(q, j)];
-                const typename Pol::Op xb = Pol::make(vb);
+                for (int j = 0; j < 8; ++j) vb[j] = xr[kb][j] * wout[32 * kb + kslot<Pol>(q, j)];
+                const Op xb = Pol::make(vb);
 #pragma unroll
                 for (int nt = 0; nt < NTN; ++nt) {
                     const int n = 16 * nt + l16;
-                    float va[8];
+                    V va[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) va[j] = Bs[(32 * kb + kslot(q, j)) * LDS_ROW + n];
+                    for (int j = 0; j < 8; ++j) va[j] = Bs[(32 * kb + kslot<Pol>(q, j)) * LDS_ROW + n];
                     Pol::mma(hacc[nt], Pol::make(va), xb);
                 }
             }
@@ -278,32 +288,33 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
         __syncthreads();  // every wave is done reading Bs / Cs
 
         // 5. M^T tiles to LDS in accumulator layout, then y^T += X^T M^T
-        float* Ms = Bs;
+        V* Ms = Bs;
 #pragma unroll
         for (int s = 0; s < MYT; ++s) {
             const int k = wave + s * W;
-            if (k < ntiles)
-                *reinterpret_cast<float4*>(Ms + (k * 64 + lane) * 4) =
-                    float4{mt[s][0], mt[s][1], mt[s][2], mt[s][3]};
+            if (k < ntiles) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ms[(k * 64 + lane) * 4 + r] = mt[s][r];
+            }
         }
         __syncthreads();
 #pragma unroll
-        for (int kb = 0; kb < QMAX / 32; ++kb) {
+        for (int kb = 0; kb < NKBQ; ++kb) {
             if (kb < nkbi) {
-                const typename Pol::Op xa = Pol::make(xr[kb]);
+                const Op xa = Pol::make(xr[kb]);
 #pragma unroll
                 for (int tt = 0; tt < NTQ; ++tt) {
                     if (tt < nT && 2 * kb <= tt) {
-                        float vb[8];
-                        const float4 lo4 = *reinterpret_cast<const float4*>(
-                            Ms + ((tt * (tt + 1) / 2 + 2 * kb) * 64 + lane) * 4);
-                        vb[0] = lo4.x; vb[1] = lo4.y; vb[2] = lo4.z; vb[3] = lo4.w;
+                        V vb[8];
+                        const V* lo4 = Ms + ((tt * (tt + 1) / 2 + 2 * kb) * 64 + lane) * 4;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) vb[r] = lo4[r];
                         if (2 * kb + 1 <= tt) {
-                            const float4 hi4 = *reinterpret_cast<const float4*>(
-                                Ms + ((tt * (tt + 1) / 2 + 2 * kb + 1) * 64 + lane) * 4);
-                            vb[4] = hi4.x; vb[5] = hi4.y; vb[6] = hi4.z; vb[7] = hi4.w;
+                            const V* hi4 = Ms + ((tt * (tt + 1) / 2 + 2 * kb + 1) * 64 + lane) * 4;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) vb[4 + r] = hi4[r];
                         } else {
-                            vb[4] = vb[5] = vb[6] = vb[7] = 0.f;
+                            vb[4] = vb[5] = vb[6] = vb[7] = 0;
                         }
                         Pol::mma(yacc[tt], xa, Pol::make(vb));
                     }
@@ -311,33 +322,44 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
             }
         }
 
-        // 6. store y rows of the chunk: lane holds y[t = 16 tt + l16][16 w + 4 q + r]
+        // 6. store y rows of the chunk: lane holds y[t = 16 tt + l16][16 w + orow(q, r)]
 #pragma unroll
         for (int tt = 0; tt < NTQ; ++tt) {
             const int t = 16 * tt + l16;
             if (tt < nT && t < S) {
-                float* dst = a.y + (r0 + t) * a.ld_y + (int64_t)head * P + 16 * wave + 4 * q;
-                *reinterpret_cast<float4*>(dst) = float4{yacc[tt][0], yacc[tt][1], yacc[tt][2], yacc[tt][3]};
+                float* dst = a.y + (r0 + t) * a.ld_y + (int64_t)head * P + 16 * wave;
+                if constexpr (Pol::kRowsContiguous) {
+                    *reinterpret_cast<float4*>(dst + 4 * q) =
+                        float4{(float)yacc[tt][0], (float)yacc[tt][1], (float)yacc[tt][2], (float)yacc[tt][3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[Pol::orow(q, r)] = (float)yacc[tt][r];
+                }
             }
         }
     }
 
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt)
-        *reinterpret_cast<float4*>(st + p * N + 16 * nt + 4 * q) =
-            float4{hacc[nt][0], hacc[nt][1], hacc[nt][2], hacc[nt][3]};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[p * N + 16 * nt + Pol::orow(q, r)] = (float)hacc[nt][r];
 }
 
 template <int P, int N>
 hipError_t launch_pn(const ScanArgs& a, hipStream_t stream) {
     const dim3 grid(a.nheads * a.batch);
     const dim3 block(64 * (P / 16));
-    if (a.act_dtype == kBF16)
-        hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyBf16x3, uint16_t>), grid, block, 0, stream, a);
-    else if (a.policy == kPolicyBf16x3)
-        hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyBf16x3, float>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyF32, float>), grid, block, 0, stream, a);
+    if (a.policy == kPolicyBf16x3) {
+        if (a.act_dtype == kBF16)
+            hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyBf16x3, uint16_t>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyBf16x3, float>), grid, block, 0, stream, a);
+    } else {
+        if (a.act_dtype == kF64)
+            hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyF64, double>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((ssd_scan_kernel<P, N, PolicyF64, float>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ def test_conv_and_norm_reject_bad_arguments():
 
 def test_workspace_query_and_prefill_workspace_error():
     lib = m2.load()
-    n = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128)
+    n = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128, 1)
     assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4
-    assert lib.mamba2_prefill_workspace_size(-1, 1, 1, 64, 64, 128, 8, 128) == 0
+    n32 = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128, 0)
+    assert n32 >= 1000 * (4096 + 2048) * 8 + 1000 * 4096 * 4
+    assert lib.mamba2_prefill_workspace_size(-1, 1, 1, 64, 64, 128, 8, 128, 1) == 0
+    assert lib.mamba2_prefill_workspace_size(10, 1, 10, 64, 64, 128, 8, 128, 5) == 0

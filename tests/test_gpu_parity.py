@@ -267,10 +267,10 @@ def test_deterministic_and_counters():
     y2, c2, s2 = gpu_prefill(inp, w.shape, "bf16")
     assert torch.equal(y1, y2) and torch.equal(c1, c2) and torch.equal(s1, s2)
     c = m2.get_counters()
-    assert c["prefill_calls"] == 2 and c["scan_bf16x3_launches"] == 2 and c["scan_f32_launches"] == 0
+    assert c["prefill_calls"] == 2 and c["scan_bf16x3_launches"] == 2 and c["scan_f64_launches"] == 0
     inp0 = make_inputs(WORKLOADS[0], 0)
     gpu_prefill(inp0, WORKLOADS[0].shape, "f32", 16)
-    assert m2.get_counters()["scan_f32_launches"] == 1
+    assert m2.get_counters()["scan_f64_launches"] == 1
 
 
 def test_carried_state_matters():
