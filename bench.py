@@ -44,7 +44,7 @@ def _oracle_item(args):
     return time.perf_counter() - t
 
 
-def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=512):
+def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=1536):
     """Oracle on the first `tokens` rows of `seqs`, all groups, one (sequence, group) slice per task."""
     import multiprocessing as mp
     import concurrent.futures as cf
@@ -81,16 +81,27 @@ def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=512):
 # ---------------------------------------------------------------- algorithmic work per kernel
 
 def kernel_bytes(w, T, nseq):
-    """Algorithmic HBM bytes of one launch of each kernel of the current prefill chain."""
+    """Algorithmic HBM bytes of one launch of each kernel of the prefill chain (bf16 inputs).
+
+    conv         read x|B|C, write the post-conv activations (fp32)
+    conv_state   read the old and write the new conv state of each sequence
+    scan_pass    read post-conv x, B and dt; write the state entering every
+                 chunk; read the initial and write the final SSM state
+    scan_out     read post-conv x, B, C, dt and the entry state of every chunk;
+                 write y before the norm (fp32)
+    norm         read y (fp32) and z, write the output (fp32)
+    """
     s = w.shape
     act = 2 if w.act == "bf16" else 4
-    di, cd = s.d_inner, s.conv_dim
+    di, cd, gn = s.d_inner, s.conv_dim, s.ngroups * s.dstate
     state = s.nheads * s.headdim * s.dstate * 4
+    slots = T // w.chunk_size + nseq
     return {
-        "conv": T * (cd * act + cd * 4),                  # read xBC, write post-conv (fp32)
+        "conv": T * (cd * act + cd * 4),
         "conv_state": nseq * 2 * 3 * cd * 4,
-        "scan": T * (cd * 4 + s.nheads * 4 + di * 4) + nseq * 2 * state,  # u, dt in; y_pre out; states
-        "norm": T * (di * 4 + di * act + di * 4),         # y_pre, z in; y out
+        "scan_pass": T * (di * 4 + gn * 4 + s.nheads * 4) + slots * state + nseq * 2 * state,
+        "scan_out": T * (di * 4 + 2 * gn * 4 + s.nheads * 4 + di * 4) + slots * state,
+        "norm": T * (di * 4 + di * act + di * 4),
     }
 
 
@@ -116,6 +127,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device-to-device copy of this many MiB "
+                         "(a reference kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -186,11 +200,22 @@ def main():
     m2.timing_enable(0)
     assert kt["calls"] == args.steps, kt
     assert torch.isfinite(y).all().item(), "non-finite output"
+    stages = ("conv", "conv_state", "scan_pass", "scan_out", "norm")
+    kms = {k: kt[k + "_ms"] / args.steps for k in stages}
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; kernel ms/step: " +
-        ", ".join(f"{k[:-3]} {kt[k] / args.steps:.3f}" for k in ("conv_ms", "conv_state_ms", "scan_ms", "norm_ms")))
+        ", ".join(f"{k} {v:.3f}" for k, v in kms.items()))
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
+        del src, dst
 
     kb = kernel_bytes(w, T, nseq)
-    kms = {k: kt[k + "_ms"] / args.steps for k in ("conv", "conv_state", "scan", "norm")}
     dom = max(kms, key=kms.get)
     achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -198,7 +223,7 @@ def main():
             "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
             "step_bytes": fused_bytes(w, T, nseq),
             "step_frac": round(fused_bytes(w, T, nseq) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "scan_tflops_alg": round(scan_flops(w, T) / (kms["scan"] * 1e-3) / 1e12, 2),
+            "scan_tflops_alg": round(scan_flops(w, T) / ((kms["scan_pass"] + kms["scan_out"]) * 1e-3) / 1e12, 2),
             "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
     out = {"metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -146,12 +146,23 @@ int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
  *   ssm_state [n_slots, nheads, headdim, dstate] fp32, read and advanced in place.
  *   y   [T, nheads*headdim] fp32 (ld_y), must not overlap any input.
  *   chunk_size: multiple of 16 in [16, 128].
+ *   workspace: device memory of at least ssd_chunk_scan_workspace_size()
+ *     bytes, 16-byte aligned (NULL allowed when that size is 0); its contents
+ *     on entry do not matter and are undefined on return.
+ * Alignment: x, B, C, y, ssm_state 16-byte aligned; ld_x, ld_B, ld_C times
+ * the element size and ld_y * 4 multiples of 16 bytes.
  * Supported (headdim, dstate): (16,16), (32,64), (64,64), (64,128).
- * Arithmetic: bf16 inputs use bf16 matrix instructions on a two-term (high,
- * low) bf16 split of every fp32 operand (three products per tile) with fp32
- * accumulation; fp32 inputs are computed in fp64 (fp64 matrix instructions,
- * chunks evaluated 64 rows at a time -- the same function of the inputs).
- * Cumulative sums and exponent differences are fp64 on both paths.
+ * Arithmetic:
+ *   bf16 inputs, headdim 64, dstate 64 or 128, chunk_size 128 (chunk-parallel
+ *     path): x, B, C enter bf16 matrix instructions as they are; the computed
+ *     operands (dt-weighted x, the masked decay matrix, the carried state) are
+ *     split into (high, low) bf16 pairs and enter two products; fp32
+ *     accumulation.  The workspace holds the state entering every chunk.
+ *   other bf16 shapes (one-pass path): every fp32 operand split into a (high,
+ *     low) bf16 pair, three products per tile, fp32 accumulation; no workspace.
+ *   fp32 inputs: computed in fp64 (fp64 matrix instructions, chunks evaluated
+ *     64 rows at a time -- the same function of the inputs); no workspace.
+ * Cumulative sums and exponent differences are fp64 on every path.
  */
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                    const void* C, int64_t ld_C, int act_dtype,
@@ -160,7 +171,16 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                    const int32_t* cu_seqlens, int batch, int64_t total_tokens,
                    int max_seqlen, const int32_t* state_idx, const uint8_t* has_init,
                    int nheads, int headdim, int dstate, int ngroups, int chunk_size,
-                   float* y, int64_t ld_y, void* stream);
+                   float* y, int64_t ld_y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Bytes of device workspace ssd_chunk_scan needs for these sizes (0 when the
+ * shape runs on a path without workspace, or on bad arguments):
+ * (total_tokens/128 + batch) * nheads * headdim * dstate * 4 on the
+ * chunk-parallel path.
+ */
+size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads, int headdim,
+                                     int dstate, int ngroups, int chunk_size, int act_dtype);
 
 /*
  * gated_rmsnorm_group -- grouped RMSNorm with the SiLU(z) gate.
@@ -181,7 +201,9 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
 /*
  * Bytes of device workspace mamba2_prefill needs for these sizes and this
  * activation dtype (0 on bad arguments).  The workspace holds the post-conv
- * activations of the batch and, when y is bf16, the pre-norm output.
+ * activations of the batch (bf16 for bf16 inputs, fp64 for fp32 inputs), the
+ * fp32 pre-norm output and, on the chunk-parallel scan path, the state
+ * entering every chunk.
  */
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
                                      int nheads, int headdim, int dstate, int ngroups,
@@ -217,9 +239,10 @@ typedef struct {
     uint64_t conv_launches;        /* conv kernel launches */
     uint64_t conv_state_launches;  /* conv-state update launches */
     uint64_t scan_f64_launches;    /* scan launches, fp64 matrix path (fp32 inputs) */
-    uint64_t scan_bf16x3_launches; /* scan launches, split-bf16 matrix path (bf16 inputs) */
+    uint64_t scan_bf16x3_launches; /* scan launches, one-pass split-bf16 path (bf16 inputs) */
     uint64_t norm_launches;        /* gated norm launches */
     uint64_t prefill_calls;        /* successful mamba2_prefill calls */
+    uint64_t scan_chunked_launches; /* scan launches, chunk-parallel path (bf16 inputs) */
 } m2_counters;
 
 /* Copy the counters into *out (M2_ERR_NULL if out is NULL). */
@@ -239,7 +262,8 @@ void m2_reset_counters(void);
 typedef struct {
     double conv_ms;        /* conv kernel */
     double conv_state_ms;  /* conv-state update */
-    double scan_ms;        /* chunked scan */
+    double scan_pass_ms;   /* scan state pass (the whole scan on the one-pass paths) */
+    double scan_out_ms;    /* scan chunk-output kernel (0 on the one-pass paths) */
     double norm_ms;        /* gated norm */
     uint64_t calls;        /* recorded prefill calls */
 } m2_kernel_times;

@@ -6,11 +6,12 @@ with ``python -m mamba_ssd_selective_amd.build``.
 """
 from ._lib import (M2_BF16, M2_F32, M2Error, cu_seqlens_of, gated_rmsnorm_group, get_counters,
                    load, mamba2_conv_rows, mamba2_prefill, mamba2_prefill_workspace_size,
-                   reset_counters, ssd_chunk_scan, timing_enable, timing_read, version,
-                   LIB_PATH)
+                   reset_counters, ssd_chunk_scan, ssd_chunk_scan_workspace_size, timing_enable,
+                   timing_read, version, LIB_PATH)
 
 __all__ = ["M2_BF16", "M2_F32", "M2Error", "cu_seqlens_of", "gated_rmsnorm_group",
            "get_counters", "load", "mamba2_conv_rows", "mamba2_prefill",
-           "mamba2_prefill_workspace_size", "reset_counters", "ssd_chunk_scan", "timing_enable",
+           "mamba2_prefill_workspace_size", "reset_counters", "ssd_chunk_scan",
+           "ssd_chunk_scan_workspace_size", "timing_enable",
            "timing_read", "version",
            "LIB_PATH"]

@@ -32,12 +32,14 @@ class M2Error(RuntimeError):
 class Counters(ctypes.Structure):
     _fields_ = [("conv_launches", ctypes.c_uint64), ("conv_state_launches", ctypes.c_uint64),
                 ("scan_f64_launches", ctypes.c_uint64), ("scan_bf16x3_launches", ctypes.c_uint64),
-                ("norm_launches", ctypes.c_uint64), ("prefill_calls", ctypes.c_uint64)]
+                ("norm_launches", ctypes.c_uint64), ("prefill_calls", ctypes.c_uint64),
+                ("scan_chunked_launches", ctypes.c_uint64)]
 
 
 class KernelTimes(ctypes.Structure):
     _fields_ = [("conv_ms", ctypes.c_double), ("conv_state_ms", ctypes.c_double),
-                ("scan_ms", ctypes.c_double), ("norm_ms", ctypes.c_double),
+                ("scan_pass_ms", ctypes.c_double), ("scan_out_ms", ctypes.c_double),
+                ("norm_ms", ctypes.c_double),
                 ("calls", ctypes.c_uint64)]
 
 
@@ -56,7 +58,9 @@ _SIGS = {
     "mamba2_conv_rows": (_I, [_P, _L, _P, _L, _P, _L, _I, _I, _I, _P, _P, _I, _P, _I,
                               _P, _I, _L, _I, _P, _P, _I, _P, _L, _I, _P]),
     "ssd_chunk_scan": (_I, [_P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _I,
-                            _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I, _P, _L, _P]),
+                            _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I, _P, _L, _P,
+                            ctypes.c_size_t, _P]),
+    "ssd_chunk_scan_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I]),
     "gated_rmsnorm_group": (_I, [_P, _L, _P, _L, _I, _P, _F, _I, _I, _L, _I, _P, _L, _I, _P]),
     "mamba2_prefill_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I, _I]),
     "mamba2_prefill": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
@@ -187,11 +191,29 @@ def mamba2_conv_rows(x, B, C, conv_w, conv_b, conv_state, cu_seqlens, max_seqlen
     return out
 
 
+def ssd_chunk_scan_workspace_size(total_tokens, batch, nheads, headdim, dstate, ngroups,
+                                  chunk_size=128, act_dtype=torch.bfloat16) -> int:
+    code = M2_BF16 if act_dtype == torch.bfloat16 else M2_F32
+    return int(load().ssd_chunk_scan_workspace_size(total_tokens, batch, nheads, headdim, dstate,
+                                                    ngroups, chunk_size, code))
+
+
 def ssd_chunk_scan(x, B, C, dt, A, D, ssm_state, cu_seqlens, max_seqlen, nheads, headdim,
-                   dstate, ngroups, chunk_size=128, state_idx=None, has_init=None, y=None):
-    """Chunked selective scan from post-conv x [T, H*P], B, C [T, G*N]; returns pre-norm y (fp32)."""
+                   dstate, ngroups, chunk_size=128, state_idx=None, has_init=None, y=None,
+                   workspace=None):
+    """Chunked selective scan from post-conv x [T, H*P], B, C [T, G*N]; returns pre-norm y (fp32).
+
+    workspace: uint8 device tensor of at least ssd_chunk_scan_workspace_size() bytes
+    (allocated here when None and the size is nonzero).
+    """
     lib = load()
     T = x.size(0)
+    batch = cu_seqlens.numel() - 1
+    need = ssd_chunk_scan_workspace_size(T, batch, nheads, headdim, dstate, ngroups, chunk_size,
+                                         x.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if y is None:
         y = torch.empty((T, nheads * headdim), dtype=torch.float32, device=x.device)
     for t, n in ((A, "A"), (D, "D"), (ssm_state, "ssm_state")):
@@ -208,7 +230,7 @@ def ssd_chunk_scan(x, B, C, dt, A, D, ssm_state, cu_seqlens, max_seqlen, nheads,
         _ptr(dt), _rows(dt, "dt"), _ptr(A), _ptr(D), _ptr(ssm_state), ssm_state.size(0),
         _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, int(max_seqlen), _ptr(state_idx),
         _ptr(has_init), nheads, headdim, dstate, ngroups, chunk_size, _ptr(y), _rows(y, "y"),
-        _stream())
+        _ptr(workspace), ws_bytes, _stream())
     _check(st)
     return y
 

@@ -21,17 +21,20 @@ namespace {
 thread_local std::string g_last_error;
 
 struct Counters {
-    std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f64{0}, scan_bf16x3{0}, norm{0}, prefill{0};
+    std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f64{0}, scan_bf16x3{0}, norm{0}, prefill{0},
+        scan_chunked{0};
 } g_counters;
 
-// Event recorder for m2_timing_*: set k holds 5 events around the 4 launches of call k.
+// Event recorder for m2_timing_*: set k holds kEv events around the kernel
+// stages of call k (conv, conv state, scan state pass, scan output, norm).
+constexpr int kEv = 6;
 struct Timing {
     std::vector<hipEvent_t> ev;
     int max_calls = 0;
     int used = 0;
     hipEvent_t* next() {  // event set for the next prefill call, or null when off / full
         if (used >= max_calls) return nullptr;
-        return &ev[5 * used++];
+        return &ev[kEv * used++];
     }
 } g_timing;
 
@@ -162,10 +165,10 @@ int validate_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
     if (ld_x < di || ld_B < gn || ld_C < gn || ld_dt < nheads || ld_y < di)
         return fail(M2_ERR_STRIDE, "scan: a row stride is smaller than its row width");
     const int es = elem_size(act_dtype);
-    if (!aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(ssm_state))
-        return fail(M2_ERR_ALIGN, "scan: B, C, y and ssm_state must be 16-byte aligned");
-    if ((ld_B * es) % 16 || (ld_C * es) % 16 || (ld_y * 4) % 16)
-        return fail(M2_ERR_ALIGN, "scan: ld_B, ld_C and ld_y must be multiples of 16 bytes");
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(ssm_state))
+        return fail(M2_ERR_ALIGN, "scan: x, B, C, y and ssm_state must be 16-byte aligned");
+    if ((ld_x * es) % 16 || (ld_B * es) % 16 || (ld_C * es) % 16 || (ld_y * 4) % 16)
+        return fail(M2_ERR_ALIGN, "scan: ld_x, ld_B, ld_C and ld_y must be multiples of 16 bytes");
     return check_batch(cu_seqlens, batch, total_tokens, max_seqlen, state_idx, n_slots);
 }
 
@@ -184,6 +187,32 @@ int validate_norm(const float* y, int64_t ld_y, const void* z, int64_t ld_z, int
     return M2_OK;
 }
 
+// Scan launch: the chunk-parallel kernels when a.states is set (it points at the
+// entry-state buffer; the caller sets it only for shapes those kernels cover),
+// else the one-pass kernel.  ev_mid (optional) is recorded after the state pass,
+// or after the whole one-pass scan.
+int launch_scan(m2::ScanArgs& a, int64_t total_tokens, hipStream_t s, hipEvent_t ev_mid) {
+    int st;
+    if (a.states) {
+        if ((st = hip_status(m2::launch_ssd_state_pass(a, s), "scan state pass launch"))) return st;
+        if (ev_mid) (void)hipEventRecord(ev_mid, s);
+        if ((st = hip_status(m2::launch_ssd_chunk_out(a, total_tokens, s), "scan chunk output launch"))) return st;
+        g_counters.scan_chunked++;
+        return M2_OK;
+    }
+    if ((st = hip_status(m2::launch_ssd_scan(a, s), "scan launch"))) return st;
+    if (ev_mid) (void)hipEventRecord(ev_mid, s);
+    (a.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f64)++;
+    return M2_OK;
+}
+
+size_t scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate,
+                         int chunk_size, int act_dtype) {
+    const int policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
+    if (!m2::chunked_scan_supported(policy, headdim, dstate, chunk_size)) return 0;
+    return m2::chunked_scan_states_bytes(total_tokens, batch, nheads, headdim, dstate);
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +229,7 @@ int m2_get_counters(m2_counters* out) {
     out->scan_bf16x3_launches = g_counters.scan_bf16x3.load();
     out->norm_launches = g_counters.norm.load();
     out->prefill_calls = g_counters.prefill.load();
+    out->scan_chunked_launches = g_counters.scan_chunked.load();
     return ok();
 }
 
@@ -210,6 +240,7 @@ void m2_reset_counters(void) {
     g_counters.scan_bf16x3 = 0;
     g_counters.norm = 0;
     g_counters.prefill = 0;
+    g_counters.scan_chunked = 0;
 }
 
 int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -244,16 +275,29 @@ int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B, c
     return ok();
 }
 
+size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads, int headdim,
+                                     int dstate, int ngroups, int chunk_size, int act_dtype) {
+    if (total_tokens < 0 || batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
+        ngroups <= 0 || !valid_dtype(act_dtype))
+        return 0;
+    return scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype);
+}
+
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
                    int64_t ld_C, int act_dtype, const float* dt, int64_t ld_dt, const float* A,
                    const float* D, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
                    int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
                    const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
-                   int chunk_size, float* y, int64_t ld_y, void* stream) {
+                   int chunk_size, float* y, int64_t ld_y, void* workspace, size_t ws_bytes,
+                   void* stream) {
     int st = validate_scan(x, ld_x, B, ld_B, C, ld_C, act_dtype, dt, ld_dt, A, D, ssm_state,
                            n_slots, cu_seqlens, batch, total_tokens, max_seqlen, state_idx, nheads,
                            headdim, dstate, ngroups, chunk_size, y, ld_y);
     if (st) return st;
+    const size_t need = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(M2_ERR_WORKSPACE, "scan: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (need > 0 && !aligned16(workspace)) return fail(M2_ERR_ALIGN, "scan: workspace must be 16-byte aligned");
     m2::ScanArgs a{};
     a.x = x; a.ld_x = ld_x; a.B = B; a.ld_B = ld_B; a.C = C; a.ld_C = ld_C;
     a.act_dtype = act_dtype; a.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
@@ -261,8 +305,8 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     a.cu_seqlens = cu_seqlens; a.batch = batch; a.state_idx = state_idx; a.has_init = has_init;
     a.nheads = nheads; a.headdim = headdim; a.dstate = dstate; a.ngroups = ngroups;
     a.chunk = chunk_size; a.y = y; a.ld_y = ld_y;
-    if ((st = hip_status(m2::launch_ssd_scan(a, static_cast<hipStream_t>(stream)), "scan launch"))) return st;
-    (a.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f64)++;
+    a.states = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    if ((st = launch_scan(a, total_tokens, static_cast<hipStream_t>(stream), nullptr))) return st;
     return ok();
 }
 
@@ -287,16 +331,17 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen, int nheads,
                                      int headdim, int dstate, int ngroups, int chunk_size,
                                      int act_dtype) {
-    (void)batch; (void)max_seqlen; (void)chunk_size;
-    if (total_tokens < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
-        !valid_dtype(act_dtype))
+    (void)max_seqlen;
+    if (total_tokens < 0 || batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
+        ngroups <= 0 || !valid_dtype(act_dtype))
         return 0;
     const int64_t conv_dim = (int64_t)nheads * headdim + 2 * (int64_t)ngroups * dstate;
     const int64_t di = (int64_t)nheads * headdim;
-    // post-conv activations (fp32 for bf16 inputs, fp64 for fp32 inputs) + the
-    // pre-norm output (fp32; used when y is not fp32)
+    // post-conv activations (fp32 for bf16 inputs, fp64 for fp32 inputs), the
+    // pre-norm output (fp32; used when y is not fp32) and the scan's entry states
     const int64_t ues = act_dtype == M2_BF16 ? 4 : 8;
-    return (size_t)(round256(total_tokens * conv_dim * ues) + round256(total_tokens * di * 4));
+    return (size_t)(round256(total_tokens * conv_dim * ues) + round256(total_tokens * di * 4)) +
+           scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype);
 }
 
 int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -321,12 +366,18 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
         return fail(M2_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (workspace && !aligned16(workspace)) return fail(M2_ERR_ALIGN, "prefill: workspace must be 16-byte aligned");
     // Post-conv activations: fp32 for bf16 inputs, fp64 for fp32 inputs (the
-    // fp64 scan path reads them without an fp32 rounding in between).
+    // fp64 scan path reads them without an fp32 rounding in between).  They are
+    // not rounded to bf16: y and the state reach max|err|/RMS ~ 0.05 from that
+    // rounding alone, where the largest outputs are tens of times the RMS.
     const int u_dtype = act_dtype == M2_BF16 ? m2::kF32 : m2::kF64;
-    const int64_t u_bytes = round256((int64_t)total_tokens * conv_dim * (u_dtype == m2::kF64 ? 8 : 4));
+    const int ues = u_dtype == m2::kF64 ? 8 : 4;
+    const int64_t u_bytes = round256((int64_t)total_tokens * conv_dim * ues);
+    const int64_t ypre_bytes = round256((int64_t)total_tokens * d_x * 4);
     char* wsb = static_cast<char*>(workspace);
     void* u = wsb;
     float* ypre_ws = wsb ? reinterpret_cast<float*>(wsb + u_bytes) : nullptr;
+    const bool chunked = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype) > 0;
+    float* states_ws = (wsb && chunked) ? reinterpret_cast<float*>(wsb + u_bytes + ypre_bytes) : nullptr;
     if ((st = validate_conv(x, ld_x, B, ld_B, C, ld_C, d_x, d_b, act_dtype, conv_w, conv_b, 4,
                             conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
                             state_idx, u ? u : y, conv_dim, M2_F32)))
@@ -365,7 +416,6 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     float* ypre = (y_dtype == M2_F32) ? static_cast<float*>(y) : ypre_ws;
     const int64_t ld_pre = (y_dtype == M2_F32) ? ld_y : d_x;
     m2::ScanArgs sa{};
-    const int ues = u_dtype == m2::kF64 ? 8 : 4;
     sa.x = u; sa.ld_x = conv_dim;
     sa.B = static_cast<char*>(u) + (int64_t)d_x * ues; sa.ld_B = conv_dim;
     sa.C = static_cast<char*>(u) + (int64_t)(d_x + d_b) * ues; sa.ld_C = conv_dim;
@@ -375,9 +425,9 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     sa.cu_seqlens = cu_seqlens; sa.batch = batch; sa.state_idx = state_idx; sa.has_init = has_init;
     sa.nheads = nheads; sa.headdim = headdim; sa.dstate = dstate; sa.ngroups = ngroups;
     sa.chunk = chunk_size; sa.y = ypre; sa.ld_y = ld_pre;
-    if ((st = hip_status(m2::launch_ssd_scan(sa, s), "prefill scan launch"))) return st;
-    (sa.policy == m2::kPolicyBf16x3 ? g_counters.scan_bf16x3 : g_counters.scan_f64)++;
-    mark(3);
+    sa.states = states_ws;
+    if ((st = launch_scan(sa, total_tokens, s, tev ? tev[3] : nullptr))) return st;
+    mark(4);
 
     if (total_tokens > 0) {
         m2::NormArgs na{};
@@ -388,7 +438,7 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
         if ((st = hip_status(m2::launch_gated_norm(na, s), "prefill norm launch"))) return st;
         g_counters.norm++;
     }
-    mark(4);
+    mark(5);
     g_counters.prefill++;
     return ok();
 }
@@ -400,7 +450,7 @@ int m2_timing_enable(int max_calls) {
     g_timing.used = 0;
     g_timing.max_calls = 0;
     if (max_calls == 0) return ok();
-    g_timing.ev.resize((size_t)5 * max_calls);
+    g_timing.ev.resize((size_t)kEv * max_calls);
     for (auto& e : g_timing.ev) {
         const hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -415,12 +465,13 @@ int m2_timing_enable(int max_calls) {
 int m2_timing_read(m2_kernel_times* out) {
     if (!out) return fail(M2_ERR_NULL, "m2_timing_read: out is NULL");
     *out = m2_kernel_times{};
-    double* dst[4] = {&out->conv_ms, &out->conv_state_ms, &out->scan_ms, &out->norm_ms};
+    double* dst[kEv - 1] = {&out->conv_ms, &out->conv_state_ms, &out->scan_pass_ms, &out->scan_out_ms,
+                            &out->norm_ms};
     for (int c = 0; c < g_timing.used; ++c) {
-        hipEvent_t* e = &g_timing.ev[5 * c];
-        const hipError_t r = hipEventSynchronize(e[4]);
+        hipEvent_t* e = &g_timing.ev[kEv * c];
+        const hipError_t r = hipEventSynchronize(e[kEv - 1]);
         if (r != hipSuccess) return fail(M2_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(r));
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kEv - 1; ++k) {
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, e[k], e[k + 1]) != hipSuccess) ms = 0.f;
             *dst[k] += ms;

@@ -1,0 +1,646 @@
+// Chunk-parallel selective scan (Mamba-2 SSD) for bf16 activations on gfx950:
+// headdim 64, dstate 64 or 128, chunks of 128 rows.
+//
+// The chunk formulas are those of page "perf(nemotron_h): prefill single-GPU
+// prompts in multi-token chunks", section Implementation: a_t = dt_t * A,
+// gamma the inclusive cumulative sum of a over the chunk, gamma_S its last
+// element, every exponent clamped at 0 (e(v) = exp(min(v, 0))):
+//   y_t   = e(gamma_t) C_t . h_in + sum_{i<=t} e(gamma_t - gamma_i) (C_t . B_i) dt_i x_i + D x_t
+//   h_out = e(gamma_S) h_in + sum_i e(gamma_S - gamma_i) dt_i x_i (outer) B_i
+// The only sequential dependence between chunks is h_in, so the work splits in
+// two kernels:
+//
+//  state pass  one workgroup per (sequence, head) walks the chunks in order and
+//              keeps h^T [N x P] in matrix-core accumulators.  Per chunk it
+//              writes h_in to the entry-state buffer, scales the accumulators by
+//              e(gamma_S) and adds B^T (dt e(gamma_S - gamma_i) x) with the
+//              accumulators as the running sum.  Only B, x and dt are read.
+//  chunk out   one workgroup per (chunk, group), all chunks at once.  It forms
+//              G^T = B C^T once for the group's heads, then for each head
+//              y^T = e(gamma_t) (h_in C^T) + X^T M^T with
+//              M^T[i, t] = G^T[i, t] dt_i e(gamma_t - gamma_i) (i <= t) and D on
+//              the diagonal, and stores y.
+//
+// Operands: x, B and C are bf16 already, so they feed the bf16 matrix
+// instructions exactly.  The computed operands (dt-weighted x, M^T, h_in) are
+// split as v = hi + lo (hi = bf16(v), lo = bf16(v - hi)) and enter two products
+// (hi and lo), so every product is exact to ~2^-17 relative with fp32
+// accumulation.  Cumulative sums of a are fp64, exponent differences fp64,
+// clamped, then exp'd in fp32.
+//
+// Matrix-core tile layout (16x16x32 bf16): an A operand lane l holds row l%16
+// and K slots 8(l/16)..8(l/16)+7; a B operand lane holds column l%16 and the
+// same K slots; the 16x16 fp32 result lands with lane l holding column l%16 and
+// rows 4(l/16)+r in register r.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace m2 {
+namespace {
+
+constexpr int Q = 128;     // chunk rows
+constexpr int P = 64;      // headdim
+constexpr int RS = Q + 8;  // LDS row stride (bf16 elements) of token-indexed rows: 272 bytes
+
+typedef uint16_t u16;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint4 lds128(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 lds64(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Half e (0 = low) of the bf16 pair packed in w.
+__device__ __forceinline__ uint32_t half_of(uint32_t w, int e) { return e ? (w >> 16) : (w & 0xffffu); }
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// bf16 bits of the high and low parts of v.
+__device__ __forceinline__ void split_bits(float v, uint32_t& hi, uint32_t& lo) {
+    const __bf16 h = static_cast<__bf16>(v);
+    const __bf16 l = static_cast<__bf16>(v - static_cast<float>(h));
+    hi = __builtin_bit_cast(u16, h);
+    lo = __builtin_bit_cast(u16, l);
+}
+
+// Inclusive prefix sum of a = dt * A over the 128 rows of a chunk on one wave:
+// lane l holds rows 2l and 2l+1 (dt already 0 beyond the chunk's rows).
+__device__ __forceinline__ void gamma_scan(float d0, float d1, float Ah, int lane, double& g0, double& g1) {
+    const double a0 = (double)d0 * (double)Ah;
+    const double a1 = (double)d1 * (double)Ah;
+    double v = a0 + a1;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const double t = __shfl_up(v, s, 64);
+        if (lane >= s) v += t;
+    }
+    double run = __shfl_up(v, 1, 64);
+    if (lane == 0) run = 0.0;
+    g0 = run + a0;
+    g1 = g0 + a1;
+}
+
+__device__ __forceinline__ float expc(double v) { return __expf(static_cast<float>(fmin(v, 0.0))); }
+
+// Workgroup -> (sequence, head), with the heads of one group of one sequence on
+// one XCD (workgroups are dealt round-robin over the 8 XCDs), so the group's
+// B rows are shared through that XCD's L2.
+__device__ __forceinline__ int item_of(int lin, int total) {
+    return (total % 8 == 0) ? (lin % 8) * (total / 8) + lin / 8 : lin;
+}
+
+// Inputs come as bf16 (8 channels per 16-byte load, exact in bf16) or fp32 (4
+// channels per load, entering the products as a (hi, lo) pair).
+template <typename Tin>
+struct In {
+    static constexpr bool kSplit = sizeof(Tin) == 4;
+    static constexpr int CPL = 16 / (int)sizeof(Tin);
+    __device__ __forceinline__ static float val(const uint4& v, int j) {
+        if constexpr (kSplit) return __builtin_bit_cast(float, word_of(v, j));
+        else return bf16_bits_to_f32((u16)half_of(word_of(v, j >> 1), j & 1));
+    }
+};
+
+// acc += a b over (hi, lo) operands: the lo x lo term (~2^-18 relative) is dropped,
+// and a lo part that is known to be zero (SA / SB false) is skipped.
+template <bool SA, bool SB>
+__device__ __forceinline__ void mma2(f32x4_t& acc, bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl) {
+    if constexpr (SA) acc = mfma(al, bh, acc);
+    if constexpr (SB) acc = mfma(ah, bl, acc);
+    acc = mfma(ah, bh, acc);
+}
+
+// 8 values -> packed bf16 high parts and low parts.
+__device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) split_bits(v[k], h[k], l[k]);
+    hi = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    lo = uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+}
+
+// Loads rows k = 0..7 of a staging piece (16 bytes each, zero beyond `valid`).
+template <typename Tin>
+__device__ __forceinline__ void load_rows8(const Tin* base, int64_t ld, int valid, uint4 (&r)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        r[k] = (k < valid) ? *reinterpret_cast<const uint4*>(base + k * ld) : uint4{0u, 0u, 0u, 0u};
+}
+
+// ------------------------------------------------------------------ state pass
+
+template <int N, typename Tin>
+__global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
+    constexpr bool SP = In<Tin>::kSplit;
+    constexpr int CPL = In<Tin>::CPL;
+    constexpr int NTW = N / 64;                 // 16-row n tiles per wave (N/16 tiles over 4 waves)
+    constexpr int NBP = 16 * N / CPL;           // B pieces: 8 tokens x CPL channels
+    constexpr int PB = (NBP + 255) / 256;
+    constexpr int NXP = 16 * P / CPL;           // x pieces
+    __shared__ __align__(16) u16 BTh[N * RS];           // B^T [n][token], high parts
+    __shared__ __align__(16) u16 BTl[SP ? N * RS : 8];  // low parts (fp32 inputs)
+    __shared__ __align__(16) u16 XH[P * RS];            // (w x)^T [p][token], high parts
+    __shared__ __align__(16) u16 XL[P * RS];            // low parts
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
+    const int item = item_of(blockIdx.x, a.nheads * a.batch);
+    const int seq = item / a.nheads, head = item % a.nheads;
+    const int grp = head / (a.nheads / a.ngroups);
+    const int64_t s0 = a.cu_seqlens[seq];
+    const int64_t L = a.cu_seqlens[seq + 1] - s0;
+    const int slot = a.state_idx ? a.state_idx[seq] : seq;
+    const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
+    const float Ah = a.A[head];
+    float* st = a.ssm_state + ((int64_t)slot * a.nheads + head) * (int64_t)(P * N);
+
+    // acc[i][pt] holds h^T tile (n tile NTW*wave + i, p tile pt): lane has
+    // p = 16 pt + l16 and n = 16 (NTW wave + i) + 4q + r, i.e. 4 consecutive n.
+    f32x4_t acc[NTW][4];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            const int off = (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q;
+            if (init && L > 0) {
+                const float4 v = *reinterpret_cast<const float4*>(st + off);
+                acc[i][pt] = f32x4_t{v.x, v.y, v.z, v.w};
+            } else {
+                acc[i][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    if (L <= 0) {
+        // Empty sequence: a fresh slot is still reset, a carried one is untouched.
+        if (!init) {
+#pragma unroll
+            for (int i = 0; i < NTW; ++i)
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    *reinterpret_cast<float4*>(st + (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q) =
+                        float4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
+
+    const int nch = (int)((L + Q - 1) / Q);
+    const int64_t cbase = s0 / Q + seq;   // entry-state slot of the sequence's first chunk
+    const Tin* Xg = static_cast<const Tin*>(a.x);
+    const Tin* Bg = static_cast<const Tin*>(a.B);
+
+    // Staging pieces are 8 consecutive tokens x CPL channels, token group fastest
+    // across lanes so a wave's transposed LDS writes are contiguous.
+    const int tg = tid % 16;
+    uint4 br[PB][8], xr[8];
+    float dr0, dr1;
+    auto prefetch = [&](int c) {
+        const int64_t r0 = s0 + (int64_t)c * Q;
+        const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
+        const int valid = S - 8 * tg;
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int e = tid + 256 * m;
+            if (e < NBP)
+                load_rows8(Bg + (r0 + 8 * tg) * a.ld_B + grp * N + (e / 16) * CPL, a.ld_B, valid, br[m]);
+        }
+        if (tid < NXP)
+            load_rows8(Xg + (r0 + 8 * tg) * a.ld_x + (int64_t)head * P + (tid / 16) * CPL, a.ld_x, valid, xr);
+        dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
+        dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
+    };
+    prefetch(0);
+
+    for (int c = 0; c < nch; ++c) {
+        const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
+
+        // gamma over the chunk (every wave), weights w_i = dt_i e(gamma_S - gamma_i)
+        double g0, g1;
+        gamma_scan(dr0, dr1, Ah, lane, g0, g1);
+        const double gS = __shfl(((S - 1) & 1) ? g1 : g0, (S - 1) >> 1, 64);
+        const float w0 = dr0 * expc(gS - g0);
+        const float w1 = dr1 * expc(gS - g1);
+        const float decay = expc(gS);
+        // weights of this thread's staging rows 8 tg + k (held by lane 4 tg + k / 2)
+        float wx[8];
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+            wx[k] = __shfl(w0, 4 * tg + k / 2, 64);
+            wx[k + 1] = __shfl(w1, 4 * tg + k / 2, 64);
+        }
+
+        __syncthreads();  // the previous chunk's products are done with the LDS tiles
+
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int e = tid + 256 * m;
+            if (e < NBP) {
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const int off = ((e / 16) * CPL + j) * RS + 8 * tg;
+                    if constexpr (SP) {
+                        float v[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) v[k] = In<Tin>::val(br[m][k], j);
+                        uint4 hi, lo;
+                        split8(v, hi, lo);
+                        *reinterpret_cast<uint4*>(BTh + off) = hi;
+                        *reinterpret_cast<uint4*>(BTl + off) = lo;
+                    } else {
+                        uint32_t hb[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) hb[k] = half_of(word_of(br[m][k], j >> 1), j & 1);
+                        *reinterpret_cast<uint4*>(BTh + off) =
+                            uint4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+                    }
+                }
+            }
+        }
+        if (tid < NXP) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = In<Tin>::val(xr[k], j) * wx[k];
+                uint4 hi, lo;
+                split8(v, hi, lo);
+                const int off = ((tid / 16) * CPL + j) * RS + 8 * tg;
+                *reinterpret_cast<uint4*>(XH + off) = hi;
+                *reinterpret_cast<uint4*>(XL + off) = lo;
+            }
+        }
+        if (c + 1 < nch) prefetch(c + 1);
+
+        // entry state of this chunk, then h <- e(gamma_S) h
+        float* he = a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int off = (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q;
+                *reinterpret_cast<float4*>(he + off) =
+                    float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
+                acc[i][pt] *= decay;
+            }
+        __syncthreads();
+
+        // h^T += B^T (w x): A = B^T rows n, B = (w x) columns p, K = tokens
+        const int nkb = (S + 31) >> 5;
+#pragma unroll
+        for (int k = 0; k < Q / 32; ++k) {
+            if (k < nkb) {
+                bf16x8_t xh[4], xl[4];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    xh[pt] = as_bf16x8(lds128(XH + (16 * pt + l16) * RS + 32 * k + 8 * q));
+                    xl[pt] = as_bf16x8(lds128(XL + (16 * pt + l16) * RS + 32 * k + 8 * q));
+                }
+#pragma unroll
+                for (int i = 0; i < NTW; ++i) {
+                    const int row = (16 * (NTW * wave + i) + l16) * RS + 32 * k + 8 * q;
+                    const bf16x8_t bh = as_bf16x8(lds128(BTh + row));
+                    const bf16x8_t bl = SP ? as_bf16x8(lds128(BTl + (SP ? row : 0))) : bh;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) mma2<SP, true>(acc[i][pt], bh, bl, xh[pt], xl[pt]);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+            *reinterpret_cast<float4*>(st + (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q) =
+                float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
+}
+
+// ------------------------------------------------------------------ chunk out
+
+template <int N, typename Tin>
+__global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
+    constexpr bool SP = In<Tin>::kSplit;
+    constexpr int CPL = In<Tin>::CPL;
+    constexpr int NKB = N / 32;        // K blocks over n
+    constexpr int NPASS = N / 64;      // B, C staged 64 n at a time
+    constexpr int HR = 64 + 8;         // LDS row stride of a staged 64-n slice
+    constexpr int NRS = N + 8;         // LDS row stride of the h_in planes
+    constexpr int STAGE = (SP ? 4 : 2) * Q * HR;
+    constexpr int HEAD = (SP ? 2 : 1) * P * RS + 2 * P * NRS;
+    constexpr int SMEM = STAGE > HEAD ? STAGE : HEAD;
+    constexpr int NXP = 16 * P / CPL;  // x pieces: 8 tokens x CPL columns
+    __shared__ __align__(16) u16 smem[SMEM];
+    __shared__ __align__(16) double gam[Q];
+    __shared__ __align__(16) float dts[Q];
+    __shared__ __align__(16) float din[Q];
+    // staging of one 64-n slice of B and C rows (natural [row][n] order)
+    u16* Bh = smem;
+    u16* Ch = smem + Q * HR;
+    u16* Bl = smem + 2 * Q * HR;
+    u16* Cl = smem + 3 * Q * HR;
+    // per head: x^T [p][i] planes and the h_in planes [p][n]
+    u16* Xh = smem;
+    u16* Xl = smem + P * RS;
+    u16* HH = smem + (SP ? 2 : 1) * P * RS;
+    u16* HL = HH + P * NRS;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
+    const int G = a.ngroups;
+    const int hpg = a.nheads / G;
+    const int cslot = blockIdx.x / G;
+    const int grp = blockIdx.x % G;
+
+    // chunk slot -> (sequence, chunk): sequence b owns slots cu[b]/Q + b + c
+    int lo = 0, hi = a.batch;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu_seqlens[mid] / Q + mid <= cslot) lo = mid; else hi = mid;
+    }
+    const int seq = lo;
+    const int64_t s0 = a.cu_seqlens[seq];
+    const int64_t L = a.cu_seqlens[seq + 1] - s0;
+    const int64_t c = cslot - (s0 / Q + seq);
+    if (c * Q >= L) return;
+    const int S = (int)((L - c * Q) < Q ? (L - c * Q) : Q);
+    const int64_t r0 = s0 + c * Q;
+
+    const Tin* Xg = static_cast<const Tin*>(a.x);
+    const Tin* Bg = static_cast<const Tin*>(a.B);
+    const Tin* Cg = static_cast<const Tin*>(a.C);
+
+    // per-head staging registers: x piece (8 tokens x CPL columns), h_in, dt
+    const int tg = tid % 16;
+    uint4 xr[8];
+    float4 hr[(P * N / 4) / 256];
+    float dr0 = 0.f, dr1 = 0.f;
+    auto prefetch = [&](int head) {
+        if (tid < NXP)
+            load_rows8(Xg + (r0 + 8 * tg) * a.ld_x + (int64_t)head * P + (tid / 16) * CPL, a.ld_x, S - 8 * tg, xr);
+        const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+        for (int k = 0; k < (P * N / 4) / 256; ++k)
+            hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + 256 * k));
+        if (wave == 0) {
+            dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
+            dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
+        }
+    };
+    prefetch(grp * hpg);
+
+    // Wave w owns t tiles T0 = w and T1 = 7 - w (9 causal i tiles between them).
+    const int T0 = wave, T1 = 7 - wave;
+    const bool act0 = 16 * T0 < S, act1 = 16 * T1 < S;
+    // C operands of the two t tiles (column t, K = n), kept for every head
+    bf16x8_t ch[2][NKB], cl[2][NKB];
+    // G^T[i, t] = B_i . C_t for i tile it <= T: g[0][it] (T0 <= 3, so it < 4), g[1][it]
+    f32x4_t g[2][8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        g[0][it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        g[1][it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+        if (ps > 0) __syncthreads();   // the previous slice's products are done
+        constexpr int PPR = 64 / CPL;  // pieces per 64-n row slice
+        for (int e = tid; e < Q * PPR; e += 256) {
+            const int i = e / PPR, o = e % PPR;
+            const int64_t col = grp * N + 64 * ps + o * CPL;
+            uint4 vb = uint4{0u, 0u, 0u, 0u}, vc = vb;
+            if (i < S) {
+                vb = *reinterpret_cast<const uint4*>(Bg + (r0 + i) * a.ld_B + col);
+                vc = *reinterpret_cast<const uint4*>(Cg + (r0 + i) * a.ld_C + col);
+            }
+            const int off = i * HR + o * CPL;
+            if constexpr (SP) {
+                uint32_t bh4[4], bl4[4], ch4[4], cl4[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    split_bits(In<Tin>::val(vb, j), bh4[j], bl4[j]);
+                    split_bits(In<Tin>::val(vc, j), ch4[j], cl4[j]);
+                }
+                *reinterpret_cast<uint2*>(Bh + off) = uint2{bh4[0] | (bh4[1] << 16), bh4[2] | (bh4[3] << 16)};
+                *reinterpret_cast<uint2*>(Bl + off) = uint2{bl4[0] | (bl4[1] << 16), bl4[2] | (bl4[3] << 16)};
+                *reinterpret_cast<uint2*>(Ch + off) = uint2{ch4[0] | (ch4[1] << 16), ch4[2] | (ch4[3] << 16)};
+                *reinterpret_cast<uint2*>(Cl + off) = uint2{cl4[0] | (cl4[1] << 16), cl4[2] | (cl4[3] << 16)};
+            } else {
+                *reinterpret_cast<uint4*>(Bh + off) = vb;
+                *reinterpret_cast<uint4*>(Ch + off) = vc;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int k = 2 * ps + k2;
+            ch[0][k] = as_bf16x8(lds128(Ch + (16 * T0 + l16) * HR + 32 * k2 + 8 * q));
+            ch[1][k] = as_bf16x8(lds128(Ch + (16 * T1 + l16) * HR + 32 * k2 + 8 * q));
+            if constexpr (SP) {
+                cl[0][k] = as_bf16x8(lds128(Cl + (16 * T0 + l16) * HR + 32 * k2 + 8 * q));
+                cl[1][k] = as_bf16x8(lds128(Cl + (16 * T1 + l16) * HR + 32 * k2 + 8 * q));
+            } else {
+                cl[0][k] = ch[0][k];
+                cl[1][k] = ch[1][k];
+            }
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                if (16 * it < S) {
+                    const bool do0 = it < 4 && it <= T0 && act0, do1 = it <= T1 && act1;
+                    if (do0 || do1) {
+                        const int row = (16 * it + l16) * HR + 32 * k2 + 8 * q;
+                        const bf16x8_t bh = as_bf16x8(lds128(Bh + row));
+                        const bf16x8_t bl = SP ? as_bf16x8(lds128(Bl + (SP ? row : 0))) : bh;
+                        if (it < 4 && do0) mma2<SP, SP>(g[0][it], bh, bl, ch[0][k], cl[0][k]);
+                        if (do1) mma2<SP, SP>(g[1][it], bh, bl, ch[1][k], cl[1][k]);
+                    }
+                }
+            }
+        }
+    }
+
+    for (int j = 0; j < hpg; ++j) {
+        const int head = grp * hpg + j;
+        const float Ah = a.A[head];
+        const float Dh = a.D ? a.D[head] : 0.f;
+        double ga0 = 0.0, ga1 = 0.0;
+        if (wave == 0) gamma_scan(dr0, dr1, Ah, lane, ga0, ga1);
+
+        __syncthreads();  // B / C slices (first head) or the previous head's tiles are no longer read
+
+        // x^T planes: column (tid / 16) * CPL + jj, tokens 8 tg .. +7
+        if (tid < NXP) {
+#pragma unroll
+            for (int jj = 0; jj < CPL; ++jj) {
+                const int off = ((tid / 16) * CPL + jj) * RS + 8 * tg;
+                if constexpr (SP) {
+                    float v[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) v[k] = In<Tin>::val(xr[k], jj);
+                    uint4 hi4, lo4;
+                    split8(v, hi4, lo4);
+                    *reinterpret_cast<uint4*>(Xh + off) = hi4;
+                    *reinterpret_cast<uint4*>(Xl + off) = lo4;
+                } else {
+                    uint32_t hb[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) hb[k] = half_of(word_of(xr[k], jj >> 1), jj & 1);
+                    *reinterpret_cast<uint4*>(Xh + off) =
+                        uint4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+                }
+            }
+        }
+        // h_in split planes: float4 k covers p = idx / N, n = idx % N .. +3
+#pragma unroll
+        for (int k = 0; k < (P * N / 4) / 256; ++k) {
+            const int idx = 4 * (tid + 256 * k);
+            const int p = idx / N, n = idx % N;
+            uint32_t hb[4], lb[4];
+            split_bits(hr[k].x, hb[0], lb[0]);
+            split_bits(hr[k].y, hb[1], lb[1]);
+            split_bits(hr[k].z, hb[2], lb[2]);
+            split_bits(hr[k].w, hb[3], lb[3]);
+            *reinterpret_cast<uint2*>(HH + p * NRS + n) = uint2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+            *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+        }
+        if (wave == 0) {
+            gam[2 * lane] = ga0;
+            gam[2 * lane + 1] = ga1;
+            dts[2 * lane] = dr0;
+            dts[2 * lane + 1] = dr1;
+            din[2 * lane] = expc(ga0);
+            din[2 * lane + 1] = expc(ga1);
+        }
+        if (j + 1 < hpg) prefetch(head + 1);
+        __syncthreads();
+
+        // y^T[p, t] tiles: yacc[ti][pt], lane has t = 16 T + l16, p = 16 pt + 4q + r
+        f32x4_t yacc[2][4];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) yacc[ti][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // inter-chunk term: h_in C^T (A = h_in rows p, B = C columns t, K = n)
+#pragma unroll
+        for (int k = 0; k < NKB; ++k) {
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const bf16x8_t ah = as_bf16x8(lds128(HH + (16 * pt + l16) * NRS + 32 * k + 8 * q));
+                const bf16x8_t al = as_bf16x8(lds128(HL + (16 * pt + l16) * NRS + 32 * k + 8 * q));
+                if (act0) mma2<true, SP>(yacc[0][pt], ah, al, ch[0][k], cl[0][k]);
+                if (act1) mma2<true, SP>(yacc[1][pt], ah, al, ch[1][k], cl[1][k]);
+            }
+        }
+        const float s0f = din[16 * T0 + l16], s1f = din[16 * T1 + l16];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            yacc[0][pt] *= s0f;
+            yacc[1][pt] *= s1f;
+        }
+
+        // intra-chunk term: X^T M^T over i tile pairs (2kb, 2kb+1); the M^T
+        // operand slot j < 4 is row 4q + j of tile 2kb, j >= 4 row 4q + j - 4 of
+        // tile 2kb + 1 (the rows this lane's accumulators hold), so x is read
+        // in that row order.
+        auto intra = [&](const f32x4_t (&gt_)[8], int ti, int T, int ntile_max) __attribute__((always_inline)) {
+            const int t = 16 * T + l16;
+            const double gt = gam[t];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (2 * kb <= T && 2 * kb < ntile_max) {
+                    float m[8];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int it = 2 * kb + h2;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = 16 * it + 4 * q + r;
+                            float v = 0.f;
+                            if (it <= T && i <= t) {
+                                v = gt_[it][r] * dts[i] * expc(gt - gam[i]);
+                                if (i == t) v += Dh;
+                            }
+                            m[4 * h2 + r] = v;
+                        }
+                    }
+                    bf16x8_t mh, ml;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const __bf16 hh = static_cast<__bf16>(m[e]);
+                        mh[e] = hh;
+                        ml[e] = static_cast<__bf16>(m[e] - static_cast<float>(hh));
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const int xo = (16 * pt + l16) * RS + 32 * kb + 4 * q;
+                        const uint2 a0 = lds64(Xh + xo), a1 = lds64(Xh + xo + 16);
+                        const bf16x8_t xh = as_bf16x8(uint4{a0.x, a0.y, a1.x, a1.y});
+                        bf16x8_t xl = xh;
+                        if constexpr (SP) {
+                            const uint2 b0 = lds64(Xl + xo), b1 = lds64(Xl + xo + 16);
+                            xl = as_bf16x8(uint4{b0.x, b0.y, b1.x, b1.y});
+                        }
+                        mma2<SP, true>(yacc[ti][pt], xh, xl, mh, ml);
+                    }
+                }
+            }
+        };
+        if (act0) intra(g[0], 0, T0, 4);
+        if (act1) intra(g[1], 1, T1, 8);
+
+        // store y rows of the chunk: lane has y[t][16 pt + 4q .. +3]
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            const int t = 16 * (ti ? T1 : T0) + l16;
+            if (t < S) {
+                float* dst = a.y + (r0 + t) * a.ld_y + (int64_t)head * P + 4 * q;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    *reinterpret_cast<float4*>(dst + 16 * pt) =
+                        float4{yacc[ti][pt][0], yacc[ti][pt][1], yacc[ti][pt][2], yacc[ti][pt][3]};
+            }
+        }
+    }
+}
+
+template <int N, typename Tin>
+hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((ssd_state_pass_kernel<N, Tin>), dim3(a.nheads * a.batch), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int N, typename Tin>
+hipError_t launch_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream) {
+    const int64_t slots = total_tokens / Q + a.batch;
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Tin>), dim3((unsigned)(slots * a.ngroups)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunked_scan_supported(int policy, int headdim, int dstate, int chunk) {
+    return policy == kPolicyBf16x3 && headdim == P && (dstate == 64 || dstate == 128) && chunk == Q;
+}
+
+size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate) {
+    return (size_t)(total_tokens / Q + batch) * (size_t)nheads * (size_t)headdim * (size_t)dstate * sizeof(float);
+}
+
+hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream) {
+    const bool f = a.act_dtype == kF32;
+    if (a.dstate == 128) return f ? launch_pass<128, float>(a, stream) : launch_pass<128, u16>(a, stream);
+    if (a.dstate == 64) return f ? launch_pass<64, float>(a, stream) : launch_pass<64, u16>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream) {
+    const bool f = a.act_dtype == kF32;
+    if (a.dstate == 128) return f ? launch_out<128, float>(a, total_tokens, stream) : launch_out<128, u16>(a, total_tokens, stream);
+    if (a.dstate == 64) return f ? launch_out<64, float>(a, total_tokens, stream) : launch_out<64, u16>(a, total_tokens, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace m2

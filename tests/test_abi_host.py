@@ -22,8 +22,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("mamba2_conv_rows", "ssd_chunk_scan", "gated_rmsnorm_group", "mamba2_prefill",
-              "mamba2_prefill_workspace_size", "m2_last_error", "m2_get_counters"):
+    for n in ("mamba2_conv_rows", "ssd_chunk_scan", "ssd_chunk_scan_workspace_size",
+              "gated_rmsnorm_group", "mamba2_prefill", "mamba2_prefill_workspace_size",
+              "m2_last_error", "m2_get_counters"):
         assert n in names
 
 
@@ -42,19 +43,26 @@ def test_version_and_counters():
 def _scan(lib, **kw):
     a = dict(x=16, ld_x=64, B=32, ld_B=32, C=48, ld_C=32, act=0, dt=64, ld_dt=4, A=80, D=None,
              ss=96, n_slots=1, cu=112, batch=1, T=8, maxlen=8, idx=None, init=None,
-             H=4, P=16, N=16, G=2, chunk=16, y=128, ld_y=64)
+             H=4, P=16, N=16, G=2, chunk=16, y=128, ld_y=64, ws=None, ws_bytes=0)
     a.update(kw)
     return lib.ssd_chunk_scan(a["x"], a["ld_x"], a["B"], a["ld_B"], a["C"], a["ld_C"], a["act"],
                               a["dt"], a["ld_dt"], a["A"], a["D"], a["ss"], a["n_slots"], a["cu"],
                               a["batch"], a["T"], a["maxlen"], a["idx"], a["init"], a["H"],
-                              a["P"], a["N"], a["G"], a["chunk"], a["y"], a["ld_y"], None)
+                              a["P"], a["N"], a["G"], a["chunk"], a["y"], a["ld_y"], a["ws"],
+                              a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), -1), (dict(act=7), -3), (dict(chunk=144), -4), (dict(chunk=24), -4),
     (dict(chunk=0), -4), (dict(P=24), -7), (dict(G=3), -2), (dict(ld_x=10), -5),
     (dict(ld_y=60), -5), (dict(B=40), -6), (dict(ld_B=34), -6), (dict(batch=0), -2),
-    (dict(T=100, maxlen=8), -2), (dict(n_slots=0), -2),
+    (dict(T=100, maxlen=8), -2), (dict(n_slots=0), -2), (dict(x=24), -6), (dict(ld_x=66), -6),
+    # bf16, headdim 64, dstate 128, chunk 128 takes the chunk-parallel path, which needs a workspace
+    (dict(act=1, H=4, P=64, N=128, G=1, ld_x=256, ld_B=128, ld_C=128, ld_y=256, chunk=128), -8),
+    (dict(act=1, H=4, P=64, N=128, G=1, ld_x=256, ld_B=128, ld_C=128, ld_y=256, chunk=128,
+          ws=4096, ws_bytes=64), -8),
+    (dict(act=1, H=4, P=64, N=128, G=1, ld_x=256, ld_B=128, ld_C=128, ld_y=256, chunk=128,
+          ws=4104, ws_bytes=1 << 30), -6),
 ])
 def test_scan_rejects_bad_arguments(kw, code):
     """Validation happens on the host: the fake (aligned, never dereferenced) pointers are not touched."""
@@ -86,3 +94,18 @@ def test_workspace_query_and_prefill_workspace_error():
     assert n32 >= 1000 * (4096 + 2048) * 8 + 1000 * 4096 * 4
     assert lib.mamba2_prefill_workspace_size(-1, 1, 1, 64, 64, 128, 8, 128, 1) == 0
     assert lib.mamba2_prefill_workspace_size(10, 1, 10, 64, 64, 128, 8, 128, 5) == 0
+
+
+def test_scan_workspace_query():
+    """Chunk-parallel path: one fp32 state per chunk slot, slots = T // 128 + batch."""
+    lib = m2.load()
+    per_slot = 64 * 64 * 128 * 4
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 1) == (1000 // 128 + 3) * per_slot
+    assert lib.ssd_chunk_scan_workspace_size(4096 * 8, 8, 64, 64, 128, 8, 128, 1) == (256 + 8) * per_slot
+    # paths without workspace: fp32 inputs, other chunk sizes, other shapes
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 0) == 0
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 64, 1) == 0
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 8, 32, 64, 2, 128, 1) == 0
+    # the prefill workspace includes it, plus fp32 activations and the fp32 pre-norm output
+    n = lib.mamba2_prefill_workspace_size(1000, 3, 1000, 64, 64, 128, 8, 128, 1)
+    assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4 + (1000 // 128 + 3) * per_slot

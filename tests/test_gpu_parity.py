@@ -100,6 +100,10 @@ SCAN_CASES = [
     (LayerShape(16, 64, 64, 2), [200, 1, 129], 128),
     (LayerShape(16, 64, 128, 2), [300, 37], 128),
     (LayerShape(16, 64, 128, 1), [161], 64),
+    # chunk-parallel path (bf16): empty, 1-row, exact-multiple and ragged sequences
+    (LayerShape(16, 64, 128, 1), [128, 0, 1, 257, 255], 128),
+    (LayerShape(8, 64, 64, 4), [513, 3, 0], 128),
+    (LayerShape(64, 64, 128, 8), [129, 384], 128),
 ]
 
 
@@ -267,7 +271,8 @@ def test_deterministic_and_counters():
     y2, c2, s2 = gpu_prefill(inp, w.shape, "bf16")
     assert torch.equal(y1, y2) and torch.equal(c1, c2) and torch.equal(s1, s2)
     c = m2.get_counters()
-    assert c["prefill_calls"] == 2 and c["scan_bf16x3_launches"] == 2 and c["scan_f64_launches"] == 0
+    assert c["prefill_calls"] == 2 and c["scan_chunked_launches"] == 2
+    assert c["scan_bf16x3_launches"] == 0 and c["scan_f64_launches"] == 0
     inp0 = make_inputs(WORKLOADS[0], 0)
     gpu_prefill(inp0, WORKLOADS[0].shape, "f32", 16)
     assert m2.get_counters()["scan_f64_launches"] == 1
