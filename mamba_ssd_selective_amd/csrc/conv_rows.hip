@@ -41,6 +41,23 @@ __device__ __forceinline__ const Tin* seg_row(const ConvArgs& a, int seg, int64_
     return static_cast<const Tin*>(a.seg_ptr[seg]) + row * a.seg_ld[seg] + cs;
 }
 
+// Stores of 8 consecutive outputs (16-byte aligned rows).
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ void store8(double* p, const double (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<double2*>(p + 2 * k) = double2{v[2 * k], v[2 * k + 1]};
+}
+
 // Computes in fp64 when the output is fp64 (the fp32-input prefill path), else fp32.
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
@@ -66,6 +83,53 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     int b = seq_of(a.cu_seqlens, a.batch, t0);
     int64_t s0 = a.cu_seqlens[b];
     int64_t s1 = a.cu_seqlens[b + 1];
+    Tout* out = static_cast<Tout*>(a.out);
+
+    if (t0 - 3 >= s0 && t1 <= s1) {
+        // The run and its 3-row halo lie inside one sequence: issue every row's
+        // load up front, then slide the window over registers.
+        // raw 16-byte pieces: one per row for bf16, two for fp32
+        constexpr int PR = (int)sizeof(Tin) / 2;
+        uint4 raw[TOK + 3][PR];
+#pragma unroll
+        for (int k = 0; k < TOK + 3; ++k) {
+            const int64_t t = t0 - 3 + k;
+            if (t < t1) {
+                const uint4* src = reinterpret_cast<const uint4*>(seg_row<Tin>(a, seg, t, cs));
+#pragma unroll
+                for (int h = 0; h < PR; ++h) raw[k][h] = src[h];
+            }
+        }
+        auto val = [&](int k, int c) -> T {
+            if constexpr (sizeof(Tin) == 2) {
+                const uint32_t wd = c < 2 ? raw[k][0].x : c < 4 ? raw[k][0].y : c < 6 ? raw[k][0].z : raw[k][0].w;
+                return (T)__builtin_bit_cast(float, (c & 1) ? (wd & 0xffff0000u) : (wd << 16));
+            } else {
+                const uint4& q4 = raw[k][c >> 2];
+                const int e = c & 3;
+                return (T)__builtin_bit_cast(float, e == 0 ? q4.x : e == 1 ? q4.y : e == 2 ? q4.z : q4.w);
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < TOK; ++k) {
+            const int64_t t = t0 + k;
+            if (t < t1) {
+                T o[CPT];
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    T acc = bias[c];
+                    acc = fma(w[c][0], val(k, c), acc);
+                    acc = fma(w[c][1], val(k + 1, c), acc);
+                    acc = fma(w[c][2], val(k + 2, c), acc);
+                    acc = fma(w[c][3], val(k + 3, c), acc);
+                    o[c] = a.apply_silu ? silu(acc) : acc;
+                }
+                store8(out + t * a.ld_out + c0, o);
+            }
+        }
+        return;
+    }
+
     T win[3][CPT];   // raw rows t-3, t-2, t-1
 
     auto fill_window = [&](int64_t t) {
@@ -90,7 +154,6 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     };
     fill_window(t0);
 
-    Tout* out = static_cast<Tout*>(a.out);
     for (int64_t t = t0; t < t1; ++t) {
         if (t >= s1) {   // entered a later sequence (skip empty ones)
             while (t >= a.cu_seqlens[b + 1]) ++b;
@@ -113,9 +176,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
             win[1][c] = win[2][c];
             win[2][c] = cur[c];
         }
-        Tout* dst = out + t * a.ld_out + c0;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) Act<Tout>::store(dst + c, o[c]);
+        store8(out + t * a.ld_out + c0, o);
     }
 }
 

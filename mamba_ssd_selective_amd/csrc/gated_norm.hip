@@ -5,9 +5,10 @@
 // default here); the other order (gate, then norm) is selected by a flag.  The
 // NemotronH decode page names the op RmsNormGatedGroup(n_groups).
 //
-// HBM-bound: one wavefront per (token, group); lanes stride over the group's
-// channels (4 per load when the group width allows), a butterfly reduction
-// gives the group's mean square, and the same lanes write the result.
+// HBM-bound: one wavefront per (token, group); a butterfly reduction gives the
+// group's mean square and the same lanes write the result.  Group widths that
+// are multiples of 8 with 16-byte aligned rows take the vector kernel (8
+// channels per lane per load); others the scalar one (lanes stride by one).
 
 #include "device_common.h"
 #include "kernels.h"
@@ -66,12 +67,99 @@ __global__ __launch_bounds__(BLOCK) void gated_norm_kernel(NormArgs a) {
     }
 }
 
+// Vector form for group widths that are multiples of 8 with 16-byte aligned
+// rows: lane l handles 8-channel blocks l, l + 64, ... of its (token, group),
+// each one 32-byte fp32 load of y and one 16- or 32-byte load of z.
+template <typename T> __device__ __forceinline__ void load8v(const T* p, float (&v)[8]) { load8(p, v); }
+
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
+}
+
+constexpr int MAXB = 4;   // 8-channel blocks per lane: group width up to 2048
+
+template <typename Tz, typename Tout>
+__global__ __launch_bounds__(BLOCK) void gated_norm_vec_kernel(NormArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * (BLOCK / 64) + (threadIdx.x >> 6);
+    const int gs = a.d_inner / a.ngroups;
+    if (item >= a.total_tokens * a.ngroups) return;
+    const int64_t t = item / a.ngroups;
+    const int j = (int)(item % a.ngroups);
+    const int cbase = j * gs;
+    const int nb = gs / 8;
+    const float* yr = a.y + t * a.ld_y + cbase;
+    const Tz* zr = static_cast<const Tz*>(a.z) + t * a.ld_z + cbase;
+
+    float v[MAXB][8], gate[MAXB][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXB; ++k) {
+        const int b = lane + 64 * k;
+        if (b < nb) {
+            float yv[8], zv[8];
+            load8v(yr + 8 * b, yv);
+            load8v(zr + 8 * b, zv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float g = silu(zv[e]);
+                const float u = a.norm_before_gate ? yv[e] : yv[e] * g;
+                v[k][e] = u;
+                gate[k][e] = g;
+                ss = fmaf(u, u, ss);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float rstd = 1.0f / sqrtf(ss / (float)gs + a.eps);
+
+    Tout* orow = static_cast<Tout*>(a.out) + t * a.ld_out + cbase;
+#pragma unroll
+    for (int k = 0; k < MAXB; ++k) {
+        const int b = lane + 64 * k;
+        if (b < nb) {
+            float wv[8], o[8];
+            load8(a.norm_w + cbase + 8 * b, wv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[e] = v[k][e] * rstd * wv[e];
+                if (a.norm_before_gate) o[e] *= gate[k][e];
+            }
+            store8(orow + 8 * b, o);
+        }
+    }
+}
+
 }  // namespace
+
+static bool gated_norm_vec_ok(const NormArgs& a) {
+    const int gs = a.d_inner / a.ngroups;
+    const int zes = a.z_dtype == kBF16 ? 2 : 4, oes = a.out_dtype == kBF16 ? 2 : 4;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    return gs % 8 == 0 && gs <= 64 * 8 * MAXB && al16(a.y) && al16(a.z) && al16(a.out) && al16(a.norm_w) &&
+           (a.ld_y * 4) % 16 == 0 && (a.ld_z * zes) % 16 == 0 && (a.ld_out * oes) % 16 == 0;
+}
 
 hipError_t launch_gated_norm(const NormArgs& a, hipStream_t stream) {
     const int64_t items = a.total_tokens * a.ngroups;
     const dim3 grid((unsigned)((items + (BLOCK / 64) - 1) / (BLOCK / 64)));
     const bool zb = a.z_dtype == kBF16, ob = a.out_dtype == kBF16;
+    if (gated_norm_vec_ok(a)) {
+        if (zb && ob) hipLaunchKernelGGL((gated_norm_vec_kernel<uint16_t, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
+        else if (zb) hipLaunchKernelGGL((gated_norm_vec_kernel<uint16_t, float>), grid, dim3(BLOCK), 0, stream, a);
+        else if (ob) hipLaunchKernelGGL((gated_norm_vec_kernel<float, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
+        else hipLaunchKernelGGL((gated_norm_vec_kernel<float, float>), grid, dim3(BLOCK), 0, stream, a);
+        return hipGetLastError();
+    }
     if (zb && ob) hipLaunchKernelGGL((gated_norm_kernel<uint16_t, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
     else if (zb) hipLaunchKernelGGL((gated_norm_kernel<uint16_t, float>), grid, dim3(BLOCK), 0, stream, a);
     else if (ob) hipLaunchKernelGGL((gated_norm_kernel<float, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
