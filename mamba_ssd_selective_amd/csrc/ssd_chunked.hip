@@ -33,6 +33,8 @@
 // same K slots; the 16x16 fp32 result lands with lane l holding column l%16 and
 // rows 4(l/16)+r in register r.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -319,11 +321,19 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
 }
 
 // ------------------------------------------------------------------ chunk out
+//
+// 8 waves; wave w owns t tile T = w (w < 4) or 11 - w, so the two waves that
+// share a SIMD (w and w + 4) hold tiles T and 7 - T: 9 causal (i, t) tiles per
+// SIMD.  The decay e(gamma_t - gamma_i) of an off-diagonal tile is the product
+// of a row factor dt_i e(gamma_r - gamma_i) and a column factor
+// e(gamma_t - gamma_r), r the last row of i's tile (both exponents <= 0, so
+// neither factor overflows); diagonal tiles take the exponential per element.
 
 template <int N, typename Tin>
-__global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
+__global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     constexpr bool SP = In<Tin>::kSplit;
     constexpr int CPL = In<Tin>::CPL;
+    constexpr int NT = 512;
     constexpr int NKB = N / 32;        // K blocks over n
     constexpr int NPASS = N / 64;      // B, C staged 64 n at a time
     constexpr int HR = 64 + 8;         // LDS row stride of a staged 64-n slice
@@ -332,16 +342,17 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
     constexpr int HEAD = (SP ? 2 : 1) * P * RS + 2 * P * NRS;
     constexpr int SMEM = STAGE > HEAD ? STAGE : HEAD;
     constexpr int NXP = 16 * P / CPL;  // x pieces: 8 tokens x CPL columns
+    constexpr int NHV = (P * N / 4) / NT;   // float4 of h_in per thread
     __shared__ __align__(16) u16 smem[SMEM];
+    __shared__ __align__(16) float rowf[Q];      // dt_i e(gamma_r(i) - gamma_i)
+    __shared__ __align__(16) float colf[Q * 8];  // [t][it]: e(gamma_t - gamma_r(it)), it below t's tile
     __shared__ __align__(16) double gam[Q];
     __shared__ __align__(16) float dts[Q];
-    __shared__ __align__(16) float din[Q];
-    // staging of one 64-n slice of B and C rows (natural [row][n] order)
+    __shared__ __align__(16) float din[Q];       // e(gamma_t)
     u16* Bh = smem;
     u16* Ch = smem + Q * HR;
     u16* Bl = smem + 2 * Q * HR;
     u16* Cl = smem + 3 * Q * HR;
-    // per head: x^T [p][i] planes and the h_in planes [p][n]
     u16* Xh = smem;
     u16* Xl = smem + P * RS;
     u16* HH = smem + (SP ? 2 : 1) * P * RS;
@@ -375,15 +386,14 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
     // per-head staging registers: x piece (8 tokens x CPL columns), h_in, dt
     const int tg = tid % 16;
     uint4 xr[8];
-    float4 hr[(P * N / 4) / 256];
+    float4 hr[NHV];
     float dr0 = 0.f, dr1 = 0.f;
     auto prefetch = [&](int head) {
         if (tid < NXP)
             load_rows8(Xg + (r0 + 8 * tg) * a.ld_x + (int64_t)head * P + (tid / 16) * CPL, a.ld_x, S - 8 * tg, xr);
         const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
-        for (int k = 0; k < (P * N / 4) / 256; ++k)
-            hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + 256 * k));
+        for (int k = 0; k < NHV; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + NT * k));
         if (wave == 0) {
             dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
             dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
@@ -391,23 +401,20 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
     };
     prefetch(grp * hpg);
 
-    // Wave w owns t tiles T0 = w and T1 = 7 - w (9 causal i tiles between them).
-    const int T0 = wave, T1 = 7 - wave;
-    const bool act0 = 16 * T0 < S, act1 = 16 * T1 < S;
-    // C operands of the two t tiles (column t, K = n), kept for every head
-    bf16x8_t ch[2][NKB], cl[2][NKB];
-    // G^T[i, t] = B_i . C_t for i tile it <= T: g[0][it] (T0 <= 3, so it < 4), g[1][it]
-    f32x4_t g[2][8];
+    const int T = wave < 4 ? wave : 11 - wave;
+    const bool act = 16 * T < S;
+    const int t = 16 * T + l16;          // this lane's output row
+    // C operands of tile T (column t, K = n), kept for every head
+    bf16x8_t ch[NKB], cl[NKB];
+    // G^T[i, t] = B_i . C_t for i tiles it <= T
+    f32x4_t g[8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        g[0][it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        g[1][it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int it = 0; it < 8; ++it) g[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
         if (ps > 0) __syncthreads();   // the previous slice's products are done
         constexpr int PPR = 64 / CPL;  // pieces per 64-n row slice
-        for (int e = tid; e < Q * PPR; e += 256) {
+        for (int e = tid; e < Q * PPR; e += NT) {
             const int i = e / PPR, o = e % PPR;
             const int64_t col = grp * N + 64 * ps + o * CPL;
             uint4 vb = uint4{0u, 0u, 0u, 0u}, vc = vb;
@@ -436,25 +443,16 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int k = 2 * ps + k2;
-            ch[0][k] = as_bf16x8(lds128(Ch + (16 * T0 + l16) * HR + 32 * k2 + 8 * q));
-            ch[1][k] = as_bf16x8(lds128(Ch + (16 * T1 + l16) * HR + 32 * k2 + 8 * q));
-            if constexpr (SP) {
-                cl[0][k] = as_bf16x8(lds128(Cl + (16 * T0 + l16) * HR + 32 * k2 + 8 * q));
-                cl[1][k] = as_bf16x8(lds128(Cl + (16 * T1 + l16) * HR + 32 * k2 + 8 * q));
-            } else {
-                cl[0][k] = ch[0][k];
-                cl[1][k] = ch[1][k];
-            }
+            ch[k] = as_bf16x8(lds128(Ch + t * HR + 32 * k2 + 8 * q));
+            cl[k] = SP ? as_bf16x8(lds128(Cl + (SP ? t * HR + 32 * k2 + 8 * q : 0))) : ch[k];
+            if (act) {
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                if (16 * it < S) {
-                    const bool do0 = it < 4 && it <= T0 && act0, do1 = it <= T1 && act1;
-                    if (do0 || do1) {
+                for (int it = 0; it < 8; ++it) {
+                    if (it <= T && 16 * it < S) {
                         const int row = (16 * it + l16) * HR + 32 * k2 + 8 * q;
                         const bf16x8_t bh = as_bf16x8(lds128(Bh + row));
                         const bf16x8_t bl = SP ? as_bf16x8(lds128(Bl + (SP ? row : 0))) : bh;
-                        if (it < 4 && do0) mma2<SP, SP>(g[0][it], bh, bl, ch[0][k], cl[0][k]);
-                        if (do1) mma2<SP, SP>(g[1][it], bh, bl, ch[1][k], cl[1][k]);
+                        mma2<SP, SP>(g[it], bh, bl, ch[k], cl[k]);
                     }
                 }
             }
@@ -463,10 +461,24 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
 
     for (int j = 0; j < hpg; ++j) {
         const int head = grp * hpg + j;
-        const float Ah = a.A[head];
         const float Dh = a.D ? a.D[head] : 0.f;
+        // wave 0: gamma and the decay factors of this head, from the prefetched dt
         double ga0 = 0.0, ga1 = 0.0;
-        if (wave == 0) gamma_scan(dr0, dr1, Ah, lane, ga0, ga1);
+        float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
+        if (wave == 0) {
+            gamma_scan(dr0, dr1, a.A[head], lane, ga0, ga1);
+            // rows 2 lane, 2 lane + 1 lie in tile lane / 8, whose last row 16 (lane / 8) + 15
+            // is held (as ga1) by lane 8 (lane / 8) + 7
+            const double gr = __shfl(ga1, 8 * (lane >> 3) + 7, 64);
+            rf0 = dr0 * expc(gr - ga0);
+            rf1 = dr1 * expc(gr - ga1);
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const double gri = __shfl(ga1, 8 * it + 7, 64);
+                cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri) : 0.f;
+                cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri) : 0.f;
+            }
+        }
 
         __syncthreads();  // B / C slices (first head) or the previous head's tiles are no longer read
 
@@ -494,8 +506,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
         }
         // h_in split planes: float4 k covers p = idx / N, n = idx % N .. +3
 #pragma unroll
-        for (int k = 0; k < (P * N / 4) / 256; ++k) {
-            const int idx = 4 * (tid + 256 * k);
+        for (int k = 0; k < NHV; ++k) {
+            const int idx = 4 * (tid + NT * k);
             const int p = idx / N, n = idx % N;
             uint32_t hb[4], lb[4];
             split_bits(hr[k].x, hb[0], lb[0]);
@@ -512,58 +524,75 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
             dts[2 * lane + 1] = dr1;
             din[2 * lane] = expc(ga0);
             din[2 * lane + 1] = expc(ga1);
+            rowf[2 * lane] = rf0;
+            rowf[2 * lane + 1] = rf1;
+            *reinterpret_cast<float4*>(colf + 16 * lane) = float4{cf0[0], cf0[1], cf0[2], cf0[3]};
+            *reinterpret_cast<float4*>(colf + 16 * lane + 4) = float4{cf0[4], cf0[5], cf0[6], cf0[7]};
+            *reinterpret_cast<float4*>(colf + 16 * lane + 8) = float4{cf1[0], cf1[1], cf1[2], cf1[3]};
+            *reinterpret_cast<float4*>(colf + 16 * lane + 12) = float4{cf1[4], cf1[5], cf1[6], cf1[7]};
         }
         if (j + 1 < hpg) prefetch(head + 1);
         __syncthreads();
 
-        // y^T[p, t] tiles: yacc[ti][pt], lane has t = 16 T + l16, p = 16 pt + 4q + r
-        f32x4_t yacc[2][4];
+        if (act) {
+            // y^T[p, t] tiles: yacc[pt], lane has t, p = 16 pt + 4q + r
+            f32x4_t yacc[4];
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) yacc[ti][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int pt = 0; pt < 4; ++pt) yacc[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // inter-chunk term: h_in C^T (A = h_in rows p, B = C columns t, K = n)
+            // inter-chunk term: h_in C^T (A = h_in rows p, B = C columns t, K = n)
 #pragma unroll
-        for (int k = 0; k < NKB; ++k) {
+            for (int k = 0; k < NKB; ++k) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const bf16x8_t ah = as_bf16x8(lds128(HH + (16 * pt + l16) * NRS + 32 * k + 8 * q));
-                const bf16x8_t al = as_bf16x8(lds128(HL + (16 * pt + l16) * NRS + 32 * k + 8 * q));
-                if (act0) mma2<true, SP>(yacc[0][pt], ah, al, ch[0][k], cl[0][k]);
-                if (act1) mma2<true, SP>(yacc[1][pt], ah, al, ch[1][k], cl[1][k]);
+                for (int pt = 0; pt < 4; ++pt) {
+                    const bf16x8_t ah = as_bf16x8(lds128(HH + (16 * pt + l16) * NRS + 32 * k + 8 * q));
+                    const bf16x8_t al = as_bf16x8(lds128(HL + (16 * pt + l16) * NRS + 32 * k + 8 * q));
+                    mma2<true, SP>(yacc[pt], ah, al, ch[k], cl[k]);
+                }
             }
-        }
-        const float s0f = din[16 * T0 + l16], s1f = din[16 * T1 + l16];
+            const float sc = din[t];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            yacc[0][pt] *= s0f;
-            yacc[1][pt] *= s1f;
-        }
+            for (int pt = 0; pt < 4; ++pt) yacc[pt] *= sc;
 
-        // intra-chunk term: X^T M^T over i tile pairs (2kb, 2kb+1); the M^T
-        // operand slot j < 4 is row 4q + j of tile 2kb, j >= 4 row 4q + j - 4 of
-        // tile 2kb + 1 (the rows this lane's accumulators hold), so x is read
-        // in that row order.
-        auto intra = [&](const f32x4_t (&gt_)[8], int ti, int T, int ntile_max) __attribute__((always_inline)) {
-            const int t = 16 * T + l16;
-            const double gt = gam[t];
+            // intra-chunk term: X^T M^T over i tile pairs (2kb, 2kb+1); the M^T
+            // operand slot j < 4 is row 4q + j of tile 2kb, j >= 4 row 4q + j - 4
+            // of tile 2kb + 1 (the rows this lane's accumulators hold), so x is
+            // read in that row order.
+            const float4* cft = reinterpret_cast<const float4*>(colf + 8 * t);
+            const float4 cfa = cft[0], cfb = cft[1];
+            const float cfv[8] = {cfa.x, cfa.y, cfa.z, cfa.w, cfb.x, cfb.y, cfb.z, cfb.w};
+            // the tile index is a compile-time constant inside (one instance per tile)
+            auto intra = [&](auto Tc) __attribute__((always_inline)) {
+                constexpr int TT = decltype(Tc)::value;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (2 * kb <= T && 2 * kb < ntile_max) {
+                for (int kb = 0; kb <= TT / 2; ++kb) {
                     float m[8];
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int it = 2 * kb + h2;
+                        const int i0 = 16 * it + 4 * q;
+                        if (it < TT) {
+                            const float4 rf = *reinterpret_cast<const float4*>(rowf + i0);
+                            const float cv = cfv[it];
+                            m[4 * h2 + 0] = g[it][0] * rf.x * cv;
+                            m[4 * h2 + 1] = g[it][1] * rf.y * cv;
+                            m[4 * h2 + 2] = g[it][2] * rf.z * cv;
+                            m[4 * h2 + 3] = g[it][3] * rf.w * cv;
+                        } else if (it == TT) {
+                            const double gt = gam[t];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int i = 16 * it + 4 * q + r;
-                            float v = 0.f;
-                            if (it <= T && i <= t) {
-                                v = gt_[it][r] * dts[i] * expc(gt - gam[i]);
-                                if (i == t) v += Dh;
+                            for (int r = 0; r < 4; ++r) {
+                                const int i = i0 + r;
+                                float v = 0.f;
+                                if (i <= t) {
+                                    v = g[it][r] * dts[i] * expc(gt - gam[i]);
+                                    if (i == t) v += Dh;
+                                }
+                                m[4 * h2 + r] = v;
                             }
-                            m[4 * h2 + r] = v;
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) m[4 * h2 + r] = 0.f;
                         }
                     }
                     bf16x8_t mh, ml;
@@ -583,24 +612,28 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(ScanArgs a) {
                             const uint2 b0 = lds64(Xl + xo), b1 = lds64(Xl + xo + 16);
                             xl = as_bf16x8(uint4{b0.x, b0.y, b1.x, b1.y});
                         }
-                        mma2<SP, true>(yacc[ti][pt], xh, xl, mh, ml);
+                        mma2<SP, true>(yacc[pt], xh, xl, mh, ml);
                     }
                 }
+            };
+            switch (T) {
+                case 0: intra(std::integral_constant<int, 0>{}); break;
+                case 1: intra(std::integral_constant<int, 1>{}); break;
+                case 2: intra(std::integral_constant<int, 2>{}); break;
+                case 3: intra(std::integral_constant<int, 3>{}); break;
+                case 4: intra(std::integral_constant<int, 4>{}); break;
+                case 5: intra(std::integral_constant<int, 5>{}); break;
+                case 6: intra(std::integral_constant<int, 6>{}); break;
+                default: intra(std::integral_constant<int, 7>{}); break;
             }
-        };
-        if (act0) intra(g[0], 0, T0, 4);
-        if (act1) intra(g[1], 1, T1, 8);
 
-        // store y rows of the chunk: lane has y[t][16 pt + 4q .. +3]
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            const int t = 16 * (ti ? T1 : T0) + l16;
+            // store y row t of the chunk: lane has y[t][16 pt + 4q .. +3]
             if (t < S) {
                 float* dst = a.y + (r0 + t) * a.ld_y + (int64_t)head * P + 4 * q;
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
                     *reinterpret_cast<float4*>(dst + 16 * pt) =
-                        float4{yacc[ti][pt][0], yacc[ti][pt][1], yacc[ti][pt][2], yacc[ti][pt][3]};
+                        float4{yacc[pt][0], yacc[pt][1], yacc[pt][2], yacc[pt][3]};
             }
         }
     }
@@ -615,7 +648,7 @@ hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
 template <int N, typename Tin>
 hipError_t launch_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream) {
     const int64_t slots = total_tokens / Q + a.batch;
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Tin>), dim3((unsigned)(slots * a.ngroups)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Tin>), dim3((unsigned)(slots * a.ngroups)), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
