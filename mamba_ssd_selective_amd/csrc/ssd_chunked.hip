@@ -135,19 +135,60 @@ __device__ __forceinline__ void load_rows8(const Tin* base, int64_t ld, int vali
 }
 
 // ------------------------------------------------------------------ state pass
+//
+// 4 waves.  h^T [N x P] lives in matrix-core accumulators: wave w owns n tiles
+// w * NTW .. w * NTW + NTW - 1 and all 4 p tiles.  Each chunk is staged and
+// multiplied in two halves of 64 rows, so the LDS tiles are small enough for
+// two workgroups per CU (one stages while the other multiplies).  The loads of
+// the next half are in flight while the current half is multiplied; they are
+// branch-free (rows clamped into the chunk and zeroed after the load), so the
+// compiler's wait counts stay exact.
+
+constexpr int QH = Q / 2;        // rows per staged half
+constexpr int RH = QH + 8;       // LDS row stride (bf16) of token-indexed half rows: 144 bytes
+
+template <typename Tin, int TB, int TX>
+struct HalfBuf {
+    uint4 br[TB];      // B piece: TB tokens x CPL channels
+    uint4 xr[TX];      // x piece: TX tokens x CPL columns
+};
+
+template <int K, typename Tin>
+__device__ __forceinline__ void load_rows_clamped(const Tin* base, int64_t ld, int valid, uint4 (&r)[K]) {
+    const int last = valid < 1 ? 0 : valid - 1;
+#pragma unroll
+    for (int k = 0; k < K; ++k) r[k] = *reinterpret_cast<const uint4*>(base + (k < last ? k : last) * ld);
+}
+
+// Packs the TB values of channel j of a staged piece (rows = tokens) as bf16
+// bits, low token in the low half.
+template <int TB>
+__device__ __forceinline__ void pack_tokens(const uint32_t (&h)[TB], uint32_t (&w)[(TB + 1) / 2]) {
+#pragma unroll
+    for (int m = 0; m < TB / 2; ++m) w[m] = h[2 * m] | (h[2 * m + 1] << 16);
+}
+
+template <int TB>
+__device__ __forceinline__ void store_tokens(u16* dst, const uint32_t (&w)[(TB + 1) / 2]) {
+    if constexpr (TB == 8) *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
+    else if constexpr (TB == 4) *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+    else *reinterpret_cast<uint32_t*>(dst) = w[0];
+}
 
 template <int N, typename Tin>
-__global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     constexpr bool SP = In<Tin>::kSplit;
     constexpr int CPL = In<Tin>::CPL;
-    constexpr int NTW = N / 64;                 // 16-row n tiles per wave (N/16 tiles over 4 waves)
-    constexpr int NBP = 16 * N / CPL;           // B pieces: 8 tokens x CPL channels
-    constexpr int PB = (NBP + 255) / 256;
-    constexpr int NXP = 16 * P / CPL;           // x pieces
-    __shared__ __align__(16) u16 BTh[N * RS];           // B^T [n][token], high parts
-    __shared__ __align__(16) u16 BTl[SP ? N * RS : 8];  // low parts (fp32 inputs)
-    __shared__ __align__(16) u16 XH[P * RS];            // (w x)^T [p][token], high parts
-    __shared__ __align__(16) u16 XL[P * RS];            // low parts
+    constexpr int NT = 256;
+    constexpr int NTW = N / 64;                        // n tiles per wave
+    constexpr int TB = QH * N / (CPL * NT);            // tokens per B piece (one piece per thread)
+    constexpr int TX = QH * P / (CPL * NT);            // tokens per x piece
+    constexpr int BG = QH / TB, XG = QH / TX;          // token groups (fastest across lanes)
+    static_assert(TB >= 2 && TX >= 2, "staging pieces");
+    __shared__ __align__(16) u16 BTh[N * RH];           // B^T [n][token of the half], high parts
+    __shared__ __align__(16) u16 BTl[SP ? N * RH : 8];  // low parts (fp32 inputs)
+    __shared__ __align__(16) u16 XH[P * RH];            // (w x)^T [p][token], high parts
+    __shared__ __align__(16) u16 XL[P * RH];            // low parts
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
@@ -161,16 +202,16 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
     const float Ah = a.A[head];
     float* st = a.ssm_state + ((int64_t)slot * a.nheads + head) * (int64_t)(P * N);
 
-    // acc[i][pt] holds h^T tile (n tile NTW*wave + i, p tile pt): lane has
-    // p = 16 pt + l16 and n = 16 (NTW wave + i) + 4q + r, i.e. 4 consecutive n.
+    // acc[i][pt]: h^T tile (n tile NTW wave + i, p tile pt); lane has p = 16 pt + l16
+    // and n = 16 (NTW wave + i) + 4q + r, i.e. 4 consecutive n.
+    auto soff = [&](int i, int pt) { return (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q; };
     f32x4_t acc[NTW][4];
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-            const int off = (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q;
             if (init && L > 0) {
-                const float4 v = *reinterpret_cast<const float4*>(st + off);
+                const float4 v = *reinterpret_cast<const float4*>(st + soff(i, pt));
                 acc[i][pt] = f32x4_t{v.x, v.y, v.z, v.w};
             } else {
                 acc[i][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -182,9 +223,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
 #pragma unroll
             for (int i = 0; i < NTW; ++i)
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    *reinterpret_cast<float4*>(st + (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q) =
-                        float4{0.f, 0.f, 0.f, 0.f};
+                for (int pt = 0; pt < 4; ++pt) *reinterpret_cast<float4*>(st + soff(i, pt)) = float4{0.f, 0.f, 0.f, 0.f};
         }
         return;
     }
@@ -194,115 +233,92 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
     const Tin* Xg = static_cast<const Tin*>(a.x);
     const Tin* Bg = static_cast<const Tin*>(a.B);
 
-    // Staging pieces are 8 consecutive tokens x CPL channels, token group fastest
-    // across lanes so a wave's transposed LDS writes are contiguous.
-    const int tg = tid % 16;
-    uint4 br[PB][8], xr[8];
-    float dr0, dr1;
-    auto prefetch = [&](int c) {
+    const int b_tg = tid % BG, b_cg = tid / BG;   // B piece: tokens TB b_tg.., channels CPL b_cg..
+    const int x_tg = tid % XG, x_cg = tid / XG;   // x piece
+
+    // Loads of half h (0, 1) of chunk c, clamped to the last chunk so the call is
+    // unconditional; rows beyond the chunk re-read its last row (zeroed later).
+    auto load_half = [&](HalfBuf<Tin, TB, TX>& b, int c, int h) __attribute__((always_inline)) {
+        c = c < nch ? c : nch - 1;
+        const int64_t left = L - (int64_t)c * Q - h * QH;     // rows of the sequence from this half on
+        const int S = (int)(left < QH ? left : QH);
+        // an empty half (the chunk ends in its first half) reads the chunk's first row
+        const int64_t r0 = s0 + (int64_t)c * Q + (S > 0 ? h * QH : 0);
+        const int rb = TB * b_tg < S ? TB * b_tg : 0;
+        load_rows_clamped<TB>(Bg + (r0 + rb) * a.ld_B + grp * N + b_cg * CPL, a.ld_B, S - rb, b.br);
+        const int rx = TX * x_tg < S ? TX * x_tg : 0;
+        load_rows_clamped<TX>(Xg + (r0 + rx) * a.ld_x + (int64_t)head * P + x_cg * CPL, a.ld_x, S - rx, b.xr);
+    };
+    auto load_dt = [&](int c, float& d0, float& d1) __attribute__((always_inline)) {
+        c = c < nch ? c : nch - 1;
         const int64_t r0 = s0 + (int64_t)c * Q;
         const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
-        const int valid = S - 8 * tg;
-#pragma unroll
-        for (int m = 0; m < PB; ++m) {
-            const int e = tid + 256 * m;
-            if (e < NBP)
-                load_rows8(Bg + (r0 + 8 * tg) * a.ld_B + grp * N + (e / 16) * CPL, a.ld_B, valid, br[m]);
-        }
-        if (tid < NXP)
-            load_rows8(Xg + (r0 + 8 * tg) * a.ld_x + (int64_t)head * P + (tid / 16) * CPL, a.ld_x, valid, xr);
-        dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
-        dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
+        d0 = a.dt[(r0 + (2 * lane < S ? 2 * lane : S - 1)) * a.ld_dt + head];
+        d1 = a.dt[(r0 + (2 * lane + 1 < S ? 2 * lane + 1 : S - 1)) * a.ld_dt + head];
     };
-    prefetch(0);
 
-    for (int c = 0; c < nch; ++c) {
-        const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
-
-        // gamma over the chunk (every wave), weights w_i = dt_i e(gamma_S - gamma_i)
-        double g0, g1;
-        gamma_scan(dr0, dr1, Ah, lane, g0, g1);
-        const double gS = __shfl(((S - 1) & 1) ? g1 : g0, (S - 1) >> 1, 64);
-        const float w0 = dr0 * expc(gS - g0);
-        const float w1 = dr1 * expc(gS - g1);
-        const float decay = expc(gS);
-        // weights of this thread's staging rows 8 tg + k (held by lane 4 tg + k / 2)
-        float wx[8];
+    // Stage half h of chunk c from b (rows >= Sh zeroed) with weights w0/w1 (rows 2 lane, 2 lane + 1).
+    auto stage = [&](HalfBuf<Tin, TB, TX>& b, int Sh, int h, float w0, float w1) __attribute__((always_inline)) {
+        // B^T: channel CPL b_cg + j, tokens TB b_tg ..
 #pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-            wx[k] = __shfl(w0, 4 * tg + k / 2, 64);
-            wx[k + 1] = __shfl(w1, 4 * tg + k / 2, 64);
-        }
-
-        __syncthreads();  // the previous chunk's products are done with the LDS tiles
-
+        for (int j = 0; j < CPL; ++j) {
+            uint32_t hb[TB], lb[TB];
 #pragma unroll
-        for (int m = 0; m < PB; ++m) {
-            const int e = tid + 256 * m;
-            if (e < NBP) {
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    const int off = ((e / 16) * CPL + j) * RS + 8 * tg;
-                    if constexpr (SP) {
-                        float v[8];
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) v[k] = In<Tin>::val(br[m][k], j);
-                        uint4 hi, lo;
-                        split8(v, hi, lo);
-                        *reinterpret_cast<uint4*>(BTh + off) = hi;
-                        *reinterpret_cast<uint4*>(BTl + off) = lo;
-                    } else {
-                        uint32_t hb[8];
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) hb[k] = half_of(word_of(br[m][k], j >> 1), j & 1);
-                        *reinterpret_cast<uint4*>(BTh + off) =
-                            uint4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-                    }
+            for (int k = 0; k < TB; ++k) {
+                const bool ok = TB * b_tg + k < Sh;
+                if constexpr (SP) {
+                    split_bits(ok ? In<Tin>::val(b.br[k], j) : 0.f, hb[k], lb[k]);
+                } else {
+                    hb[k] = ok ? half_of(word_of(b.br[k], j >> 1), j & 1) : 0u;
                 }
             }
-        }
-        if (tid < NXP) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                float v[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = In<Tin>::val(xr[k], j) * wx[k];
-                uint4 hi, lo;
-                split8(v, hi, lo);
-                const int off = ((tid / 16) * CPL + j) * RS + 8 * tg;
-                *reinterpret_cast<uint4*>(XH + off) = hi;
-                *reinterpret_cast<uint4*>(XL + off) = lo;
+            uint32_t wh[(TB + 1) / 2];
+            pack_tokens<TB>(hb, wh);
+            store_tokens<TB>(BTh + (b_cg * CPL + j) * RH + TB * b_tg, wh);
+            if constexpr (SP) {
+                uint32_t wl[(TB + 1) / 2];
+                pack_tokens<TB>(lb, wl);
+                store_tokens<TB>(BTl + (b_cg * CPL + j) * RH + TB * b_tg, wl);
             }
         }
-        if (c + 1 < nch) prefetch(c + 1);
-
-        // entry state of this chunk, then h <- e(gamma_S) h
-        float* he = a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N);
+        // (w x)^T: weights of rows 64 h + TX x_tg + k, held by lane (64 h + TX x_tg + k) / 2
+        float wx[TX];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
+        for (int k = 0; k < TX; ++k) {
+            const int row = QH * h + TX * x_tg + k;
+            const float wa = __shfl(w0, row >> 1, 64), wb = __shfl(w1, row >> 1, 64);
+            wx[k] = (row & 1) ? wb : wa;
+        }
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int off = (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q;
-                *reinterpret_cast<float4*>(he + off) =
-                    float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
-                acc[i][pt] *= decay;
+        for (int j = 0; j < CPL; ++j) {
+            uint32_t hb[TX], lb[TX];
+#pragma unroll
+            for (int k = 0; k < TX; ++k) {
+                const bool ok = TX * x_tg + k < Sh;
+                split_bits(ok ? In<Tin>::val(b.xr[k], j) * wx[k] : 0.f, hb[k], lb[k]);
             }
-        __syncthreads();
+            uint32_t wh[(TX + 1) / 2], wl[(TX + 1) / 2];
+            pack_tokens<TX>(hb, wh);
+            pack_tokens<TX>(lb, wl);
+            store_tokens<TX>(XH + (x_cg * CPL + j) * RH + TX * x_tg, wh);
+            store_tokens<TX>(XL + (x_cg * CPL + j) * RH + TX * x_tg, wl);
+        }
+    };
 
-        // h^T += B^T (w x): A = B^T rows n, B = (w x) columns p, K = tokens
-        const int nkb = (S + 31) >> 5;
+    // h^T += B^T (w x) over the two 32-row K blocks of a staged half
+    auto multiply = [&](int nkb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < Q / 32; ++k) {
+        for (int k = 0; k < QH / 32; ++k) {
             if (k < nkb) {
                 bf16x8_t xh[4], xl[4];
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    xh[pt] = as_bf16x8(lds128(XH + (16 * pt + l16) * RS + 32 * k + 8 * q));
-                    xl[pt] = as_bf16x8(lds128(XL + (16 * pt + l16) * RS + 32 * k + 8 * q));
+                    xh[pt] = as_bf16x8(lds128(XH + (16 * pt + l16) * RH + 32 * k + 8 * q));
+                    xl[pt] = as_bf16x8(lds128(XL + (16 * pt + l16) * RH + 32 * k + 8 * q));
                 }
 #pragma unroll
                 for (int i = 0; i < NTW; ++i) {
-                    const int row = (16 * (NTW * wave + i) + l16) * RS + 32 * k + 8 * q;
+                    const int row = (16 * (NTW * wave + i) + l16) * RH + 32 * k + 8 * q;
                     const bf16x8_t bh = as_bf16x8(lds128(BTh + row));
                     const bf16x8_t bl = SP ? as_bf16x8(lds128(BTl + (SP ? row : 0))) : bh;
 #pragma unroll
@@ -310,14 +326,56 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(ScanArgs a) {
                 }
             }
         }
+    };
+
+    HalfBuf<Tin, TB, TX> buf;
+    float d0, d1;
+    load_half(buf, 0, 0);
+    load_dt(0, d0, d1);
+    for (int c = 0; c < nch; ++c) {
+        const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
+        if (2 * lane >= S) d0 = 0.f;
+        if (2 * lane + 1 >= S) d1 = 0.f;
+        // gamma over the chunk (every wave), weights w_i = dt_i e(gamma_S - gamma_i)
+        double g0, g1;
+        gamma_scan(d0, d1, Ah, lane, g0, g1);
+        const double gS = __shfl(((S - 1) & 1) ? g1 : g0, (S - 1) >> 1, 64);
+        const float w0 = d0 * expc(gS - g0);
+        const float w1 = d1 * expc(gS - g1);
+        const float decay = expc(gS);
+
+        // first half
+        const int S0 = S < QH ? S : QH;
+        __syncthreads();  // the previous half's products are done with the LDS tiles
+        stage(buf, S0, 0, w0, w1);
+        load_half(buf, c, 1);
+        float* he = a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                *reinterpret_cast<float4*>(he + soff(i, pt)) =
+                    float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
+                acc[i][pt] *= decay;
+            }
+        __syncthreads();
+        multiply((S0 + 31) >> 5);
+
+        // second half
+        const int S1 = S - QH;
+        __syncthreads();
+        stage(buf, S1, 1, w0, w1);
+        load_half(buf, c + 1, 0);
+        load_dt(c + 1, d0, d1);
+        __syncthreads();
+        multiply(S1 > 0 ? (S1 + 31) >> 5 : 0);
     }
 
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
-            *reinterpret_cast<float4*>(st + (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q) =
-                float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
+            *reinterpret_cast<float4*>(st + soff(i, pt)) = float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
 }
 
 // ------------------------------------------------------------------ chunk out
