@@ -397,24 +397,23 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     constexpr int HR = 64 + 8;         // LDS row stride of a staged 64-n slice
     constexpr int NRS = N + 8;         // LDS row stride of the h_in planes
     constexpr int STAGE = (SP ? 4 : 2) * Q * HR;
-    constexpr int HEAD = (SP ? 2 : 1) * P * RS + 2 * P * NRS;
-    constexpr int SMEM = STAGE > HEAD ? STAGE : HEAD;
+    constexpr int HX = (SP ? 2 : 1) * P * RS;   // x^T planes of one head
+    constexpr int HBUF = HX + 2 * P * NRS;      // + h_in planes: one head buffer
+    constexpr int SMEM = STAGE > 2 * HBUF ? STAGE : 2 * HBUF;
     constexpr int NXP = 16 * P / CPL;  // x pieces: 8 tokens x CPL columns
     constexpr int NHV = (P * N / 4) / NT;   // float4 of h_in per thread
+    // Two head buffers: head j + 1 is staged into one while head j is multiplied
+    // out of the other.  The B / C slices of the G phase use the same memory.
     __shared__ __align__(16) u16 smem[SMEM];
-    __shared__ __align__(16) float rowf[Q];      // dt_i e(gamma_r(i) - gamma_i)
-    __shared__ __align__(16) float colf[Q * 8];  // [t][it]: e(gamma_t - gamma_r(it)), it below t's tile
-    __shared__ __align__(16) double gam[Q];
-    __shared__ __align__(16) float dts[Q];
-    __shared__ __align__(16) float din[Q];       // e(gamma_t)
+    __shared__ __align__(16) float rowf[2][Q];      // dt_i e(gamma_r(i) - gamma_i)
+    __shared__ __align__(16) float colf[2][Q * 8];  // [t][it]: e(gamma_t - gamma_r(it)), it below t's tile
+    __shared__ __align__(16) double gam[2][Q];
+    __shared__ __align__(16) float dts[2][Q];
+    __shared__ __align__(16) float din[2][Q];       // e(gamma_t)
     u16* Bh = smem;
     u16* Ch = smem + Q * HR;
     u16* Bl = smem + 2 * Q * HR;
     u16* Cl = smem + 3 * Q * HR;
-    u16* Xh = smem;
-    u16* Xl = smem + P * RS;
-    u16* HH = smem + (SP ? 2 : 1) * P * RS;
-    u16* HL = HH + P * NRS;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
@@ -517,9 +516,13 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         }
     }
 
-    for (int j = 0; j < hpg; ++j) {
+    // Stage head j (whose loads are in xr / hr / dr) into head buffer bf.
+    auto stage_head = [&](int bf, int j) __attribute__((always_inline)) {
         const int head = grp * hpg + j;
-        const float Dh = a.D ? a.D[head] : 0.f;
+        u16* Xh = smem + bf * HBUF;
+        u16* Xl = Xh + P * RS;
+        u16* HH = Xh + HX;
+        u16* HL = HH + P * NRS;
         // wave 0: gamma and the decay factors of this head, from the prefetched dt
         double ga0 = 0.0, ga1 = 0.0;
         float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
@@ -537,8 +540,6 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                 cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri) : 0.f;
             }
         }
-
-        __syncthreads();  // B / C slices (first head) or the previous head's tiles are no longer read
 
         // x^T planes: column (tid / 16) * CPL + jj, tokens 8 tg .. +7
         if (tid < NXP) {
@@ -576,22 +577,31 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
         }
         if (wave == 0) {
-            gam[2 * lane] = ga0;
-            gam[2 * lane + 1] = ga1;
-            dts[2 * lane] = dr0;
-            dts[2 * lane + 1] = dr1;
-            din[2 * lane] = expc(ga0);
-            din[2 * lane + 1] = expc(ga1);
-            rowf[2 * lane] = rf0;
-            rowf[2 * lane + 1] = rf1;
-            *reinterpret_cast<float4*>(colf + 16 * lane) = float4{cf0[0], cf0[1], cf0[2], cf0[3]};
-            *reinterpret_cast<float4*>(colf + 16 * lane + 4) = float4{cf0[4], cf0[5], cf0[6], cf0[7]};
-            *reinterpret_cast<float4*>(colf + 16 * lane + 8) = float4{cf1[0], cf1[1], cf1[2], cf1[3]};
-            *reinterpret_cast<float4*>(colf + 16 * lane + 12) = float4{cf1[4], cf1[5], cf1[6], cf1[7]};
+            gam[bf][2 * lane] = ga0;
+            gam[bf][2 * lane + 1] = ga1;
+            dts[bf][2 * lane] = dr0;
+            dts[bf][2 * lane + 1] = dr1;
+            din[bf][2 * lane] = expc(ga0);
+            din[bf][2 * lane + 1] = expc(ga1);
+            rowf[bf][2 * lane] = rf0;
+            rowf[bf][2 * lane + 1] = rf1;
+            *reinterpret_cast<float4*>(colf[bf] + 16 * lane) = float4{cf0[0], cf0[1], cf0[2], cf0[3]};
+            *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 4) = float4{cf0[4], cf0[5], cf0[6], cf0[7]};
+            *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 8) = float4{cf1[0], cf1[1], cf1[2], cf1[3]};
+            *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 12) = float4{cf1[4], cf1[5], cf1[6], cf1[7]};
         }
-        if (j + 1 < hpg) prefetch(head + 1);
-        __syncthreads();
-
+    };
+    // Multiply head j out of head buffer bf and store its y rows.
+    auto compute_head = [&](int bf, int j) __attribute__((always_inline)) {
+        const int head = grp * hpg + j;
+        const float Dh = a.D ? a.D[head] : 0.f;
+        const u16* Xh = smem + bf * HBUF;
+        const u16* Xl = Xh + P * RS;
+        const u16* HH = Xh + HX;
+        const u16* HL = HH + P * NRS;
+        const float* rowfb = rowf[bf];
+        const float* dtsb = dts[bf];
+        const double* gamb = gam[bf];
         if (act) {
             // y^T[p, t] tiles: yacc[pt], lane has t, p = 16 pt + 4q + r
             f32x4_t yacc[4];
@@ -608,7 +618,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                     mma2<true, SP>(yacc[pt], ah, al, ch[k], cl[k]);
                 }
             }
-            const float sc = din[t];
+            const float sc = din[bf][t];
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) yacc[pt] *= sc;
 
@@ -616,7 +626,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             // operand slot j < 4 is row 4q + j of tile 2kb, j >= 4 row 4q + j - 4
             // of tile 2kb + 1 (the rows this lane's accumulators hold), so x is
             // read in that row order.
-            const float4* cft = reinterpret_cast<const float4*>(colf + 8 * t);
+            const float4* cft = reinterpret_cast<const float4*>(colf[bf] + 8 * t);
             const float4 cfa = cft[0], cfb = cft[1];
             const float cfv[8] = {cfa.x, cfa.y, cfa.z, cfa.w, cfb.x, cfb.y, cfb.z, cfb.w};
             // the tile index is a compile-time constant inside (one instance per tile)
@@ -630,20 +640,20 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                         const int it = 2 * kb + h2;
                         const int i0 = 16 * it + 4 * q;
                         if (it < TT) {
-                            const float4 rf = *reinterpret_cast<const float4*>(rowf + i0);
+                            const float4 rf = *reinterpret_cast<const float4*>(rowfb + i0);
                             const float cv = cfv[it];
                             m[4 * h2 + 0] = g[it][0] * rf.x * cv;
                             m[4 * h2 + 1] = g[it][1] * rf.y * cv;
                             m[4 * h2 + 2] = g[it][2] * rf.z * cv;
                             m[4 * h2 + 3] = g[it][3] * rf.w * cv;
                         } else if (it == TT) {
-                            const double gt = gam[t];
+                            const double gt = gamb[t];
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const int i = i0 + r;
                                 float v = 0.f;
                                 if (i <= t) {
-                                    v = g[it][r] * dts[i] * expc(gt - gam[i]);
+                                    v = g[it][r] * dtsb[i] * expc(gt - gamb[i]);
                                     if (i == t) v += Dh;
                                 }
                                 m[4 * h2 + r] = v;
@@ -694,6 +704,19 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                         float4{yacc[pt][0], yacc[pt][1], yacc[pt][2], yacc[pt][3]};
             }
         }
+    };
+
+    __syncthreads();   // the G phase is done with the B / C slices
+    stage_head(0, 0);
+    prefetch(hpg > 1 ? grp * hpg + 1 : grp * hpg);
+    __syncthreads();
+    for (int j = 0; j < hpg; ++j) {
+        if (j + 1 < hpg) {
+            stage_head((j + 1) & 1, j + 1);
+            if (j + 2 < hpg) prefetch(grp * hpg + j + 2);
+        }
+        compute_head(j & 1, j);
+        __syncthreads();
     }
 }
 
