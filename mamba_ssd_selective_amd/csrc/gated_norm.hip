@@ -51,7 +51,7 @@ __global__ __launch_bounds__(BLOCK) void gated_norm_kernel(NormArgs a) {
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    const float rstd = 1.0f / sqrtf(ss / (float)gs + a.eps);
+    const float rstd = __builtin_amdgcn_rsqf(ss / (float)gs + a.eps);
 
     Tout* orow = static_cast<Tout*>(a.out) + t * a.ld_out + cbase;
 #pragma unroll
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(BLOCK) void gated_norm_vec_kernel(NormArgs a) {
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    const float rstd = 1.0f / sqrtf(ss / (float)gs + a.eps);
+    const float rstd = __builtin_amdgcn_rsqf(ss / (float)gs + a.eps);
 
     Tout* orow = static_cast<Tout*>(a.out) + t * a.ld_out + cbase;
 #pragma unroll

@@ -77,11 +77,11 @@ hipError_t launch_gated_norm(const NormArgs& a, hipStream_t stream);
 bool scan_supported(int headdim, int dstate);
 
 // Chunk-parallel scan (ssd_chunked.hip) for PolicyBf16x3 (x/B/C stored as bf16
-// or fp32), headdim 64, dstate 64 or 128, chunk 128.  The state pass writes the entry state of every chunk to
+// or fp32), headdim 64, dstate 64 or 128, chunk 128, at most 256 heads per group.  The state pass writes the entry state of every chunk to
 // `states` ([total_tokens/128 + batch chunk slots, H, P, N] fp32; sequence b's
 // chunk c is slot cu_seqlens[b]/128 + b + c) and the final states; the chunk
 // pass reads them and writes y.
-bool chunked_scan_supported(int policy, int headdim, int dstate, int chunk);
+bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, int dstate, int chunk);
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate);
 hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream);

@@ -207,9 +207,9 @@ int launch_scan(m2::ScanArgs& a, int64_t total_tokens, hipStream_t s, hipEvent_t
 }
 
 size_t scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate,
-                         int chunk_size, int act_dtype) {
+                         int ngroups, int chunk_size, int act_dtype) {
     const int policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
-    if (!m2::chunked_scan_supported(policy, headdim, dstate, chunk_size)) return 0;
+    if (!m2::chunked_scan_supported(policy, nheads, ngroups, headdim, dstate, chunk_size)) return 0;
     return m2::chunked_scan_states_bytes(total_tokens, batch, nheads, headdim, dstate);
 }
 
@@ -280,7 +280,7 @@ size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads
     if (total_tokens < 0 || batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
         ngroups <= 0 || !valid_dtype(act_dtype))
         return 0;
-    return scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype);
+    return scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -294,7 +294,7 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
                            n_slots, cu_seqlens, batch, total_tokens, max_seqlen, state_idx, nheads,
                            headdim, dstate, ngroups, chunk_size, y, ld_y);
     if (st) return st;
-    const size_t need = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype);
+    const size_t need = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(M2_ERR_WORKSPACE, "scan: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (need > 0 && !aligned16(workspace)) return fail(M2_ERR_ALIGN, "scan: workspace must be 16-byte aligned");
@@ -341,7 +341,7 @@ size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_se
     // pre-norm output (fp32; used when y is not fp32) and the scan's entry states
     const int64_t ues = act_dtype == M2_BF16 ? 4 : 8;
     return (size_t)(round256(total_tokens * conv_dim * ues) + round256(total_tokens * di * 4)) +
-           scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype);
+           scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
 int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -376,7 +376,7 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     char* wsb = static_cast<char*>(workspace);
     void* u = wsb;
     float* ypre_ws = wsb ? reinterpret_cast<float*>(wsb + u_bytes) : nullptr;
-    const bool chunked = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, chunk_size, act_dtype) > 0;
+    const bool chunked = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype) > 0;
     float* states_ws = (wsb && chunked) ? reinterpret_cast<float*>(wsb + u_bytes + ypre_bytes) : nullptr;
     if ((st = validate_conv(x, ld_x, B, ld_B, C, ld_C, d_x, d_b, act_dtype, conv_w, conv_b, 4,
                             conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,

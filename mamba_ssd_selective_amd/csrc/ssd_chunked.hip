@@ -43,6 +43,7 @@ namespace {
 
 constexpr int Q = 128;     // chunk rows
 constexpr int P = 64;      // headdim
+constexpr int MAXHPG = 256;  // heads per group the chunk-parallel path takes
 constexpr int RS = Q + 8;  // LDS row stride (bf16 elements) of token-indexed rows: 272 bytes
 
 typedef uint16_t u16;
@@ -410,6 +411,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     __shared__ __align__(16) double gam[2][Q];
     __shared__ __align__(16) float dts[2][Q];
     __shared__ __align__(16) float din[2][Q];       // e(gamma_t)
+    __shared__ float sA[MAXHPG], sD[MAXHPG];        // A and D of the group's heads
     u16* Bh = smem;
     u16* Ch = smem + Q * HR;
     u16* Bl = smem + 2 * Q * HR;
@@ -457,6 +459,12 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         }
     };
     prefetch(grp * hpg);
+    // A and D of the group's heads, read once (a per-head load issued after the
+    // next head's prefetch would make the compiler wait for that prefetch too)
+    for (int e = tid; e < hpg; e += NT) {
+        sA[e] = a.A[grp * hpg + e];
+        sD[e] = a.D ? a.D[grp * hpg + e] : 0.f;
+    }
 
     const int T = wave < 4 ? wave : 11 - wave;
     const bool act = 16 * T < S;
@@ -518,7 +526,6 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
 
     // Stage head j (whose loads are in xr / hr / dr) into head buffer bf.
     auto stage_head = [&](int bf, int j) __attribute__((always_inline)) {
-        const int head = grp * hpg + j;
         u16* Xh = smem + bf * HBUF;
         u16* Xl = Xh + P * RS;
         u16* HH = Xh + HX;
@@ -527,7 +534,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         double ga0 = 0.0, ga1 = 0.0;
         float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
         if (wave == 0) {
-            gamma_scan(dr0, dr1, a.A[head], lane, ga0, ga1);
+            gamma_scan(dr0, dr1, sA[j], lane, ga0, ga1);
             // rows 2 lane, 2 lane + 1 lie in tile lane / 8, whose last row 16 (lane / 8) + 15
             // is held (as ga1) by lane 8 (lane / 8) + 7
             const double gr = __shfl(ga1, 8 * (lane >> 3) + 7, 64);
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     // Multiply head j out of head buffer bf and store its y rows.
     auto compute_head = [&](int bf, int j) __attribute__((always_inline)) {
         const int head = grp * hpg + j;
-        const float Dh = a.D ? a.D[head] : 0.f;
+        const float Dh = sD[j];
         const u16* Xh = smem + bf * HBUF;
         const u16* Xl = Xh + P * RS;
         const u16* HH = Xh + HX;
@@ -735,8 +742,9 @@ hipError_t launch_out(const ScanArgs& a, int64_t total_tokens, hipStream_t strea
 
 }  // namespace
 
-bool chunked_scan_supported(int policy, int headdim, int dstate, int chunk) {
-    return policy == kPolicyBf16x3 && headdim == P && (dstate == 64 || dstate == 128) && chunk == Q;
+bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, int dstate, int chunk) {
+    return policy == kPolicyBf16x3 && headdim == P && (dstate == 64 || dstate == 128) && chunk == Q &&
+           ngroups > 0 && nheads % ngroups == 0 && nheads / ngroups <= MAXHPG;
 }
 
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate) {
