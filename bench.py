@@ -105,6 +105,36 @@ def kernel_bytes(w, T, nseq):
     }
 
 
+def kernel_sources_sha1():
+    """sha1 over the kernel sources (name + bytes, sorted): ties a traffic record to a build."""
+    import glob
+    import hashlib
+    h = hashlib.sha1()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mamba_ssd_selective_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE / WRITE_SIZE record in
+    profiles/, scaled by the copy calibration stored with it; None when no record matches
+    the workload and the current kernel sources."""
+    import glob
+    for f in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md")):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("traffic-record:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1])
+                k = rec["kernels"].get(kernel)
+                if rec["workload"] == workload and k and rec["sources_sha1"] == kernel_sources_sha1():
+                    return int((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024)
+    return None
+
+
 def fused_bytes(w, T, nseq):
     """Algorithmic bytes of the whole step: read x|B|C, z, dt, states; write y (fp32), states."""
     s = w.shape
@@ -219,7 +249,8 @@ def main():
     dom = max(kms, key=kms.get)
     achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, dom),
+            "kernel": dom,
             "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
             "step_bytes": fused_bytes(w, T, nseq),
             "step_frac": round(fused_bytes(w, T, nseq) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
