@@ -329,9 +329,14 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         }
     };
 
-    HalfBuf<Tin, TB, TX> buf;
+    // One register buffer per half, each refilled a whole chunk ahead; dt of the
+    // next chunk is requested right after the gamma scan consumed the current one.
+    // Every wait therefore covers loads issued about a chunk earlier, while the
+    // newer ones stay in flight.
+    HalfBuf<Tin, TB, TX> buf0, buf1;
     float d0, d1;
-    load_half(buf, 0, 0);
+    load_half(buf0, 0, 0);
+    load_half(buf1, 0, 1);
     load_dt(0, d0, d1);
     for (int c = 0; c < nch; ++c) {
         const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
@@ -344,12 +349,13 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         const float w0 = d0 * expc(gS - g0);
         const float w1 = d1 * expc(gS - g1);
         const float decay = expc(gS);
+        load_dt(c + 1, d0, d1);
 
         // first half
         const int S0 = S < QH ? S : QH;
         __syncthreads();  // the previous half's products are done with the LDS tiles
-        stage(buf, S0, 0, w0, w1);
-        load_half(buf, c, 1);
+        stage(buf0, S0, 0, w0, w1);
+        load_half(buf0, c + 1, 0);
         float* he = a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
@@ -365,9 +371,8 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         // second half
         const int S1 = S - QH;
         __syncthreads();
-        stage(buf, S1, 1, w0, w1);
-        load_half(buf, c + 1, 0);
-        load_dt(c + 1, d0, d1);
+        stage(buf1, S1, 1, w0, w1);
+        load_half(buf1, c + 1, 1);
         __syncthreads();
         multiply(S1 > 0 ? (S1 + 31) >> 5 : 0);
     }
