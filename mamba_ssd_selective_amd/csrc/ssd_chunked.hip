@@ -118,6 +118,16 @@ __device__ __forceinline__ void mma2(f32x4_t& acc, bf16x8_t ah, bf16x8_t al, bf1
     acc = mfma(ah, bh, acc);
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 32x32x16 counterpart of mma2.
+template <bool SA, bool SB>
+__device__ __forceinline__ void mma32(f32x16_t& acc, bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl) {
+    if constexpr (SA) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+    if constexpr (SB) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+}
+
 // 8 values -> packed bf16 high parts and low parts.
 __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo) {
     uint32_t h[8], l[8];
@@ -137,8 +147,8 @@ __device__ __forceinline__ void load_rows8(const Tin* base, int64_t ld, int vali
 
 // ------------------------------------------------------------------ state pass
 //
-// 4 waves.  h^T [N x P] lives in matrix-core accumulators: wave w owns n tiles
-// w * NTW .. w * NTW + NTW - 1 and all 4 p tiles.  Each chunk is staged and
+// 4 waves.  h^T [N x P] lives in matrix-core accumulators (32x32 tiles spread
+// over the waves).  Each chunk is staged and
 // multiplied in two halves of 64 rows, so the LDS tiles are small enough for
 // two workgroups per CU (one stages while the other multiplies).  The loads of
 // the next half are in flight while the current half is multiplied; they are
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     constexpr bool SP = In<Tin>::kSplit;
     constexpr int CPL = In<Tin>::CPL;
     constexpr int NT = 256;
-    constexpr int NTW = N / 64;                        // n tiles per wave
+    constexpr int TPW = N / 64;                        // 32x32 state tiles per wave
     constexpr int TB = QH * N / (CPL * NT);            // tokens per B piece (one piece per thread)
     constexpr int TX = QH * P / (CPL * NT);            // tokens per x piece
     constexpr int BG = QH / TB, XG = QH / TX;          // token groups (fastest across lanes)
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     __shared__ __align__(16) u16 XL[P * RH];            // low parts
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
+    const int wave = tid >> 6, lane = tid & 63;
     const int item = item_of(blockIdx.x, a.nheads * a.batch);
     const int seq = item / a.nheads, head = item % a.nheads;
     const int grp = head / (a.nheads / a.ngroups);
@@ -203,28 +213,31 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     const float Ah = a.A[head];
     float* st = a.ssm_state + ((int64_t)slot * a.nheads + head) * (int64_t)(P * N);
 
-    // acc[i][pt]: h^T tile (n tile NTW wave + i, p tile pt); lane has p = 16 pt + l16
-    // and n = 16 (NTW wave + i) + 4q + r, i.e. 4 consecutive n.
-    auto soff = [&](int i, int pt) { return (16 * pt + l16) * N + 16 * (NTW * wave + i) + 4 * q; };
-    f32x4_t acc[NTW][4];
+    // h^T [N x P] in 32x32 tiles (the 32x32x16 instruction does twice the work of
+    // the 16x16x32 one in about the same time): N/32 n tiles x 2 p tiles over the
+    // 4 waves, TPW tiles each.  acc[i] is tile wave * TPW + i = (n tile mt, p tile
+    // pt); lane l has p = 32 pt + l % 32 and, in registers 4m .. 4m + 3, the four
+    // consecutive n = 32 mt + 8m + 4 (l / 32) + 0..3.
+    const int l32 = lane & 31, g32 = lane >> 5;
+    auto tile_mt = [&](int i) { return (wave * TPW + i) >> 1; };
+    auto tile_pt = [&](int i) { return (wave * TPW + i) & 1; };
+    auto soff = [&](int i, int m) { return (32 * tile_pt(i) + l32) * N + 32 * tile_mt(i) + 8 * m + 4 * g32; };
+    f32x16_t acc[TPW];
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
+    for (int i = 0; i < TPW; ++i)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            if (init && L > 0) {
-                const float4 v = *reinterpret_cast<const float4*>(st + soff(i, pt));
-                acc[i][pt] = f32x4_t{v.x, v.y, v.z, v.w};
-            } else {
-                acc[i][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
+        for (int m = 0; m < 4; ++m) {
+            float4 v = float4{0.f, 0.f, 0.f, 0.f};
+            if (init && L > 0) v = *reinterpret_cast<const float4*>(st + soff(i, m));
+            acc[i][4 * m + 0] = v.x; acc[i][4 * m + 1] = v.y; acc[i][4 * m + 2] = v.z; acc[i][4 * m + 3] = v.w;
         }
     if (L <= 0) {
         // Empty sequence: a fresh slot is still reset, a carried one is untouched.
         if (!init) {
 #pragma unroll
-            for (int i = 0; i < NTW; ++i)
+            for (int i = 0; i < TPW; ++i)
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) *reinterpret_cast<float4*>(st + soff(i, pt)) = float4{0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < 4; ++m) *reinterpret_cast<float4*>(st + soff(i, m)) = float4{0.f, 0.f, 0.f, 0.f};
         }
         return;
     }
@@ -306,24 +319,21 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         }
     };
 
-    // h^T += B^T (w x) over the two 32-row K blocks of a staged half
+    // h^T += B^T (w x) over the 16-row K blocks of a staged half (32x32x16: an
+    // operand lane supplies row (or column) l % 32 and K slots 8 (l / 32) .. + 7)
     auto multiply = [&](int nkb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < QH / 32; ++k) {
+        for (int k = 0; k < QH / 16; ++k) {
             if (k < nkb) {
-                bf16x8_t xh[4], xl[4];
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    xh[pt] = as_bf16x8(lds128(XH + (16 * pt + l16) * RH + 32 * k + 8 * q));
-                    xl[pt] = as_bf16x8(lds128(XL + (16 * pt + l16) * RH + 32 * k + 8 * q));
-                }
-#pragma unroll
-                for (int i = 0; i < NTW; ++i) {
-                    const int row = (16 * (NTW * wave + i) + l16) * RH + 32 * k + 8 * q;
-                    const bf16x8_t bh = as_bf16x8(lds128(BTh + row));
-                    const bf16x8_t bl = SP ? as_bf16x8(lds128(BTl + (SP ? row : 0))) : bh;
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) mma2<SP, true>(acc[i][pt], bh, bl, xh[pt], xl[pt]);
+                for (int i = 0; i < TPW; ++i) {
+                    const int xo = (32 * tile_pt(i) + l32) * RH + 16 * k + 8 * g32;
+                    const int bo = (32 * tile_mt(i) + l32) * RH + 16 * k + 8 * g32;
+                    const bf16x8_t xh = as_bf16x8(lds128(XH + xo));
+                    const bf16x8_t xl = as_bf16x8(lds128(XL + xo));
+                    const bf16x8_t bh = as_bf16x8(lds128(BTh + bo));
+                    const bf16x8_t bl = SP ? as_bf16x8(lds128(BTl + (SP ? bo : 0))) : bh;
+                    mma32<SP, true>(acc[i], bh, bl, xh, xl);
                 }
             }
         }
@@ -349,39 +359,48 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         const float w0 = d0 * expc(gS - g0);
         const float w1 = d1 * expc(gS - g1);
         const float decay = expc(gS);
-        load_dt(c + 1, d0, d1);
-
-        // first half
-        const int S0 = S < QH ? S : QH;
-        __syncthreads();  // the previous half's products are done with the LDS tiles
-        stage(buf0, S0, 0, w0, w1);
-        load_half(buf0, c + 1, 0);
+        // entry state of this chunk, then h <- e(gamma_S) h (the stores go out first,
+        // so they are the oldest memory operations whenever a later load is awaited)
         float* he = a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
+        for (int i = 0; i < TPW; ++i) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                *reinterpret_cast<float4*>(he + soff(i, pt)) =
-                    float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
-                acc[i][pt] *= decay;
-            }
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<float4*>(he + soff(i, m)) =
+                    float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+            acc[i] *= decay;
+        }
+        load_dt(c + 1, d0, d1);
+
+        // first half.  The scheduling barriers keep each half's staging arithmetic
+        // in its phase: hoisted above the barriers it would make the compiler wait
+        // for that half's loads early and undo the prefetch distance.
+        const int S0 = S < QH ? S : QH;
+        __syncthreads();  // the previous half's products are done with the LDS tiles
+        __builtin_amdgcn_sched_barrier(0);
+        stage(buf0, S0, 0, w0, w1);
+        load_half(buf0, c + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        multiply((S0 + 31) >> 5);
+        multiply((S0 + 15) >> 4);
 
         // second half
         const int S1 = S - QH;
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
         stage(buf1, S1, 1, w0, w1);
         load_half(buf1, c + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        multiply(S1 > 0 ? (S1 + 31) >> 5 : 0);
+        multiply(S1 > 0 ? (S1 + 15) >> 4 : 0);
     }
 
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
+    for (int i = 0; i < TPW; ++i)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-            *reinterpret_cast<float4*>(st + soff(i, pt)) = float4{acc[i][pt][0], acc[i][pt][1], acc[i][pt][2], acc[i][pt][3]};
+        for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<float4*>(st + soff(i, m)) =
+                float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
 }
 
 // ------------------------------------------------------------------ chunk out
