@@ -8,11 +8,12 @@
 // SiLU; section 10: the conv state keeps (width - 1) rows per channel.
 //
 // The conv is HBM-bound (4 multiply-adds per element read), so the kernel is a
-// streaming pass: a thread owns 8 adjacent channels (one 16-byte bf16 load, two
-// for fp32) and a run of TOK consecutive packed rows, keeps the last three raw
-// rows of its channels in registers as a sliding window, and refills the window
-// from the slot's conv state (or zeros) whenever its run enters a new sequence.
-// Weights and bias of its 8 channels stay in registers for the whole run.
+// streaming pass: a thread owns CPT = 8 adjacent channels (one 16-byte bf16
+// load, two for fp32) and a run of TOK consecutive packed rows.  It issues the
+// loads of the run's rows and 3-row halo first, then slides a window over
+// registers; a run that starts a sequence or crosses into another one goes row
+// by row instead, refilling the window from the slot's conv state (or zeros).
+// Weights and bias of its channels stay in registers for the whole run.
 
 #include <type_traits>
 
@@ -36,48 +37,145 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int64_t t) {
     return lo;
 }
 
+// Column `c` of the xBC stream as (first element of that column, row stride).
+// The column pointer is marked as global memory: global loads can be waited
+// for one at a time, generic (flat) ones only all together.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef double f64x2v_t __attribute__((ext_vector_type(2)));
 template <typename Tin>
-__device__ __forceinline__ const Tin* seg_row(const ConvArgs& a, int seg, int64_t row, int cs) {
-    return static_cast<const Tin*>(a.seg_ptr[seg]) + row * a.seg_ld[seg] + cs;
+struct SegCol {
+    gptr<Tin> col;
+    int64_t ld;
+    __device__ __forceinline__ gptr<Tin> grow(int64_t t) const { return col + t * ld; }
+    __device__ __forceinline__ const Tin* row(int64_t t) const { return (const Tin*)grow(t); }
+};
+// Per lane (channel c of the whole stream; lanes of a wave may differ).
+template <typename Tin>
+__device__ __forceinline__ SegCol<Tin> seg_col_lane(const ConvArgs& a, int c) {
+    int seg = 0;
+    while (seg + 1 < a.nseg && c >= a.seg_ch[seg]) { c -= a.seg_ch[seg]; ++seg; }
+    return SegCol<Tin>{(gptr<Tin>)a.seg_ptr[seg] + c, a.seg_ld[seg]};
 }
 
-// Stores of 8 consecutive outputs (16-byte aligned rows).
-__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
-    *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
-}
-__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
-    uint32_t w[4];
+// The conv launch gives every segment its own channel blocks of BLOCK * CPT
+// channels, so a block never straddles two segments and the segment is the
+// same for all its lanes: its table entries are then scalar loads.  (A
+// per-lane choice among the three segment pointers made the compiler copy the
+// whole argument block to scratch memory.)
+struct BlockSeg {
+    int seg;     // segment index
+    int cs0;     // first channel of the block within the segment
+    int cbase;   // first channel of the segment in the whole stream
+};
+__device__ __forceinline__ BlockSeg block_seg(const ConvArgs& a, int y, int width) {
+    BlockSeg r{0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int s = 0; s < 2; ++s) {
+        if (r.seg != s || s + 1 >= a.nseg) break;
+        const int nb = (a.seg_ch[s] + width - 1) / width;
+        if (y < nb) break;
+        y -= nb;
+        r.cbase += a.seg_ch[s];
+        r.seg = s + 1;
+    }
+    r.cs0 = y * width;
+    return r;
+}
+__host__ __device__ __forceinline__ int conv_channel_blocks(const ConvArgs& a, int width) {
+    int n = 0;
+    for (int s = 0; s < a.nseg; ++s) n += (a.seg_ch[s] + width - 1) / width;
+    return n;
+}
+
+// Global-memory vector stores of one thread's CPT outputs (CPT = 4 or 8; rows
+// are 16-byte aligned and CPT-channel groups start at a multiple of CPT).
+template <typename E, int L>
+using vec = E __attribute__((ext_vector_type(L)));
+template <typename E, int L>
+using gvec = __attribute__((address_space(1))) vec<E, L>;
+template <int N>
+__device__ __forceinline__ void store_out(float* p, const float (&v)[N]) {
+    auto* q = (gvec<float, 4>*)p;
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) q[k] = f32x4v_t{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+}
+template <int N>
+__device__ __forceinline__ void store_out(uint16_t* p, const float (&v)[N]) {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k)
         w[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
-    *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
-}
-__device__ __forceinline__ void store8(double* p, const double (&v)[8]) {
+    if constexpr (N == 4) {
+        *(gvec<uint32_t, 2>*)p = u32x2_t{w[0], w[1]};
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<double2*>(p + 2 * k) = double2{v[2 * k], v[2 * k + 1]};
+        for (int k = 0; k < N / 8; ++k) ((gvec<uint32_t, 4>*)p)[k] = u32x4_t{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_out(double* p, const double (&v)[N]) {
+    auto* q = (gvec<double, 2>*)p;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) q[k] = f64x2v_t{v[2 * k], v[2 * k + 1]};
 }
 
 // Computes in fp64 when the output is fp64 (the fp32-input prefill path), else fp32.
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     using T = typename std::conditional<std::is_same<Tout, double>::value, double, float>::type;
-    const int c0 = (blockIdx.y * BLOCK + threadIdx.x) * CPT;   // first channel of this thread
-    if (c0 >= a.conv_dim) return;
+    const BlockSeg bs = block_seg(a, blockIdx.y, BLOCK * CPT);
+    const int cs = bs.cs0 + threadIdx.x * CPT;   // first channel of this thread in its segment
+    if (cs >= a.seg_ch[bs.seg]) return;
+    const int c0 = bs.cbase + cs;                 // ... and in the whole stream
     const int64_t t0 = (int64_t)blockIdx.x * TOK;
     if (t0 >= a.total_tokens) return;
     const int64_t t1 = (t0 + TOK < a.total_tokens) ? t0 + TOK : a.total_tokens;
+    const SegCol<Tin> sc{(gptr<Tin>)a.seg_ptr[bs.seg] + cs, a.seg_ld[bs.seg]};
 
-    // segment of these channels
-    int seg = 0, cs = c0;
-    while (seg + 1 < a.nseg && cs >= a.seg_ch[seg]) { cs -= a.seg_ch[seg]; ++seg; }
+    // Rows t0-3 .. t0+TOK-1 are loaded before the sequence lookup below, so their
+    // latency overlaps its dependent reads of cu_seqlens; row indices are clamped
+    // to the stream, and runs that need other rows (a sequence starts inside the
+    // window, or the stream ends) take the row-at-a-time path further down.
+    // A row's CPT inputs are NW 32-bit words, loaded as NV vectors of VL words.
+    constexpr int NW = CPT * (int)sizeof(Tin) / 4;
+    constexpr int VL = NW < 4 ? NW : 4;
+    constexpr int NV = NW / VL;
+    uint32_t raw[TOK + 3][NW];
+    {
+        const int64_t last = a.total_tokens - 1;
+#pragma unroll
+        for (int k = 0; k < TOK + 3; ++k) {
+            int64_t r = t0 - 3 + k;
+            r = r < 0 ? 0 : r > last ? last : r;
+            const auto* src = (const gvec<uint32_t, VL>*)sc.grow(r);
+#pragma unroll
+            for (int h = 0; h < NV; ++h) {
+                const vec<uint32_t, VL> v = src[h];
+#pragma unroll
+                for (int e = 0; e < VL; ++e) raw[k][h * VL + e] = v[e];
+            }
+        }
+    }
 
     T w[CPT][4], bias[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const float4 wv = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)(c0 + c) * 4);
         w[c][0] = wv.x; w[c][1] = wv.y; w[c][2] = wv.z; w[c][3] = wv.w;
-        bias[c] = a.conv_b ? a.conv_b[c0 + c] : 0.f;
+    }
+    if (a.conv_b) {
+#pragma unroll
+        for (int k = 0; k < CPT / 4; ++k) {
+            const float4 bv = *reinterpret_cast<const float4*>(a.conv_b + c0 + 4 * k);
+            bias[4 * k] = bv.x; bias[4 * k + 1] = bv.y; bias[4 * k + 2] = bv.z; bias[4 * k + 3] = bv.w;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) bias[c] = 0.f;
     }
 
     int b = seq_of(a.cu_seqlens, a.batch, t0);
@@ -85,71 +183,64 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     int64_t s1 = a.cu_seqlens[b + 1];
     Tout* out = static_cast<Tout*>(a.out);
 
-    if (t0 - 3 >= s0 && t1 <= s1) {
-        // The run and its 3-row halo lie inside one sequence: issue every row's
-        // load up front, then slide the window over registers.
-        // raw 16-byte pieces: one per row for bf16, two for fp32
-        constexpr int PR = (int)sizeof(Tin) / 2;
-        uint4 raw[TOK + 3][PR];
-#pragma unroll
-        for (int k = 0; k < TOK + 3; ++k) {
-            const int64_t t = t0 - 3 + k;
-            if (t < t1) {
-                const uint4* src = reinterpret_cast<const uint4*>(seg_row<Tin>(a, seg, t, cs));
-#pragma unroll
-                for (int h = 0; h < PR; ++h) raw[k][h] = src[h];
-            }
-        }
+    if (t0 - 3 >= s0 && t0 + TOK <= s1) {
+        // A full run whose 3-row halo lies inside the same sequence: the rows
+        // loaded above are exactly its window; slide it over registers.
         auto val = [&](int k, int c) -> T {
             if constexpr (sizeof(Tin) == 2) {
-                const uint32_t wd = c < 2 ? raw[k][0].x : c < 4 ? raw[k][0].y : c < 6 ? raw[k][0].z : raw[k][0].w;
+                const uint32_t wd = raw[k][c >> 1];
                 return (T)__builtin_bit_cast(float, (c & 1) ? (wd & 0xffff0000u) : (wd << 16));
             } else {
-                const uint4& q4 = raw[k][c >> 2];
-                const int e = c & 3;
-                return (T)__builtin_bit_cast(float, e == 0 ? q4.x : e == 1 ? q4.y : e == 2 ? q4.z : q4.w);
+                return (T)__builtin_bit_cast(float, raw[k][c]);
             }
         };
+        Tout* dst = out + t0 * a.ld_out + c0;
 #pragma unroll
         for (int k = 0; k < TOK; ++k) {
-            const int64_t t = t0 + k;
-            if (t < t1) {
-                T o[CPT];
+            T o[CPT];
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    T acc = bias[c];
-                    acc = fma(w[c][0], val(k, c), acc);
-                    acc = fma(w[c][1], val(k + 1, c), acc);
-                    acc = fma(w[c][2], val(k + 2, c), acc);
-                    acc = fma(w[c][3], val(k + 3, c), acc);
-                    o[c] = a.apply_silu ? silu(acc) : acc;
-                }
-                store8(out + t * a.ld_out + c0, o);
+            for (int c = 0; c < CPT; ++c) {
+                T acc = bias[c];
+                acc = fma(w[c][0], val(k, c), acc);
+                acc = fma(w[c][1], val(k + 1, c), acc);
+                acc = fma(w[c][2], val(k + 2, c), acc);
+                acc = fma(w[c][3], val(k + 3, c), acc);
+                o[c] = a.apply_silu ? silu(acc) : acc;
             }
+            store_out(dst + k * a.ld_out, o);
         }
         return;
     }
 
+    // Runs at a sequence start or across a sequence boundary (a few per
+    // sequence): a row at a time with element loads.
     T win[3][CPT];   // raw rows t-3, t-2, t-1
 
-    auto fill_window = [&](int64_t t) {
+    const int32_t* const state_idx = a.state_idx;
+    const uint8_t* const has_init = a.has_init;
+    const float* const conv_state = a.conv_state;
+    const int conv_dim = a.conv_dim;
+    // (captures no reference to the kernel argument block: that would make the
+    // compiler copy it to scratch memory)
+    auto fill_window = [&win, &sc, &s0, &b, state_idx, has_init, conv_state, conv_dim, c0](int64_t t) {
         // rows t-3..t-1 of sequence b: from the stream if inside it, else from the state
-        const int slot = a.state_idx ? a.state_idx[b] : b;
-        const bool init = a.has_init ? (a.has_init[b] != 0) : true;
+        const int slot = state_idx ? state_idx[b] : b;
+        const bool init = has_init ? (has_init[b] != 0) : true;
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
             const int64_t j = (t - s0) - 3 + d;     // position of the needed row in the sequence
-            T v[CPT];
             if (j >= 0) {
-                load8(seg_row<Tin>(a, seg, s0 + j, cs), v);
+                const Tin* row = sc.row(s0 + j);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) win[d][c] = (T)Act<Tin>::load(row + c);
             } else if (init) {
-                load8(a.conv_state + ((int64_t)slot * 3 + (3 + j)) * a.conv_dim + c0, v);
+                const float* st = conv_state + ((int64_t)slot * 3 + (3 + j)) * conv_dim + c0;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) win[d][c] = (T)st[c];
             } else {
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) v[c] = 0.f;
+                for (int c = 0; c < CPT; ++c) win[d][c] = (T)0;
             }
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) win[d][c] = v[c];
         }
     };
     fill_window(t0);
@@ -161,22 +252,22 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
             s1 = a.cu_seqlens[b + 1];
             fill_window(t);
         }
-        T cur[CPT];
-        load8(seg_row<Tin>(a, seg, t, cs), cur);
+        const Tin* row = sc.row(t);
         T o[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
+            const T cur = (T)Act<Tin>::load(row + c);
             T acc = bias[c];
             acc = fma(w[c][0], win[0][c], acc);
             acc = fma(w[c][1], win[1][c], acc);
             acc = fma(w[c][2], win[2][c], acc);
-            acc = fma(w[c][3], cur[c], acc);
+            acc = fma(w[c][3], cur, acc);
             o[c] = a.apply_silu ? silu(acc) : acc;
             win[0][c] = win[1][c];
             win[1][c] = win[2][c];
-            win[2][c] = cur[c];
+            win[2][c] = cur;
         }
-        store8(out + t * a.ld_out + c0, o);
+        store_out(out + t * a.ld_out + c0, o);
     }
 }
 
@@ -187,8 +278,7 @@ __global__ __launch_bounds__(BLOCK) void conv_state_kernel(ConvArgs a) {
     const int c = blockIdx.x * BLOCK + threadIdx.x;
     const int b = blockIdx.y;
     if (c >= a.conv_dim) return;
-    int seg = 0, cs = c;
-    while (seg + 1 < a.nseg && cs >= a.seg_ch[seg]) { cs -= a.seg_ch[seg]; ++seg; }
+    const SegCol<Tin> sc = seg_col_lane<Tin>(a, c);
     const int64_t s0 = a.cu_seqlens[b];
     const int64_t L = a.cu_seqlens[b + 1] - s0;
     const int slot = a.state_idx ? a.state_idx[b] : b;
@@ -201,7 +291,7 @@ __global__ __launch_bounds__(BLOCK) void conv_state_kernel(ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int64_t k = L + j;   // index into [old(3) ; rows(L)]
-        nw[j] = (k < 3) ? old[k] : Act<Tin>::load(seg_row<Tin>(a, seg, s0 + (k - 3), cs));
+        nw[j] = (k < 3) ? old[k] : Act<Tin>::load(sc.row(s0 + (k - 3)));
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) st[(int64_t)j * a.conv_dim] = nw[j];
@@ -211,7 +301,7 @@ __global__ __launch_bounds__(BLOCK) void conv_state_kernel(ConvArgs a) {
 
 hipError_t launch_conv_rows(const ConvArgs& a, hipStream_t stream) {
     const int64_t tok_blocks = (a.total_tokens + TOK - 1) / TOK;
-    const int ch_blocks = (a.conv_dim / CPT + BLOCK - 1) / BLOCK;
+    const int ch_blocks = conv_channel_blocks(a, BLOCK * CPT);
     const dim3 grid((unsigned)tok_blocks, ch_blocks);
     if (a.act_dtype == kBF16) {
         if (a.out_dtype == kBF16)
