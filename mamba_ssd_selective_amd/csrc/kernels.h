@@ -78,8 +78,9 @@ bool scan_supported(int headdim, int dstate);
 
 // Chunk-parallel scan (ssd_chunked.hip) for PolicyBf16x3 (x/B/C stored as bf16
 // or fp32), headdim 64, dstate 64 or 128, chunk 128, at most 256 heads per group.  The state pass writes the entry state of every chunk to
-// `states` ([total_tokens/128 + batch chunk slots, H, P, N] fp32; sequence b's
-// chunk c is slot cu_seqlens[b]/128 + b + c) and the final states; the chunk
+// `states` ([total_tokens/128 + batch chunk slots, H] blocks of P x N fp32, each
+// block in the state pass's accumulator order; sequence b's chunk c is slot
+// cu_seqlens[b]/128 + b + c) and the final states; the chunk
 // pass reads them and writes y.
 bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, int dstate, int chunk);
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate);

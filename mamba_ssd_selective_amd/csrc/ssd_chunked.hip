@@ -63,13 +63,6 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
     return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
-// bf16 bits of the high and low parts of v.
-__device__ __forceinline__ void split_bits(float v, uint32_t& hi, uint32_t& lo) {
-    const __bf16 h = static_cast<__bf16>(v);
-    const __bf16 l = static_cast<__bf16>(v - static_cast<float>(h));
-    hi = __builtin_bit_cast(u16, h);
-    lo = __builtin_bit_cast(u16, l);
-}
 
 // Inclusive prefix sum of a = dt * A over the 128 rows of a chunk on one wave:
 // lane l holds rows 2l and 2l+1 (dt already 0 beyond the chunk's rows).
@@ -128,13 +121,26 @@ __device__ __forceinline__ void mma32(f32x16_t& acc, bf16x8_t ah, bf16x8_t al, b
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// High and low parts of the pair (a, b) as packed bf16 (a in the low half):
+// one two-source conversion per part, so the pair is already packed.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+    const float ha = __builtin_bit_cast(float, h << 16);
+    const float hb = __builtin_bit_cast(float, h & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t));
+    hi = h;
+}
+
 // 8 values -> packed bf16 high parts and low parts.
 __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo) {
-    uint32_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) split_bits(v[k], h[k], l[k]);
-    hi = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    lo = uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+    for (int m = 0; m < 4; ++m) split2(v[2 * m], v[2 * m + 1], h[m], l[m]);
+    hi = uint4{h[0], h[1], h[2], h[3]};
+    lo = uint4{l[0], l[1], l[2], l[3]};
 }
 
 // Loads rows k = 0..7 of a staging piece (16 bytes each, zero beyond `valid`).
@@ -143,6 +149,16 @@ __device__ __forceinline__ void load_rows8(const Tin* base, int64_t ld, int vali
 #pragma unroll
     for (int k = 0; k < 8; ++k)
         r[k] = (k < valid) ? *reinterpret_cast<const uint4*>(base + k * ld) : uint4{0u, 0u, 0u, 0u};
+}
+
+// Entry-state layout.  Within a (chunk slot, head) block the P x N fp32 state
+// is stored in the state pass's accumulator order: float4 f = ((tile * 4 + m)
+// * 64 + lane) holds p = 32 (tile & 1) + lane % 32 and n = 32 (tile >> 1) + 8 m
+// + 4 (lane / 32) .. + 3.
+__device__ __forceinline__ void state_pn(int f, int& p, int& n) {
+    const int lane = f & 63, m = (f >> 6) & 3, tile = f >> 8;
+    p = 32 * (tile & 1) + (lane & 31);
+    n = 32 * (tile >> 1) + 8 * m + 4 * (lane >> 5);
 }
 
 // ------------------------------------------------------------------ state pass
@@ -171,14 +187,7 @@ __device__ __forceinline__ void load_rows_clamped(const Tin* base, int64_t ld, i
     for (int k = 0; k < K; ++k) r[k] = *reinterpret_cast<const uint4*>(base + (k < last ? k : last) * ld);
 }
 
-// Packs the TB values of channel j of a staged piece (rows = tokens) as bf16
-// bits, low token in the low half.
-template <int TB>
-__device__ __forceinline__ void pack_tokens(const uint32_t (&h)[TB], uint32_t (&w)[(TB + 1) / 2]) {
-#pragma unroll
-    for (int m = 0; m < TB / 2; ++m) w[m] = h[2 * m] | (h[2 * m + 1] << 16);
-}
-
+// Stores the packed bf16 words of TB tokens of one channel of a staged piece.
 template <int TB>
 __device__ __forceinline__ void store_tokens(u16* dst, const uint32_t (&w)[(TB + 1) / 2]) {
     if constexpr (TB == 8) *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
@@ -222,6 +231,10 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     auto tile_mt = [&](int i) { return (wave * TPW + i) >> 1; };
     auto tile_pt = [&](int i) { return (wave * TPW + i) & 1; };
     auto soff = [&](int i, int m) { return (32 * tile_pt(i) + l32) * N + 32 * tile_mt(i) + 8 * m + 4 * g32; };
+    // Entry states are stored in accumulator order (float4 index ((tile * 4 + m) * 64
+    // + lane)), so each store instruction writes 1 KB in one piece; the chunk
+    // output pass decodes the same order (see state_pn).
+    auto eoff = [&](int i, int m) { return 4 * (((wave * TPW + i) * 4 + m) * 64 + lane); };
     f32x16_t acc[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
@@ -247,8 +260,14 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     const Tin* Xg = static_cast<const Tin*>(a.x);
     const Tin* Bg = static_cast<const Tin*>(a.B);
 
-    const int b_tg = tid % BG, b_cg = tid / BG;   // B piece: tokens TB b_tg.., channels CPL b_cg..
-    const int x_tg = tid % XG, x_cg = tid / XG;   // x piece
+    // B piece: tokens TB b_tg .., channels CPL b_cg .. (a wave reads 8 whole
+    // 128-byte row segments per load for fp32 B).  x piece: for fp32 x a wave
+    // takes 8 token groups x 8 channel groups, so each load also reads whole
+    // 128-byte segments (and 32 lanes' LDS writes cover the 64 banks once).
+    const int b_tg = tid % BG, b_cg = tid / BG;
+    const int x_tg = SP ? (lane & 7) + 8 * (wave & 1) : tid % XG;
+    const int x_cg = SP ? (lane >> 3) + 8 * (wave >> 1) : tid / XG;
+    static_assert(!SP || (XG == 16 && P / CPL == 16), "fp32 x piece mapping");
 
     // Loads of half h (0, 1) of chunk c, clamped to the last chunk so the call is
     // unconditional; rows beyond the chunk re-read its last row (zeroed later).
@@ -271,29 +290,25 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         d1 = a.dt[(r0 + (2 * lane + 1 < S ? 2 * lane + 1 : S - 1)) * a.ld_dt + head];
     };
 
-    // Stage half h of chunk c from b (rows >= Sh zeroed) with weights w0/w1 (rows 2 lane, 2 lane + 1).
-    auto stage = [&](HalfBuf<Tin, TB, TX>& b, int Sh, int h, float w0, float w1) __attribute__((always_inline)) {
+    // Stage half h of chunk c from b with weights w0/w1 (rows 2 lane, 2 lane + 1).
+    // Rows past the sequence's end hold re-read (finite) rows and have weight 0
+    // (dt is zeroed there), so their (w x) is 0 and they add nothing; no mask.
+    auto stage = [&](HalfBuf<Tin, TB, TX>& b, int h, float w0, float w1) __attribute__((always_inline)) {
         // B^T: channel CPL b_cg + j, tokens TB b_tg ..
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            uint32_t hb[TB], lb[TB];
+            uint32_t wh[TB / 2], wl[TB / 2];
 #pragma unroll
-            for (int k = 0; k < TB; ++k) {
-                const bool ok = TB * b_tg + k < Sh;
+            for (int m = 0; m < TB / 2; ++m) {
                 if constexpr (SP) {
-                    split_bits(ok ? In<Tin>::val(b.br[k], j) : 0.f, hb[k], lb[k]);
+                    split2(In<Tin>::val(b.br[2 * m], j), In<Tin>::val(b.br[2 * m + 1], j), wh[m], wl[m]);
                 } else {
-                    hb[k] = ok ? half_of(word_of(b.br[k], j >> 1), j & 1) : 0u;
+                    wh[m] = half_of(word_of(b.br[2 * m], j >> 1), j & 1) |
+                            (half_of(word_of(b.br[2 * m + 1], j >> 1), j & 1) << 16);
                 }
             }
-            uint32_t wh[(TB + 1) / 2];
-            pack_tokens<TB>(hb, wh);
             store_tokens<TB>(BTh + (b_cg * CPL + j) * RH + TB * b_tg, wh);
-            if constexpr (SP) {
-                uint32_t wl[(TB + 1) / 2];
-                pack_tokens<TB>(lb, wl);
-                store_tokens<TB>(BTl + (b_cg * CPL + j) * RH + TB * b_tg, wl);
-            }
+            if constexpr (SP) store_tokens<TB>(BTl + (b_cg * CPL + j) * RH + TB * b_tg, wl);
         }
         // (w x)^T: weights of rows 64 h + TX x_tg + k, held by lane (64 h + TX x_tg + k) / 2
         float wx[TX];
@@ -305,15 +320,11 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            uint32_t hb[TX], lb[TX];
+            uint32_t wh[TX / 2], wl[TX / 2];
 #pragma unroll
-            for (int k = 0; k < TX; ++k) {
-                const bool ok = TX * x_tg + k < Sh;
-                split_bits(ok ? In<Tin>::val(b.xr[k], j) * wx[k] : 0.f, hb[k], lb[k]);
-            }
-            uint32_t wh[(TX + 1) / 2], wl[(TX + 1) / 2];
-            pack_tokens<TX>(hb, wh);
-            pack_tokens<TX>(lb, wl);
+            for (int m = 0; m < TX / 2; ++m)
+                split2(In<Tin>::val(b.xr[2 * m], j) * wx[2 * m], In<Tin>::val(b.xr[2 * m + 1], j) * wx[2 * m + 1],
+                       wh[m], wl[m]);
             store_tokens<TX>(XH + (x_cg * CPL + j) * RH + TX * x_tg, wh);
             store_tokens<TX>(XL + (x_cg * CPL + j) * RH + TX * x_tg, wl);
         }
@@ -342,12 +353,18 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     // One register buffer per half, each refilled a whole chunk ahead; dt of the
     // next chunk is requested right after the gamma scan consumed the current one.
     // Every wait therefore covers loads issued about a chunk earlier, while the
-    // newer ones stay in flight.
+    // newer ones stay in flight.  The first loads go out in the loop's own order
+    // (dt, first half, second half): the compiler's wait counts at the loop head
+    // take the later position of each register over both ways in, so a different
+    // order here would make every chunk wait for both halves at once.
     HalfBuf<Tin, TB, TX> buf0, buf1;
     float d0, d1;
-    load_half(buf0, 0, 0);
-    load_half(buf1, 0, 1);
     load_dt(0, d0, d1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(buf0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(buf1, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
     for (int c = 0; c < nch; ++c) {
         const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
         if (2 * lane >= S) d0 = 0.f;
@@ -366,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         for (int i = 0; i < TPW; ++i) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<float4*>(he + soff(i, m)) =
+                *reinterpret_cast<float4*>(he + eoff(i, m)) =
                     float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
             acc[i] *= decay;
         }
@@ -378,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         const int S0 = S < QH ? S : QH;
         __syncthreads();  // the previous half's products are done with the LDS tiles
         __builtin_amdgcn_sched_barrier(0);
-        stage(buf0, S0, 0, w0, w1);
+        stage(buf0, 0, w0, w1);
         load_half(buf0, c + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         const int S1 = S - QH;
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        stage(buf1, S1, 1, w0, w1);
+        stage(buf1, 1, w0, w1);
         load_half(buf1, c + 1, 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -513,16 +530,16 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             }
             const int off = i * HR + o * CPL;
             if constexpr (SP) {
-                uint32_t bh4[4], bl4[4], ch4[4], cl4[4];
+                uint32_t bh2[2], bl2[2], ch2[2], cl2[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    split_bits(In<Tin>::val(vb, j), bh4[j], bl4[j]);
-                    split_bits(In<Tin>::val(vc, j), ch4[j], cl4[j]);
+                for (int m = 0; m < 2; ++m) {
+                    split2(In<Tin>::val(vb, 2 * m), In<Tin>::val(vb, 2 * m + 1), bh2[m], bl2[m]);
+                    split2(In<Tin>::val(vc, 2 * m), In<Tin>::val(vc, 2 * m + 1), ch2[m], cl2[m]);
                 }
-                *reinterpret_cast<uint2*>(Bh + off) = uint2{bh4[0] | (bh4[1] << 16), bh4[2] | (bh4[3] << 16)};
-                *reinterpret_cast<uint2*>(Bl + off) = uint2{bl4[0] | (bl4[1] << 16), bl4[2] | (bl4[3] << 16)};
-                *reinterpret_cast<uint2*>(Ch + off) = uint2{ch4[0] | (ch4[1] << 16), ch4[2] | (ch4[3] << 16)};
-                *reinterpret_cast<uint2*>(Cl + off) = uint2{cl4[0] | (cl4[1] << 16), cl4[2] | (cl4[3] << 16)};
+                *reinterpret_cast<uint2*>(Bh + off) = uint2{bh2[0], bh2[1]};
+                *reinterpret_cast<uint2*>(Bl + off) = uint2{bl2[0], bl2[1]};
+                *reinterpret_cast<uint2*>(Ch + off) = uint2{ch2[0], ch2[1]};
+                *reinterpret_cast<uint2*>(Cl + off) = uint2{cl2[0], cl2[1]};
             } else {
                 *reinterpret_cast<uint4*>(Bh + off) = vb;
                 *reinterpret_cast<uint4*>(Ch + off) = vc;
@@ -594,18 +611,16 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                 }
             }
         }
-        // h_in split planes: float4 k covers p = idx / N, n = idx % N .. +3
+        // h_in split planes: float4 k of the entry state covers (p, n .. n + 3)
 #pragma unroll
         for (int k = 0; k < NHV; ++k) {
-            const int idx = 4 * (tid + NT * k);
-            const int p = idx / N, n = idx % N;
-            uint32_t hb[4], lb[4];
-            split_bits(hr[k].x, hb[0], lb[0]);
-            split_bits(hr[k].y, hb[1], lb[1]);
-            split_bits(hr[k].z, hb[2], lb[2]);
-            split_bits(hr[k].w, hb[3], lb[3]);
-            *reinterpret_cast<uint2*>(HH + p * NRS + n) = uint2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-            *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+            int p, n;
+            state_pn(tid + NT * k, p, n);
+            uint32_t hb[2], lb[2];
+            split2(hr[k].x, hr[k].y, hb[0], lb[0]);
+            split2(hr[k].z, hr[k].w, hb[1], lb[1]);
+            *reinterpret_cast<uint2*>(HH + p * NRS + n) = uint2{hb[0], hb[1]};
+            *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0], lb[1]};
         }
         if (wave == 0) {
             gam[bf][2 * lane] = ga0;
@@ -694,13 +709,9 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                             for (int r = 0; r < 4; ++r) m[4 * h2 + r] = 0.f;
                         }
                     }
-                    bf16x8_t mh, ml;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const __bf16 hh = static_cast<__bf16>(m[e]);
-                        mh[e] = hh;
-                        ml[e] = static_cast<__bf16>(m[e] - static_cast<float>(hh));
-                    }
+                    uint4 mh4, ml4;
+                    split8(m, mh4, ml4);
+                    const bf16x8_t mh = as_bf16x8(mh4), ml = as_bf16x8(ml4);
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) {
                         const int xo = (16 * pt + l16) * RS + 32 * kb + 4 * q;
