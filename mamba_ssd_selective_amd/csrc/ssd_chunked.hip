@@ -51,7 +51,6 @@ typedef uint16_t u16;
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint4 lds128(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint2 lds64(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
 
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -141,14 +140,6 @@ __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo
     for (int m = 0; m < 4; ++m) split2(v[2 * m], v[2 * m + 1], h[m], l[m]);
     hi = uint4{h[0], h[1], h[2], h[3]};
     lo = uint4{l[0], l[1], l[2], l[3]};
-}
-
-// Loads rows k = 0..7 of a staging piece (16 bytes each, zero beyond `valid`).
-template <typename Tin>
-__device__ __forceinline__ void load_rows8(const Tin* base, int64_t ld, int valid, uint4 (&r)[8]) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        r[k] = (k < valid) ? *reinterpret_cast<const uint4*>(base + k * ld) : uint4{0u, 0u, 0u, 0u};
 }
 
 // Entry-state layout.  Within a (chunk slot, head) block the P x N fp32 state
@@ -488,9 +479,20 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     uint4 xr[8];
     float4 hr[NHV];
     float dr0 = 0.f, dr1 = 0.f;
+    // x piece tg holds the chunk rows the intra products take as one K slot
+    // group: rows 32 kb + 4 q + r (slots 0-3) and 32 kb + 16 + 4 q + r (slots
+    // 4-7), kb = tg / 4, q = tg % 4, so it is staged as one contiguous 16-byte
+    // run per column and read back with one 16-byte LDS read.
+    const int xrow0 = 32 * (tg >> 2) + 4 * (tg & 3);
     auto prefetch = [&](int head) {
-        if (tid < NXP)
-            load_rows8(Xg + (r0 + 8 * tg) * a.ld_x + (int64_t)head * P + (tid / 16) * CPL, a.ld_x, S - 8 * tg, xr);
+        if (tid < NXP) {
+            const Tin* xb = Xg + r0 * a.ld_x + (int64_t)head * P + (tid / 16) * CPL;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int row = xrow0 + (k & 3) + 16 * (k >> 2);
+                xr[k] = row < S ? *reinterpret_cast<const uint4*>(xb + row * a.ld_x) : uint4{0u, 0u, 0u, 0u};
+            }
+        }
         const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
         for (int k = 0; k < NHV; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + NT * k));
@@ -589,7 +591,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             }
         }
 
-        // x^T planes: column (tid / 16) * CPL + jj, tokens 8 tg .. +7
+        // x^T planes: column (tid / 16) * CPL + jj, positions 8 tg .. +7 (the rows above)
         if (tid < NXP) {
 #pragma unroll
             for (int jj = 0; jj < CPL; ++jj) {
@@ -670,8 +672,8 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
 
             // intra-chunk term: X^T M^T over i tile pairs (2kb, 2kb+1); the M^T
             // operand slot j < 4 is row 4q + j of tile 2kb, j >= 4 row 4q + j - 4
-            // of tile 2kb + 1 (the rows this lane's accumulators hold), so x is
-            // read in that row order.
+            // of tile 2kb + 1 (the rows this lane's accumulators hold); the x^T
+            // planes hold the rows in that order (8 per (kb, q) group).
             const float4* cft = reinterpret_cast<const float4*>(colf[bf] + 8 * t);
             const float4 cfa = cft[0], cfb = cft[1];
             const float cfv[8] = {cfa.x, cfa.y, cfa.z, cfa.w, cfb.x, cfb.y, cfb.z, cfb.w};
@@ -714,14 +716,9 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                     const bf16x8_t mh = as_bf16x8(mh4), ml = as_bf16x8(ml4);
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) {
-                        const int xo = (16 * pt + l16) * RS + 32 * kb + 4 * q;
-                        const uint2 a0 = lds64(Xh + xo), a1 = lds64(Xh + xo + 16);
-                        const bf16x8_t xh = as_bf16x8(uint4{a0.x, a0.y, a1.x, a1.y});
-                        bf16x8_t xl = xh;
-                        if constexpr (SP) {
-                            const uint2 b0 = lds64(Xl + xo), b1 = lds64(Xl + xo + 16);
-                            xl = as_bf16x8(uint4{b0.x, b0.y, b1.x, b1.y});
-                        }
+                        const int xo = (16 * pt + l16) * RS + 32 * kb + 8 * q;
+                        const bf16x8_t xh = as_bf16x8(lds128(Xh + xo));
+                        const bf16x8_t xl = SP ? as_bf16x8(lds128(Xl + (SP ? xo : 0))) : xh;
                         mma2<SP, true>(yacc[pt], xh, xl, mh, ml);
                     }
                 }
