@@ -8,8 +8,9 @@
 // SiLU; section 10: the conv state keeps (width - 1) rows per channel.
 //
 // The conv is HBM-bound (4 multiply-adds per element read), so the kernel is a
-// streaming pass: a thread owns CPT = 8 adjacent channels (one 16-byte bf16
-// load, two for fp32) and a run of TOK consecutive packed rows.  It issues the
+// streaming pass: a thread owns CPT = 4 adjacent channels (an 8-byte bf16 load,
+// a 16-byte fp32 one, one 16-byte store per fp32 output row) and a run of TOK
+// consecutive packed rows.  It issues the
 // loads of the run's rows and 3-row halo first, then slides a window over
 // registers; a run that starts a sequence or crosses into another one goes row
 // by row instead, refilling the window from the slot's conv state (or zeros).
@@ -24,7 +25,7 @@ namespace m2 {
 namespace {
 
 constexpr int TOK = 16;    // rows per thread
-constexpr int CPT = 8;     // channels per thread
+constexpr int CPT = 4;     // channels per thread
 constexpr int BLOCK = 256;
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int64_t t) {
@@ -181,7 +182,10 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     int b = seq_of(a.cu_seqlens, a.batch, t0);
     int64_t s0 = a.cu_seqlens[b];
     int64_t s1 = a.cu_seqlens[b + 1];
-    Tout* out = static_cast<Tout*>(a.out);
+    // this thread's output column (its CPT channels lie in one output block)
+    const int obw = a.out_bw[bs.seg];
+    Tout* const ocol = static_cast<Tout*>(a.out_ptr[bs.seg]) + (int64_t)(cs / obw) * a.out_bs[bs.seg] + cs % obw;
+    const int64_t old = a.out_ld[bs.seg];
 
     if (t0 - 3 >= s0 && t0 + TOK <= s1) {
         // A full run whose 3-row halo lies inside the same sequence: the rows
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
                 return (T)__builtin_bit_cast(float, raw[k][c]);
             }
         };
-        Tout* dst = out + t0 * a.ld_out + c0;
+        Tout* dst = ocol + t0 * old;
 #pragma unroll
         for (int k = 0; k < TOK; ++k) {
             T o[CPT];
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
                 acc = fma(w[c][3], val(k + 3, c), acc);
                 o[c] = a.apply_silu ? silu(acc) : acc;
             }
-            store_out(dst + k * a.ld_out, o);
+            store_out(dst + k * old, o);
         }
         return;
     }
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
             win[1][c] = win[2][c];
             win[2][c] = cur;
         }
-        store_out(out + t * a.ld_out + c0, o);
+        store_out(ocol + t * old, o);
     }
 }
 

@@ -31,15 +31,23 @@ struct ConvArgs {
     const int32_t* state_idx;   // [batch] or null
     const uint8_t* has_init;    // [batch] or null
     int apply_silu;
-    void* out;
-    int64_t ld_out;
+    // Output: channel c of segment s (c counted within the segment) in row t is
+    // element (c / out_bw[s]) * out_bs[s] + t * out_ld[s] + c % out_bw[s] of
+    // out_ptr[s].  Row-major output: out_bw = the segment's channels, out_bs = 0;
+    // the prefill's blocked layout: one block per head (x) or group (B, C).
+    void* out_ptr[3];
+    int64_t out_ld[3];
+    int64_t out_bs[3];
+    int out_bw[3];
     int out_dtype;
 };
 
 struct ScanArgs {
-    const void* x; int64_t ld_x;
-    const void* B; int64_t ld_B;
-    const void* C; int64_t ld_C;
+    // x[t, head, p] = x + t * ld_x + head * hs_x + p; B[t, g, n] = B + t * ld_B + g * gs_B + n
+    // (row-major: hs_x = headdim, gs_B = gs_C = dstate)
+    const void* x; int64_t ld_x; int64_t hs_x;
+    const void* B; int64_t ld_B; int64_t gs_B;
+    const void* C; int64_t ld_C; int64_t gs_C;
     int act_dtype;              // storage type of x, B, C
     int policy;                 // Policy
     const float* dt; int64_t ld_dt;

@@ -269,9 +269,9 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
         // an empty half (the chunk ends in its first half) reads the chunk's first row
         const int64_t r0 = s0 + (int64_t)c * Q + (S > 0 ? h * QH : 0);
         const int rb = TB * b_tg < S ? TB * b_tg : 0;
-        load_rows_clamped<TB>(Bg + (r0 + rb) * a.ld_B + grp * N + b_cg * CPL, a.ld_B, S - rb, b.br);
+        load_rows_clamped<TB>(Bg + (r0 + rb) * a.ld_B + grp * a.gs_B + b_cg * CPL, a.ld_B, S - rb, b.br);
         const int rx = TX * x_tg < S ? TX * x_tg : 0;
-        load_rows_clamped<TX>(Xg + (r0 + rx) * a.ld_x + (int64_t)head * P + x_cg * CPL, a.ld_x, S - rx, b.xr);
+        load_rows_clamped<TX>(Xg + (r0 + rx) * a.ld_x + head * a.hs_x + x_cg * CPL, a.ld_x, S - rx, b.xr);
     };
     auto load_dt = [&](int c, float& d0, float& d1) __attribute__((always_inline)) {
         c = c < nch ? c : nch - 1;
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     const int xrow0 = 32 * (tg >> 2) + 4 * (tg & 3);
     auto prefetch = [&](int head) {
         if (tid < NXP) {
-            const Tin* xb = Xg + r0 * a.ld_x + (int64_t)head * P + (tid / 16) * CPL;
+            const Tin* xb = Xg + r0 * a.ld_x + head * a.hs_x + (tid / 16) * CPL;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int row = xrow0 + (k & 3) + 16 * (k >> 2);
@@ -524,11 +524,11 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         constexpr int PPR = 64 / CPL;  // pieces per 64-n row slice
         for (int e = tid; e < Q * PPR; e += NT) {
             const int i = e / PPR, o = e % PPR;
-            const int64_t col = grp * N + 64 * ps + o * CPL;
+            const int col = 64 * ps + o * CPL;
             uint4 vb = uint4{0u, 0u, 0u, 0u}, vc = vb;
             if (i < S) {
-                vb = *reinterpret_cast<const uint4*>(Bg + (r0 + i) * a.ld_B + col);
-                vc = *reinterpret_cast<const uint4*>(Cg + (r0 + i) * a.ld_C + col);
+                vb = *reinterpret_cast<const uint4*>(Bg + (r0 + i) * a.ld_B + grp * a.gs_B + col);
+                vc = *reinterpret_cast<const uint4*>(Cg + (r0 + i) * a.ld_C + grp * a.gs_C + col);
             }
             const int off = i * HR + o * CPL;
             if constexpr (SP) {

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
                 const int n0 = (e % PER_ROW) * 8;
                 V vb[8], vc[8];
                 if (i < S) {
-                    load8(Bg + (r0 + i) * a.ld_B + grp * N + n0, vb);
-                    load8(Cg + (r0 + i) * a.ld_C + grp * N + n0, vc);
+                    load8(Bg + (r0 + i) * a.ld_B + grp * a.gs_B + n0, vb);
+                    load8(Cg + (r0 + i) * a.ld_C + grp * a.gs_C + n0, vc);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) { vb[j] = 0; vc[j] = 0; }
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = 32 * kb + kslot<Pol>(q, j);
-                xr[kb][j] = (i < S) ? (V)Act<Tin>::load(X + (r0 + i) * a.ld_x + (int64_t)head * P + p) : (V)0;
+                xr[kb][j] = (i < S) ? (V)Act<Tin>::load(X + (r0 + i) * a.ld_x + head * a.hs_x + p) : (V)0;
             }
         }
         __syncthreads();
