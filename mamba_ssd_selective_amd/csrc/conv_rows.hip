@@ -24,9 +24,9 @@
 namespace m2 {
 namespace {
 
-constexpr int TOK = 16;    // rows per thread
+constexpr int TOK = 24;    // rows per thread
 constexpr int CPT = 4;     // channels per thread
-constexpr int BLOCK = 256;
+constexpr int BLOCK = 128;
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int64_t t) {
     // last b with cu[b] <= t and cu[b+1] > t (skips empty sequences)
