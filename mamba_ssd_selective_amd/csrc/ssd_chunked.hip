@@ -186,24 +186,36 @@ __device__ __forceinline__ void store_tokens(u16* dst, const uint32_t (&w)[(TB +
     else *reinterpret_cast<uint32_t*>(dst) = w[0];
 }
 
-template <int N, typename Tin>
-__global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
+// IPW = 2: one workgroup of 8 waves takes heads 2k and 2k + 1 of one sequence
+// (one group): waves 0-3 the first, 4-7 the second.  The two heads read and
+// stage the group's B tile once, into one shared LDS tile, which halves the B
+// loads, the largest part of the per-CU load instructions (the vector memory
+// units of a CU were busy 80-90% of the kernel).  Both items share their
+// sequence, so they have the same chunk count and take every barrier together.
+template <int N, int IPW, typename Tin>
+__global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_kernel(ScanArgs a) {
     constexpr bool SP = In<Tin>::kSplit;
     constexpr int CPL = In<Tin>::CPL;
-    constexpr int NT = 256;
+    constexpr int NT = 256;                            // threads per item
+    constexpr int NTB = NT * IPW;                      // threads that stage B
     constexpr int TPW = N / 64;                        // 32x32 state tiles per wave
-    constexpr int TB = QH * N / (CPL * NT);            // tokens per B piece (one piece per thread)
+    constexpr int TB = QH * N / (CPL * NTB);           // tokens per B piece (one piece per thread)
     constexpr int TX = QH * P / (CPL * NT);            // tokens per x piece
-    constexpr int BG = QH / TB, XG = QH / TX;          // token groups (fastest across lanes)
+    constexpr int BG = QH / TB, XG = QH / TX;          // token groups
+    constexpr int BC = N / CPL;                        // B channel groups
     static_assert(TB >= 2 && TX >= 2, "staging pieces");
     __shared__ __align__(16) u16 BTh[N * RH];           // B^T [n][token of the half], high parts
     __shared__ __align__(16) u16 BTl[SP ? N * RH : 8];  // low parts (fp32 inputs)
-    __shared__ __align__(16) u16 XH[P * RH];            // (w x)^T [p][token], high parts
-    __shared__ __align__(16) u16 XL[P * RH];            // low parts
+    __shared__ __align__(16) u16 sXH[IPW][P * RH];      // (w x)^T [p][token] per item, high parts
+    __shared__ __align__(16) u16 sXL[IPW][P * RH];      // low parts
 
-    const int tid = threadIdx.x;
+    const int sub = IPW > 1 ? (int)(threadIdx.x >> 8) : 0;   // item within the workgroup
+    u16* const XH = sXH[sub];
+    u16* const XL = sXL[sub];
+    const int tid = threadIdx.x & (NT - 1);
     const int wave = tid >> 6, lane = tid & 63;
-    const int item = item_of(blockIdx.x, a.nheads * a.batch);
+    const int gwave = (int)(threadIdx.x >> 6);                // wave within the workgroup
+    const int item = IPW * item_of(blockIdx.x, a.nheads * a.batch / IPW) + sub;
     const int seq = item / a.nheads, head = item % a.nheads;
     const int grp = head / (a.nheads / a.ngroups);
     const int64_t s0 = a.cu_seqlens[seq];
@@ -255,7 +267,10 @@ __global__ __launch_bounds__(256, 2) void ssd_state_pass_kernel(ScanArgs a) {
     // 128-byte row segments per load for fp32 B).  x piece: for fp32 x a wave
     // takes 8 token groups x 8 channel groups, so each load also reads whole
     // 128-byte segments (and 32 lanes' LDS writes cover the 64 banks once).
-    const int b_tg = tid % BG, b_cg = tid / BG;
+    // (B: each wave takes 8 token groups x 8 channel groups when the shape allows)
+    constexpr bool B88 = BC % 8 == 0 && BG % 8 == 0 && (BC / 8) * (BG / 8) == NTB / 64;
+    const int b_tg = B88 ? (lane & 7) + 8 * (gwave / (BC / 8)) : (int)threadIdx.x % BG;
+    const int b_cg = B88 ? (lane >> 3) + 8 * (gwave % (BC / 8)) : (int)threadIdx.x / BG;
     const int x_tg = SP ? (lane & 7) + 8 * (wave & 1) : tid % XG;
     const int x_cg = SP ? (lane >> 3) + 8 * (wave >> 1) : tid / XG;
     static_assert(!SP || (XG == 16 && P / CPL == 16), "fp32 x piece mapping");
@@ -761,7 +776,13 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
 
 template <int N, typename Tin>
 hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((ssd_state_pass_kernel<N, Tin>), dim3(a.nheads * a.batch), dim3(256), 0, stream, a);
+    if constexpr (N == 128) {
+        if ((a.nheads / a.ngroups) % 2 == 0) {
+            hipLaunchKernelGGL((ssd_state_pass_kernel<N, 2, Tin>), dim3(a.nheads * a.batch / 2), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((ssd_state_pass_kernel<N, 1, Tin>), dim3(a.nheads * a.batch), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
