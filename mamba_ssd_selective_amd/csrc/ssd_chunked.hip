@@ -533,18 +533,32 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     f32x4_t g[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) g[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Every slice's B and C pieces are requested up front, branch-free (rows
+    // clamped into the chunk): with a load and its use in the same iteration the
+    // slices cost one memory round trip per piece.  Rows past the chunk's end
+    // only reach G entries that the causal mask or a zero dt leaves unused.
+    constexpr int PPR = 64 / CPL;            // pieces per 64-n row slice
+    constexpr int GIT = Q * PPR / NT;        // pieces per thread per slice
+    uint4 gbv[NPASS][GIT], gcv[NPASS][GIT];
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+        for (int k = 0; k < GIT; ++k) {
+            const int e = tid + NT * k;
+            const int i = e / PPR, o = e % PPR;
+            const int64_t row = r0 + (i < S ? i : S - 1);
+            const int col = 64 * ps + o * CPL;
+            gbv[ps][k] = *reinterpret_cast<const uint4*>(Bg + row * a.ld_B + grp * a.gs_B + col);
+            gcv[ps][k] = *reinterpret_cast<const uint4*>(Cg + row * a.ld_C + grp * a.gs_C + col);
+        }
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
         if (ps > 0) __syncthreads();   // the previous slice's products are done
-        constexpr int PPR = 64 / CPL;  // pieces per 64-n row slice
-        for (int e = tid; e < Q * PPR; e += NT) {
+#pragma unroll
+        for (int k = 0; k < GIT; ++k) {
+            const int e = tid + NT * k;
             const int i = e / PPR, o = e % PPR;
-            const int col = 64 * ps + o * CPL;
-            uint4 vb = uint4{0u, 0u, 0u, 0u}, vc = vb;
-            if (i < S) {
-                vb = *reinterpret_cast<const uint4*>(Bg + (r0 + i) * a.ld_B + grp * a.gs_B + col);
-                vc = *reinterpret_cast<const uint4*>(Cg + (r0 + i) * a.ld_C + grp * a.gs_C + col);
-            }
+            const uint4 vb = gbv[ps][k], vc = gcv[ps][k];
             const int off = i * HR + o * CPL;
             if constexpr (SP) {
                 uint32_t bh2[2], bl2[2], ch2[2], cl2[2];
