@@ -201,9 +201,9 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
 /*
  * Bytes of device workspace mamba2_prefill needs for these sizes and this
  * activation dtype (0 on bad arguments).  The workspace holds the post-conv
- * activations of the batch (bf16 for bf16 inputs, fp64 for fp32 inputs), the
- * fp32 pre-norm output and, on the chunk-parallel scan path, the state
- * entering every chunk.
+ * activations of the batch (fp32 for bf16 inputs, fp64 for fp32 inputs; on the
+ * chunk-parallel scan path blocked per head and per group), the fp32 pre-norm
+ * output and, on the chunk-parallel scan path, the state entering every chunk.
  */
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
                                      int nheads, int headdim, int dstate, int ngroups,

@@ -10,8 +10,9 @@
 // The only sequential dependence between chunks is h_in, so the work splits in
 // two kernels:
 //
-//  state pass  one workgroup per (sequence, head) walks the chunks in order and
-//              keeps h^T [N x P] in matrix-core accumulators.  Per chunk it
+//  state pass  walks the chunks of a (sequence, head) in order and keeps h^T
+//              [N x P] in matrix-core accumulators (two heads of one group per
+//              workgroup when they can share the staged B tile).  Per chunk it
 //              writes h_in to the entry-state buffer, scales the accumulators by
 //              e(gamma_S) and adds B^T (dt e(gamma_S - gamma_i) x) with the
 //              accumulators as the running sum.  Only B, x and dt are read.
@@ -21,17 +22,20 @@
 //              M^T[i, t] = G^T[i, t] dt_i e(gamma_t - gamma_i) (i <= t) and D on
 //              the diagonal, and stores y.
 //
-// Operands: x, B and C are bf16 already, so they feed the bf16 matrix
-// instructions exactly.  The computed operands (dt-weighted x, M^T, h_in) are
-// split as v = hi + lo (hi = bf16(v), lo = bf16(v - hi)) and enter two products
-// (hi and lo), so every product is exact to ~2^-17 relative with fp32
-// accumulation.  Cumulative sums of a are fp64, exponent differences fp64,
+// Operands: x, B and C come as fp32 (the prefill's post-conv activations) or
+// as bf16 (given to the scan directly, then exact in bf16).  Every fp32 operand,
+// input or computed (dt-weighted x, M^T, h_in), is split as v = hi + lo (hi =
+// bf16(v), lo = bf16(v - hi)); a product takes hi*hi + hi*lo + lo*hi (lo*lo,
+// ~2^-18 relative, is dropped) with fp32 accumulation, and a bf16 operand skips
+// its lo products.  Cumulative sums of a are fp64, exponent differences fp64,
 // clamped, then exp'd in fp32.
 //
-// Matrix-core tile layout (16x16x32 bf16): an A operand lane l holds row l%16
-// and K slots 8(l/16)..8(l/16)+7; a B operand lane holds column l%16 and the
-// same K slots; the 16x16 fp32 result lands with lane l holding column l%16 and
-// rows 4(l/16)+r in register r.
+// Matrix-core tile layouts.  16x16x32 bf16 (chunk out): an A operand lane l
+// holds row l%16 and K slots 8(l/16)..8(l/16)+7; a B operand lane holds column
+// l%16 and the same K slots; the 16x16 fp32 result lands with lane l holding
+// column l%16 and rows 4(l/16)+r in register r.  32x32x16 bf16 (state pass): an
+// operand lane holds row (or column) l%32 and K slots 8(l/32)..+7; result
+// register r of lane l is column l%32, row 8(r/4) + 4(l/32) + r%4.
 
 #include <type_traits>
 
