@@ -15,7 +15,9 @@
  *      section 4.1 "Mamba2 SSM layer" gives the token recurrence it equals);
  *   3. the grouped gated RMSNorm with z (page "Nemotron-H", section 4.1:
  *      GroupRMSNorm(y, ssm_norm.weight), then the SiLU(z) gate; the NemotronH
- *      decode page names the op RmsNormGatedGroup(n_groups)).
+ *      decode page names the op RmsNormGatedGroup(n_groups));
+ * and the single-token decode step of the same layer at cache slots
+ * (mamba2_decode), which continues the states a prefill left.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -234,6 +236,50 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                    void* y, int64_t ld_y, int y_dtype,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * mamba2_decode -- one new token for each of `batch` sequences, at their cache
+ * slots: the conv update, the selective state update with its readout and the
+ * grouped gated RMSNorm, in one fused kernel (page "NemotronH decodes on the
+ * single-step recurrent kernels", PR description: decode rows take the
+ * single-step conv update and state update at their slots, in place, with no
+ * gather or scatter; page "Nemotron-H", section 4.1 for the recurrence and the
+ * norm).  Row b of every token-indexed argument is sequence b's new token; the
+ * result equals mamba2_prefill over one-token sequences (cu_seqlens = 0, 1, ..,
+ * batch) up to rounding.  Per sequence b with slot s = state_idx[b] (NULL:
+ * s = b), all states zero when has_init[b] == 0, group g = h / (nheads/ngroups)
+ * and e(v) = exp(min(v, 0)):
+ *   xpad      = [conv_state[s] (3 rows) ; the new x | B | C row]
+ *   u[c]      = SiLU(conv_b[c] + sum_k conv_w[c, k] * xpad[k, c]),  split into x, B, C
+ *   conv_state[s] <- rows 1..3 of xpad
+ *   h[h,p,:]  <- e(dt[b,h] * A[h]) * h[h,p,:] + dt[b,h] * x[h,p] * B[g,:]
+ *   ypre[h,p] = C[g,:] . h[h,p,:] + D[h] * x[h,p]
+ *   y         = the gated grouped RMSNorm of ypre with z, as in gated_rmsnorm_group
+ *
+ *   x [batch, nheads*headdim] (ld_x), B, C [batch, ngroups*dstate] (ld_B, ld_C),
+ *     z [batch, nheads*headdim] (ld_z): element type act_dtype;
+ *   dt [batch, nheads] fp32 (ld_dt), the final step size, expected >= 0;
+ *   A, D, conv_w, conv_b, norm_w, eps, norm_before_gate: as for mamba2_prefill;
+ *   conv_state [n_slots, 3, conv_dim], ssm_state [n_slots, nheads, headdim,
+ *     dstate] fp32, read and advanced in place;
+ *   y [batch, nheads*headdim] (ld_y), element type y_dtype; must not overlap
+ *     an input or a state.
+ * batch == 0 is a no-op (after the dtype, shape and stride checks; the
+ * pointers may then be NULL).  Slots used in one call must be distinct.  Alignment:
+ * conv_w and ssm_state 16-byte aligned (the other arrays are read per element).
+ * Supported (headdim, dstate): (16,16), (32,64), (64,64), (64,128), with a
+ * group width (nheads/ngroups)*headdim of at most 2048.  No workspace.
+ * Arithmetic: fp32, one rounding order fixed per shape (deterministic).
+ */
+int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
+                  const void* C, int64_t ld_C, const void* z, int64_t ld_z, int act_dtype,
+                  const float* dt, int64_t ld_dt, const float* A, const float* D,
+                  const float* conv_w, const float* conv_b, const float* norm_w,
+                  float eps, int norm_before_gate,
+                  float* conv_state, float* ssm_state, int n_slots, int batch,
+                  const int32_t* state_idx, const uint8_t* has_init,
+                  int nheads, int headdim, int dstate, int ngroups,
+                  void* y, int64_t ld_y, int y_dtype, void* stream);
+
 /* Launch counters (process-wide, atomic): which kernels ran, per instantiation. */
 typedef struct {
     uint64_t conv_launches;        /* conv kernel launches */
@@ -243,6 +289,7 @@ typedef struct {
     uint64_t norm_launches;        /* gated norm launches */
     uint64_t prefill_calls;        /* successful mamba2_prefill calls */
     uint64_t scan_chunked_launches; /* scan launches, chunk-parallel path (bf16 inputs) */
+    uint64_t decode_launches;      /* fused decode-step launches */
 } m2_counters;
 
 /* Copy the counters into *out (M2_ERR_NULL if out is NULL). */

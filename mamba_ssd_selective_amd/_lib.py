@@ -33,7 +33,7 @@ class Counters(ctypes.Structure):
     _fields_ = [("conv_launches", ctypes.c_uint64), ("conv_state_launches", ctypes.c_uint64),
                 ("scan_f64_launches", ctypes.c_uint64), ("scan_bf16x3_launches", ctypes.c_uint64),
                 ("norm_launches", ctypes.c_uint64), ("prefill_calls", ctypes.c_uint64),
-                ("scan_chunked_launches", ctypes.c_uint64)]
+                ("scan_chunked_launches", ctypes.c_uint64), ("decode_launches", ctypes.c_uint64)]
 
 
 class KernelTimes(ctypes.Structure):
@@ -66,6 +66,8 @@ _SIGS = {
     "mamba2_prefill": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
                             _F, _I, _P, _P, _I, _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I,
                             _P, _L, _I, _P, ctypes.c_size_t, _P]),
+    "mamba2_decode": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
+                           _F, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _L, _I, _P]),
 }
 
 _lib = None
@@ -296,5 +298,40 @@ def mamba2_prefill(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm
         _ptr(conv_state), _ptr(ssm_state), conv_state.size(0), _ptr(cu_seqlens), batch, T,
         int(max_seqlen), _ptr(state_idx), _ptr(has_init), nheads, headdim, dstate, ngroups,
         chunk_size, _ptr(y), _rows(y, "y"), _dtype_code(y), _ptr(workspace), ws_bytes, _stream())
+    _check(st)
+    return y
+
+
+def mamba2_decode(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                  nheads, headdim, dstate, ngroups, state_idx=None, has_init=None, eps=1e-5,
+                  norm_before_gate=True, y=None, y_dtype=torch.float32):
+    """One decode token per sequence at its cache slot (conv update, state update,
+    readout, D skip, gated group norm), both states advanced in place.
+
+    x [batch, H*P], B, C [batch, G*N], z [batch, H*P] (one activation dtype),
+    dt [batch, H] fp32.  Returns y [batch, H*P].
+    """
+    lib = load()
+    batch = x.size(0)
+    if y is None:
+        y = torch.empty((batch, nheads * headdim), dtype=y_dtype, device=x.device)
+    for t, n in ((A, "A"), (D, "D"), (conv_w, "conv_w"), (conv_b, "conv_b"), (norm_w, "norm_w"),
+                 (conv_state, "conv_state"), (ssm_state, "ssm_state")):
+        _vec(t, n, torch.float32)
+    _vec(state_idx, "state_idx", torch.int32)
+    _vec(has_init, "has_init", torch.uint8)
+    if dt.dtype != torch.float32:
+        raise ValueError("dt must be float32")
+    if not (x.dtype == B.dtype == C.dtype == z.dtype):
+        raise ValueError("x, B, C and z must share one dtype")
+    if conv_state.size(0) != ssm_state.size(0):
+        raise ValueError("conv_state and ssm_state must have the same number of slots")
+    st = lib.mamba2_decode(
+        _ptr(x), _rows(x, "x"), _ptr(B), _rows(B, "B"), _ptr(C), _rows(C, "C"),
+        _ptr(z), _rows(z, "z"), _dtype_code(x), _ptr(dt), _rows(dt, "dt"), _ptr(A), _ptr(D),
+        _ptr(conv_w), _ptr(conv_b), _ptr(norm_w), float(eps), int(bool(norm_before_gate)),
+        _ptr(conv_state), _ptr(ssm_state), conv_state.size(0), batch, _ptr(state_idx),
+        _ptr(has_init), nheads, headdim, dstate, ngroups, _ptr(y), _rows(y, "y"),
+        _dtype_code(y), _stream())
     _check(st)
     return y

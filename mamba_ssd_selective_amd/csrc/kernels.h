@@ -75,11 +75,41 @@ struct NormArgs {
     void* out; int64_t ld_out; int out_dtype;
 };
 
+struct DecodeArgs {
+    // One row per sequence: x [batch, nheads*headdim], B and C [batch, ngroups*dstate],
+    // z [batch, nheads*headdim] (act_dtype), dt [batch, nheads] fp32.
+    const void* x; int64_t ld_x;
+    const void* B; int64_t ld_B;
+    const void* C; int64_t ld_C;
+    const void* z; int64_t ld_z;
+    int act_dtype;
+    const float* dt; int64_t ld_dt;
+    const float* A;
+    const float* D;             // or null
+    const float* conv_w;        // [conv_dim, 4]
+    const float* conv_b;        // or null
+    const float* norm_w;        // [nheads*headdim]
+    float eps;
+    int norm_before_gate;
+    float* conv_state;          // [n_slots, 3, conv_dim]
+    float* ssm_state;           // [n_slots, H, P, N]
+    int batch;
+    const int32_t* state_idx;   // or null
+    const uint8_t* has_init;    // or null
+    int nheads, headdim, dstate, ngroups;
+    void* y; int64_t ld_y; int y_dtype;
+};
+
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
 hipError_t launch_conv_rows(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_conv_state_update(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_gated_norm(const NormArgs& a, hipStream_t stream);
+
+// Single-token decode step (decode_step.hip): one fused kernel, one workgroup
+// per (sequence, group).
+bool decode_supported(int nheads, int ngroups, int headdim, int dstate);
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
 
 // True when a scan kernel is compiled for this (headdim, dstate).
 bool scan_supported(int headdim, int dstate);

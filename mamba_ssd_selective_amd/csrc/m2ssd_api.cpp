@@ -22,7 +22,7 @@ thread_local std::string g_last_error;
 
 struct Counters {
     std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f64{0}, scan_bf16x3{0}, norm{0}, prefill{0},
-        scan_chunked{0};
+        scan_chunked{0}, decode{0};
 } g_counters;
 
 // Event recorder for m2_timing_*: set k holds kEv events around the kernel
@@ -242,6 +242,7 @@ int m2_get_counters(m2_counters* out) {
     out->norm_launches = g_counters.norm.load();
     out->prefill_calls = g_counters.prefill.load();
     out->scan_chunked_launches = g_counters.scan_chunked.load();
+    out->decode_launches = g_counters.decode.load();
     return ok();
 }
 
@@ -253,6 +254,7 @@ void m2_reset_counters(void) {
     g_counters.norm = 0;
     g_counters.prefill = 0;
     g_counters.scan_chunked = 0;
+    g_counters.decode = 0;
 }
 
 int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -472,6 +474,56 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     }
     mark(5);
     g_counters.prefill++;
+    return ok();
+}
+
+int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                  int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
+                  int64_t ld_dt, const float* A, const float* D, const float* conv_w,
+                  const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
+                  float* conv_state, float* ssm_state, int n_slots, int batch,
+                  const int32_t* state_idx, const uint8_t* has_init, int nheads, int headdim,
+                  int dstate, int ngroups, void* y, int64_t ld_y, int y_dtype, void* stream) {
+    if (!valid_dtype(act_dtype) || !valid_dtype(y_dtype))
+        return fail(M2_ERR_DTYPE, "decode: act_dtype and y_dtype must be M2_F32 or M2_BF16");
+    if (batch < 0 || n_slots <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return fail(M2_ERR_SHAPE, "decode: batch must be >= 0 and n_slots, nheads, headdim, dstate, ngroups positive");
+    if (nheads % ngroups) return fail(M2_ERR_SHAPE, "decode: nheads %% ngroups != 0 (%d, %d)", nheads, ngroups);
+    if (!state_idx && n_slots < batch) return fail(M2_ERR_SHAPE, "decode: state_idx NULL needs n_slots >= batch");
+    if (!m2::decode_supported(nheads, ngroups, headdim, dstate))
+        return fail(M2_ERR_UNSUPPORTED, "decode: no kernel for headdim=%d dstate=%d with group width %d",
+                    headdim, dstate, nheads / ngroups * headdim);
+    const int64_t di = (int64_t)nheads * headdim, gn = (int64_t)ngroups * dstate;
+    if (ld_x < di || ld_B < gn || ld_C < gn || ld_z < di || ld_dt < nheads || ld_y < di)
+        return fail(M2_ERR_STRIDE, "decode: a row stride is smaller than its row width");
+    if (batch == 0) return ok();
+    if (!x || !B || !C || !z || !dt || !A || !conv_w || !norm_w || !conv_state || !ssm_state || !y)
+        return fail(M2_ERR_NULL, "decode: x, B, C, z, dt, A, conv_w, norm_w, both states and y are required");
+    if (!aligned16(conv_w) || !aligned16(ssm_state))
+        return fail(M2_ERR_ALIGN, "decode: conv_w and ssm_state must be 16-byte aligned");
+    if (debug_enabled() && state_idx) {
+        std::vector<int32_t> hidx(batch);
+        if (hipMemcpy(hidx.data(), state_idx, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
+            return fail(M2_ERR_HIP, "debug: reading state_idx failed");
+        std::vector<char> seen(n_slots, 0);
+        for (int b = 0; b < batch; ++b) {
+            if (hidx[b] < 0 || hidx[b] >= n_slots)
+                return fail(M2_ERR_SHAPE, "debug: state_idx[%d]=%d outside [0, %d)", b, hidx[b], n_slots);
+            if (seen[hidx[b]]++)
+                return fail(M2_ERR_SHAPE, "debug: state_idx[%d]=%d repeats a slot", b, hidx[b]);
+        }
+    }
+    m2::DecodeArgs a{};
+    a.x = x; a.ld_x = ld_x; a.B = B; a.ld_B = ld_B; a.C = C; a.ld_C = ld_C; a.z = z; a.ld_z = ld_z;
+    a.act_dtype = act_dtype; a.dt = dt; a.ld_dt = ld_dt; a.A = A; a.D = D;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.norm_w = norm_w; a.eps = eps;
+    a.norm_before_gate = norm_before_gate; a.conv_state = conv_state; a.ssm_state = ssm_state;
+    a.batch = batch; a.state_idx = state_idx; a.has_init = has_init;
+    a.nheads = nheads; a.headdim = headdim; a.dstate = dstate; a.ngroups = ngroups;
+    a.y = y; a.ld_y = ld_y; a.y_dtype = y_dtype;
+    int st;
+    if ((st = hip_status(m2::launch_decode_step(a, static_cast<hipStream_t>(stream)), "decode launch"))) return st;
+    g_counters.decode++;
     return ok();
 }
 

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mamba2_conv_rows", "ssd_chunk_scan", "ssd_chunk_scan_workspace_size",
               "gated_rmsnorm_group", "mamba2_prefill", "mamba2_prefill_workspace_size",
-              "m2_last_error", "m2_get_counters"):
+              "mamba2_decode", "m2_last_error", "m2_get_counters"):
         assert n in names
 
 
@@ -109,3 +109,37 @@ def test_scan_workspace_query():
     # the prefill workspace includes it, plus fp32 activations and the fp32 pre-norm output
     n = lib.mamba2_prefill_workspace_size(1000, 3, 1000, 64, 64, 128, 8, 128, 1)
     assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4 + (1000 // 128 + 3) * per_slot
+
+
+def _decode(lib, **kw):
+    a = dict(x=16, ld_x=64, B=32, ld_B=32, C=48, ld_C=32, z=64, ld_z=64, act=0, dt=80, ld_dt=4,
+             A=96, D=None, cw=112, cb=None, nw=128, cs=144, ss=160, n_slots=2, batch=2, idx=None,
+             init=None, H=4, P=16, N=16, G=2, y=176, ld_y=64, ydt=0)
+    a.update(kw)
+    return lib.mamba2_decode(a["x"], a["ld_x"], a["B"], a["ld_B"], a["C"], a["ld_C"], a["z"],
+                             a["ld_z"], a["act"], a["dt"], a["ld_dt"], a["A"], a["D"], a["cw"],
+                             a["cb"], a["nw"], 1e-5, 1, a["cs"], a["ss"], a["n_slots"], a["batch"],
+                             a["idx"], a["init"], a["H"], a["P"], a["N"], a["G"], a["y"],
+                             a["ld_y"], a["ydt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(ss=None), -1), (dict(act=2), -3), (dict(ydt=5), -3),
+    (dict(batch=-1), -2), (dict(G=3), -2), (dict(n_slots=1), -2), (dict(n_slots=0), -2),
+    (dict(P=24), -7), (dict(N=32), -7), (dict(H=64, G=1, ld_x=4096, ld_z=4096, ld_y=4096, ld_dt=64,
+                                              P=64, N=128, ld_B=128, ld_C=128), -7),
+    (dict(ld_x=60), -5), (dict(ld_B=31), -5), (dict(ld_dt=3), -5), (dict(ld_y=10), -5),
+    (dict(ss=168), -6), (dict(cw=120), -6),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    """Host validation of mamba2_decode (fake, never dereferenced pointers)."""
+    lib = m2.load()
+    assert _decode(lib, **kw) == code
+    assert lib.m2_last_error().decode() != ""
+
+
+def test_decode_empty_batch_is_a_no_op():
+    """batch 0 returns M2_OK after the shape checks, without touching any pointer."""
+    lib = m2.load()
+    assert _decode(lib, batch=0, x=None, B=None, C=None, z=None, y=None, ss=None, cs=None) == 0
+    assert _decode(lib, batch=0, G=3) == -2
