@@ -8,8 +8,10 @@ code with the HIP library (mamba_ssd_selective_amd) and never imports it.
                  recurrence, grouped gated RMSNorm, varlen batch driver.
   chunked     -- closed-form chunked evaluation (exponent checks, clamp) and
                  the materialised quadratic form, used to pin the recurrence.
+  inproj      -- the packed in-projection row (z | xBC | dt), the step size
+                 softplus(dt + bias), and mixed decode + prefill batches.
 
 Every function is pinned by a CPU test (tests/test_oracle_pins.py) against a
 closed form, an invariant, a library routine or a hand-derived fixture.
 """
-from . import recurrence, chunked  # noqa: F401
+from . import recurrence, chunked, inproj  # noqa: F401

@@ -252,3 +252,34 @@ def slice_group(inp: Dict[str, np.ndarray], shape: LayerShape, g: int):
     out["conv_state"] = inp["conv_state"][:, :, ch]
     out["ssm_state"] = inp["ssm_state"][:, heads]
     return out, LayerShape(len(heads), shape.headdim, shape.dstate, 1, shape.width)
+
+
+def inproj_inputs(shape: LayerShape, seqlens: List[int], seed: int, act: str = "bf16",
+                  init: str = "random", n_slots: Optional[int] = None,
+                  pad: int = 8) -> Dict[str, np.ndarray]:
+    """Inputs whose activations arrive as one in-projection row per token.
+
+    The row holds z (d_inner), xBC (conv_dim) and the raw step size (nheads), in
+    that order, then zero padding up to a multiple of ``pad`` channels (so bf16
+    rows stay 16-byte aligned).  dt_raw ~ N(0, 1) is rounded like the other
+    activations; dt_bias ~ U(-4, -2) per head (fp32).  Nothing here applies the
+    step-size function: the oracle and the library each do that themselves.
+    Returns the arrays of make_inputs without xbc, z and dt, plus
+    row [T, ld_row] (float32 values, bf16-representable for bf16) and dt_bias [H].
+    """
+    base = small_shape_inputs(shape, seqlens, seed, act=act, init=init, n_slots=n_slots)
+    T = base["xbc"].shape[0]
+    H = shape.nheads
+    width = shape.d_inner + shape.conv_dim + H
+    ld_row = (width + pad - 1) // pad * pad
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xD7]))
+    act_round = round_bf16 if act == "bf16" else (lambda a: a.astype(np.float32))
+    dt_raw = act_round(rng.standard_normal((T, H), dtype=np.float32))
+    dt_bias = rng.uniform(-4.0, -2.0, size=H).astype(np.float32)
+    row = np.zeros((T, ld_row), dtype=np.float32)
+    row[:, :shape.d_inner] = base["z"]
+    row[:, shape.d_inner:shape.d_inner + shape.conv_dim] = base["xbc"]
+    row[:, shape.d_inner + shape.conv_dim:width] = dt_raw
+    out = {k: v for k, v in base.items() if k not in ("xbc", "z", "dt")}
+    out.update(row=row, dt_bias=dt_bias)
+    return out
