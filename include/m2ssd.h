@@ -17,7 +17,10 @@
  *      GroupRMSNorm(y, ssm_norm.weight), then the SiLU(z) gate; the NemotronH
  *      decode page names the op RmsNormGatedGroup(n_groups));
  * and the single-token decode step of the same layer at cache slots
- * (mamba2_decode), which continues the states a prefill left.
+ * (mamba2_decode), which continues the states a prefill left; the same
+ * operations taking packed in-projection rows with the raw step size
+ * (mamba2_prefill_inproj, mamba2_decode_inproj), and batches mixing decode rows
+ * and prefill sequences (mamba2_mixed_inproj).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -279,6 +282,96 @@ int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                   const int32_t* state_idx, const uint8_t* has_init,
                   int nheads, int headdim, int dstate, int ngroups,
                   void* y, int64_t ld_y, int y_dtype, void* stream);
+
+/*
+ * Packed in-projection rows.  A Mamba-2 layer's in-projection emits one row per
+ * token holding, in this order, z (d_inner = nheads*headdim channels), xBC
+ * (conv_dim = d_inner + 2*ngroups*dstate channels: x | B | C) and the RAW step
+ * size (nheads channels) (page "NemotronH decodes on the single-step recurrent
+ * kernels", PR description: in_proj -> QkvSplit(z | xBC | dt), three outputs of
+ * widths (I, conv_dim, num_heads) from the head, the middle and the tail of an
+ * in_proj row).  The entries below read those rows in place and compute the
+ * step size themselves (page "Nemotron-H", section 4.1: softplus of dt plus
+ * the per-head ssm_dt.bias):
+ *   dt[t, h] = softplus(raw[t, h] + dt_bias[h]),  softplus(v) = log(1 + e^v).
+ *
+ *   zxbcdt   [rows, ld_row] of act_dtype; ld_row >= 2*d_inner + 2*ngroups*dstate
+ *            + nheads (padding after the raw step size is ignored).  Alignment:
+ *            zxbcdt 16-byte aligned, ld_row * element size and d_inner *
+ *            element size multiples of 16 bytes (as the views x, B, C, z need).
+ *   dt_bias  [nheads] fp32, or NULL (0).
+ * Everything else means what it means for mamba2_prefill / mamba2_decode.
+ */
+
+/*
+ * Bytes of device workspace mamba2_prefill_inproj needs (0 on bad arguments):
+ * mamba2_prefill_workspace_size() plus the fp32 step sizes [total_tokens, nheads]
+ * (256-byte rounded, at least one row).  Always nonzero for valid arguments.
+ */
+size_t mamba2_prefill_inproj_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
+                                            int nheads, int headdim, int dstate, int ngroups,
+                                            int chunk_size, int act_dtype);
+
+/*
+ * mamba2_prefill_inproj -- mamba2_prefill over a packed varlen batch given as
+ * in-projection rows: the same conv, scan, D skip and gated norm, with dt
+ * computed on the device from the rows' raw step sizes and dt_bias.
+ * workspace is required (mamba2_prefill_inproj_workspace_size() bytes).
+ */
+int mamba2_prefill_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,
+                          const float* A, const float* D, const float* conv_w, const float* conv_b,
+                          const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                          float* ssm_state, int n_slots, const int32_t* cu_seqlens, int batch,
+                          int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                          const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                          int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * mamba2_decode_inproj -- mamba2_decode with row b of zxbcdt as sequence b's
+ * new token; the step size softplus(raw + dt_bias) is formed inside the fused
+ * decode kernel.  No workspace.  batch == 0 is a no-op.
+ */
+int mamba2_decode_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,
+                         const float* A, const float* D, const float* conv_w, const float* conv_b,
+                         const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                         float* ssm_state, int n_slots, int batch, const int32_t* state_idx,
+                         const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                         void* y, int64_t ld_y, int y_dtype, void* stream);
+
+/*
+ * Bytes of device workspace mamba2_mixed_inproj needs (0 on bad arguments):
+ * mamba2_prefill_inproj_workspace_size() for the whole batch plus the prefill
+ * part's row offsets and slot map.
+ */
+size_t mamba2_mixed_inproj_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
+                                          int nheads, int headdim, int dstate, int ngroups,
+                                          int chunk_size, int act_dtype);
+
+/*
+ * mamba2_mixed_inproj -- one layer step over a batch that mixes decode rows and
+ * prefill sequences (page "NemotronH decodes on the single-step recurrent
+ * kernels", PR description: decode rows take the single-step conv and state
+ * updates at their cache slots, prefill rows keep the chunk scan, and the split
+ * is the metadata's num_decodes, never the token count -- a fresh one-token
+ * prompt is a prefill).  Sequences 0 .. num_decodes-1 are decode sequences of
+ * exactly one row each, rows 0 .. num_decodes-1 (cu_seqlens[b] == b for
+ * b <= num_decodes: a contract on device data, checked only with
+ * M2SSD_DEBUG=1); sequences num_decodes .. batch-1 are prefills.  The decode
+ * rows run the fused decode kernel, the prefill sequences the prefill chain,
+ * both on `stream`; the result equals mamba2_prefill_inproj over the whole
+ * batch up to rounding.  cu_seqlens, state_idx, has_init cover all `batch`
+ * sequences; state_idx NULL means slot b for sequence b (needs n_slots >= batch).
+ * 0 <= num_decodes <= batch; workspace is required.
+ */
+int mamba2_mixed_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,
+                        const float* A, const float* D, const float* conv_w, const float* conv_b,
+                        const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                        float* ssm_state, int n_slots, const int32_t* cu_seqlens, int batch,
+                        int num_decodes, int64_t total_tokens, int max_seqlen,
+                        const int32_t* state_idx, const uint8_t* has_init, int nheads, int headdim,
+                        int dstate, int ngroups, int chunk_size, void* y, int64_t ld_y, int y_dtype,
+                        void* workspace, size_t ws_bytes, void* stream);
 
 /* Launch counters (process-wide, atomic): which kernels ran, per instantiation. */
 typedef struct {

@@ -68,6 +68,16 @@ _SIGS = {
                             _P, _L, _I, _P, ctypes.c_size_t, _P]),
     "mamba2_decode": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
                            _F, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _L, _I, _P]),
+    "mamba2_prefill_inproj_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "mamba2_prefill_inproj": (_I, [_P, _L, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _P, _I,
+                                   _L, _I, _P, _P, _I, _I, _I, _I, _I, _P, _L, _I, _P,
+                                   ctypes.c_size_t, _P]),
+    "mamba2_decode_inproj": (_I, [_P, _L, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P,
+                                  _P, _I, _I, _I, _I, _P, _L, _I, _P]),
+    "mamba2_mixed_inproj_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "mamba2_mixed_inproj": (_I, [_P, _L, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _P, _I, _I,
+                                 _L, _I, _P, _P, _I, _I, _I, _I, _I, _P, _L, _I, _P,
+                                 ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -333,5 +343,120 @@ def mamba2_decode(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm_
         _ptr(conv_state), _ptr(ssm_state), conv_state.size(0), batch, _ptr(state_idx),
         _ptr(has_init), nheads, headdim, dstate, ngroups, _ptr(y), _rows(y, "y"),
         _dtype_code(y), _stream())
+    _check(st)
+    return y
+
+
+def _inproj_common(row, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state, nheads,
+                   headdim, dstate, ngroups):
+    width = 2 * nheads * headdim + 2 * ngroups * dstate + nheads
+    ld_row = _rows(row, "zxbcdt")
+    if row.size(1) < width:
+        raise ValueError(f"zxbcdt rows have {row.size(1)} channels, below z | xBC | dt = {width}")
+    for t, n in ((dt_bias, "dt_bias"), (A, "A"), (D, "D"), (conv_w, "conv_w"), (conv_b, "conv_b"),
+                 (norm_w, "norm_w"), (conv_state, "conv_state"), (ssm_state, "ssm_state")):
+        _vec(t, n, torch.float32)
+    if conv_state.size(0) != ssm_state.size(0):
+        raise ValueError("conv_state and ssm_state must have the same number of slots")
+    return ld_row
+
+
+def mamba2_prefill_inproj_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim, dstate,
+                                         ngroups, chunk_size=128, act_dtype=torch.bfloat16) -> int:
+    code = M2_BF16 if act_dtype == torch.bfloat16 else M2_F32
+    return int(load().mamba2_prefill_inproj_workspace_size(total_tokens, batch, max_seqlen, nheads,
+                                                           headdim, dstate, ngroups, chunk_size, code))
+
+
+def mamba2_prefill_inproj(zxbcdt, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                          cu_seqlens, max_seqlen, nheads, headdim, dstate, ngroups, chunk_size=128,
+                          state_idx=None, has_init=None, eps=1e-5, norm_before_gate=True, y=None,
+                          y_dtype=torch.float32, workspace=None):
+    """The mixer core over packed in-projection rows zxbcdt [T, >= 2*H*P + 2*G*N + H]
+    (z | x | B | C | raw dt); dt = softplus(raw + dt_bias) is formed on the device.
+    States advance in place.  Returns y [T, H*P]."""
+    lib = load()
+    T = zxbcdt.size(0)
+    batch = cu_seqlens.numel() - 1
+    ld_row = _inproj_common(zxbcdt, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                            nheads, headdim, dstate, ngroups)
+    _vec(cu_seqlens, "cu_seqlens", torch.int32)
+    _vec(state_idx, "state_idx", torch.int32)
+    _vec(has_init, "has_init", torch.uint8)
+    if y is None:
+        y = torch.empty((T, nheads * headdim), dtype=y_dtype, device=zxbcdt.device)
+    if workspace is None:
+        need = mamba2_prefill_inproj_workspace_size(T, batch, max_seqlen, nheads, headdim, dstate,
+                                                    ngroups, chunk_size, zxbcdt.dtype)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=zxbcdt.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mamba2_prefill_inproj(
+        _ptr(zxbcdt), ld_row, _dtype_code(zxbcdt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(conv_w),
+        _ptr(conv_b), _ptr(norm_w), float(eps), int(bool(norm_before_gate)), _ptr(conv_state),
+        _ptr(ssm_state), conv_state.size(0), _ptr(cu_seqlens), batch, T, int(max_seqlen),
+        _ptr(state_idx), _ptr(has_init), nheads, headdim, dstate, ngroups, chunk_size, _ptr(y),
+        _rows(y, "y"), _dtype_code(y), _ptr(workspace), ws_bytes, _stream())
+    _check(st)
+    return y
+
+
+def mamba2_decode_inproj(zxbcdt, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                         nheads, headdim, dstate, ngroups, state_idx=None, has_init=None, eps=1e-5,
+                         norm_before_gate=True, y=None, y_dtype=torch.float32):
+    """One decode token per sequence from packed in-projection rows (row b = sequence b),
+    with dt = softplus(raw + dt_bias) formed in the decode kernel.  Returns y [batch, H*P]."""
+    lib = load()
+    batch = zxbcdt.size(0)
+    ld_row = _inproj_common(zxbcdt, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                            nheads, headdim, dstate, ngroups)
+    _vec(state_idx, "state_idx", torch.int32)
+    _vec(has_init, "has_init", torch.uint8)
+    if y is None:
+        y = torch.empty((batch, nheads * headdim), dtype=y_dtype, device=zxbcdt.device)
+    st = lib.mamba2_decode_inproj(
+        _ptr(zxbcdt), ld_row, _dtype_code(zxbcdt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(conv_w),
+        _ptr(conv_b), _ptr(norm_w), float(eps), int(bool(norm_before_gate)), _ptr(conv_state),
+        _ptr(ssm_state), conv_state.size(0), batch, _ptr(state_idx), _ptr(has_init), nheads,
+        headdim, dstate, ngroups, _ptr(y), _rows(y, "y"), _dtype_code(y), _stream())
+    _check(st)
+    return y
+
+
+def mamba2_mixed_inproj_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim, dstate,
+                                       ngroups, chunk_size=128, act_dtype=torch.bfloat16) -> int:
+    code = M2_BF16 if act_dtype == torch.bfloat16 else M2_F32
+    return int(load().mamba2_mixed_inproj_workspace_size(total_tokens, batch, max_seqlen, nheads,
+                                                         headdim, dstate, ngroups, chunk_size, code))
+
+
+def mamba2_mixed_inproj(zxbcdt, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                        cu_seqlens, num_decodes, max_seqlen, nheads, headdim, dstate, ngroups,
+                        chunk_size=128, state_idx=None, has_init=None, eps=1e-5,
+                        norm_before_gate=True, y=None, y_dtype=torch.float32, workspace=None):
+    """A batch whose first num_decodes sequences are one decode row each (rows
+    0 .. num_decodes-1) and whose other sequences are prefills, from packed
+    in-projection rows.  Decode rows run the fused decode kernel, prefills the
+    chunked chain.  Returns y [T, H*P]."""
+    lib = load()
+    T = zxbcdt.size(0)
+    batch = cu_seqlens.numel() - 1
+    ld_row = _inproj_common(zxbcdt, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                            nheads, headdim, dstate, ngroups)
+    _vec(cu_seqlens, "cu_seqlens", torch.int32)
+    _vec(state_idx, "state_idx", torch.int32)
+    _vec(has_init, "has_init", torch.uint8)
+    if y is None:
+        y = torch.empty((T, nheads * headdim), dtype=y_dtype, device=zxbcdt.device)
+    if workspace is None:
+        need = mamba2_mixed_inproj_workspace_size(T, batch, max_seqlen, nheads, headdim, dstate,
+                                                  ngroups, chunk_size, zxbcdt.dtype)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=zxbcdt.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mamba2_mixed_inproj(
+        _ptr(zxbcdt), ld_row, _dtype_code(zxbcdt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(conv_w),
+        _ptr(conv_b), _ptr(norm_w), float(eps), int(bool(norm_before_gate)), _ptr(conv_state),
+        _ptr(ssm_state), conv_state.size(0), _ptr(cu_seqlens), batch, int(num_decodes), T,
+        int(max_seqlen), _ptr(state_idx), _ptr(has_init), nheads, headdim, dstate, ngroups,
+        chunk_size, _ptr(y), _rows(y, "y"), _dtype_code(y), _ptr(workspace), ws_bytes, _stream())
     _check(st)
     return y

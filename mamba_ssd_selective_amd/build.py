@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libm2ssd.so")
 ARCH = "gfx950"
 
 SOURCES = ["conv_rows.hip", "ssd_scan.hip", "ssd_chunked.hip", "gated_norm.hip", "decode_step.hip",
-           "m2ssd_api.cpp"]
+           "inproj.hip", "m2ssd_api.cpp"]
 
 # Packed fp32 instructions are disabled for all device code (see the design notes).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

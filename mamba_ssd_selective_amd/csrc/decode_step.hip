@@ -29,10 +29,13 @@
 // (8 -> 4 -> 2 -> 1) while it sums pairs of lanes, then plain butterflies
 // finish; 9 exchanges per 8 rows instead of 40, in a fixed order, so results
 // are bitwise repeatable.  Every per-channel load of the conv, gate and
-// weights is issued before any of them is used.
+// weights is issued before any of them is used.  The step size comes either as
+// fp32 dt or, for rows taken straight from the in-projection, as the raw value
+// in the activation type, turned into softplus(raw + bias[h]) where it is read.
 
 #include "device_common.h"
 #include "kernels.h"
+#include "step_size.h"
 
 namespace m2 {
 namespace {
@@ -103,7 +106,15 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
     float* sdA = sbc + 2 * N;     // e(dt A) per head  [hpg]
     float* red = sdA + hpg;       // [NT / 64]
 
-    const float* dtr = a.dt + (int64_t)b * a.ld_dt + (int64_t)g * hpg;
+    // Step size of head g*hpg + j: given in fp32, or softplus(raw + bias) of the
+    // raw value in the activation type (the in-projection row's tail).
+    const int64_t dto = (int64_t)b * a.ld_dt + (int64_t)g * hpg;
+    auto step = [&](int j) -> float {
+        if (a.dt_softplus)
+            return softplus(Act<Tin>::load(static_cast<const Tin*>(a.dt) + dto + j) +
+                            (a.dt_bias ? a.dt_bias[g * hpg + j] : 0.f));
+        return static_cast<const float*>(a.dt)[dto + j];
+    };
     const float* Ag = a.A + (int64_t)g * hpg;
     const bool has_b = a.conv_b != nullptr, has_d = a.D != nullptr;
     const float* Dg = has_d ? a.D + (int64_t)g * hpg : Ag;
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
             w[u] = *reinterpret_cast<const f32x4_t*>(a.conv_w + cg * 4);
             cb[u] = (has_b ? a.conv_b : a.conv_w)[cg];
             const int kx = min(k, gw - 1);
-            dtv[u] = dtr[kx / P];
+            dtv[u] = step(kx / P);
             dv[u] = Dg[kx / P];
             zv[u] = Act<Tin>::load(zr + kx);
             wv[u] = nw[kx];
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
             }
         }
     }
-    for (int j = tid; j < hpg; j += NT) sdA[j] = expf(fminf(dtr[j] * Ag[j], 0.f));
+    for (int j = tid; j < hpg; j += NT) sdA[j] = expf(fminf(step(j) * Ag[j], 0.f));
     __syncthreads();
 
     // 2. State update and readout over the group's state, a contiguous run of

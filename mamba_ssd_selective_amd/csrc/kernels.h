@@ -77,13 +77,17 @@ struct NormArgs {
 
 struct DecodeArgs {
     // One row per sequence: x [batch, nheads*headdim], B and C [batch, ngroups*dstate],
-    // z [batch, nheads*headdim] (act_dtype), dt [batch, nheads] fp32.
+    // z [batch, nheads*headdim] (act_dtype), dt [batch, nheads]: fp32 step sizes,
+    // or with dt_softplus set raw values of act_dtype that give
+    // dt = softplus(raw + dt_bias[h]) (dt_bias null = 0).
     const void* x; int64_t ld_x;
     const void* B; int64_t ld_B;
     const void* C; int64_t ld_C;
     const void* z; int64_t ld_z;
     int act_dtype;
-    const float* dt; int64_t ld_dt;
+    const void* dt; int64_t ld_dt;
+    int dt_softplus;
+    const float* dt_bias;
     const float* A;
     const float* D;             // or null
     const float* conv_w;        // [conv_dim, 4]
@@ -110,6 +114,15 @@ hipError_t launch_gated_norm(const NormArgs& a, hipStream_t stream);
 // per (sequence, group).
 bool decode_supported(int nheads, int ngroups, int headdim, int dstate);
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
+
+// Packed in-projection rows (inproj.hip): dt [T, nheads] fp32 = softplus(raw +
+// bias[h]) from the raw column run of each row (bias null = 0); and the row
+// offsets (and, with slot_out, the identity slot map) of sequences first ..
+// first+count of a batch whose first `first` sequences are one row each.
+hipError_t launch_step_size(const void* raw, int64_t ld_raw, int act_dtype, const float* bias,
+                            int nheads, int64_t total_tokens, float* dt, hipStream_t stream);
+hipError_t launch_rebase(const int32_t* cu, int first, int count, int32_t rows, int32_t* out,
+                         int32_t* slot_out, hipStream_t stream);
 
 // True when a scan kernel is compiled for this (headdim, dstate).
 bool scan_supported(int headdim, int dstate);

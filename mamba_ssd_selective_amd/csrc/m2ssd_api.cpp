@@ -19,6 +19,10 @@
 namespace {
 
 thread_local std::string g_last_error;
+// Set while a mixed batch runs its parts: the whole batch's index arrays were
+// debug-checked already, and the prefill part's row offsets are computed on
+// the device by then, so the parts skip the per-call debug reads.
+thread_local bool g_parts_of_checked_batch = false;
 
 struct Counters {
     std::atomic<uint64_t> conv{0}, conv_state{0}, scan_f64{0}, scan_bf16x3{0}, norm{0}, prefill{0},
@@ -60,6 +64,7 @@ bool valid_dtype(int d) { return d == M2_F32 || d == M2_BF16; }
 
 // Debug checks of device-side index arrays, enabled per call by M2SSD_DEBUG=1.
 bool debug_enabled() {
+    if (g_parts_of_checked_batch) return false;
     const char* e = std::getenv("M2SSD_DEBUG");
     return e && e[0] == '1';
 }
@@ -361,15 +366,22 @@ size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_se
            scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
-int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
-                   int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
-                   int64_t ld_dt, const float* A, const float* D, const float* conv_w,
-                   const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
-                   float* conv_state, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
-                   int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
-                   const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
-                   int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
-                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The prefill chain.  Every argument check runs first; with launch == false the
+// call stops there (a dry run used by the entries that launch a step of their
+// own before the chain), so a failing check never leaves side effects.
+int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
+                int64_t ld_dt, const float* A, const float* D, const float* conv_w,
+                const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
+                float* conv_state, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
+                int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
+                size_t ws_bytes, void* stream, bool launch) {
     int st = validate_scan_dims(nheads, headdim, dstate, ngroups, chunk_size);
     if (st) return st;
     const int d_x = nheads * headdim, d_b = ngroups * dstate;
@@ -407,6 +419,7 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
         return st;
     if (y_dtype == M2_F32 && (ld_y * 4) % 16) return fail(M2_ERR_ALIGN, "prefill: ld_y must be a multiple of 16 bytes");
     if (!aligned16(y)) return fail(M2_ERR_ALIGN, "prefill: y must be 16-byte aligned");
+    if (!launch) return M2_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t* tev = g_timing.next();
@@ -477,13 +490,16 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     return ok();
 }
 
-int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
-                  int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
-                  int64_t ld_dt, const float* A, const float* D, const float* conv_w,
-                  const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
-                  float* conv_state, float* ssm_state, int n_slots, int batch,
-                  const int32_t* state_idx, const uint8_t* has_init, int nheads, int headdim,
-                  int dstate, int ngroups, void* y, int64_t ld_y, int y_dtype, void* stream) {
+// The fused decode step; dt is fp32 step sizes, or (dt_softplus) raw values of
+// act_dtype with dt_bias.  launch == false: checks only, as for prefill_run.
+int decode_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+               int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const void* dt,
+               int64_t ld_dt, int dt_softplus, const float* dt_bias, const float* A,
+               const float* D, const float* conv_w, const float* conv_b, const float* norm_w,
+               float eps, int norm_before_gate, float* conv_state, float* ssm_state, int n_slots,
+               int batch, const int32_t* state_idx, const uint8_t* has_init, int nheads,
+               int headdim, int dstate, int ngroups, void* y, int64_t ld_y, int y_dtype,
+               void* stream, bool launch) {
     if (!valid_dtype(act_dtype) || !valid_dtype(y_dtype))
         return fail(M2_ERR_DTYPE, "decode: act_dtype and y_dtype must be M2_F32 or M2_BF16");
     if (batch < 0 || n_slots <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
@@ -496,7 +512,7 @@ int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
     const int64_t di = (int64_t)nheads * headdim, gn = (int64_t)ngroups * dstate;
     if (ld_x < di || ld_B < gn || ld_C < gn || ld_z < di || ld_dt < nheads || ld_y < di)
         return fail(M2_ERR_STRIDE, "decode: a row stride is smaller than its row width");
-    if (batch == 0) return ok();
+    if (batch == 0) return M2_OK;
     if (!x || !B || !C || !z || !dt || !A || !conv_w || !norm_w || !conv_state || !ssm_state || !y)
         return fail(M2_ERR_NULL, "decode: x, B, C, z, dt, A, conv_w, norm_w, both states and y are required");
     if (!aligned16(conv_w) || !aligned16(ssm_state))
@@ -513,9 +529,11 @@ int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
                 return fail(M2_ERR_SHAPE, "debug: state_idx[%d]=%d repeats a slot", b, hidx[b]);
         }
     }
+    if (!launch) return M2_OK;
     m2::DecodeArgs a{};
     a.x = x; a.ld_x = ld_x; a.B = B; a.ld_B = ld_B; a.C = C; a.ld_C = ld_C; a.z = z; a.ld_z = ld_z;
-    a.act_dtype = act_dtype; a.dt = dt; a.ld_dt = ld_dt; a.A = A; a.D = D;
+    a.act_dtype = act_dtype; a.dt = dt; a.ld_dt = ld_dt; a.dt_softplus = dt_softplus;
+    a.dt_bias = dt_bias; a.A = A; a.D = D;
     a.conv_w = conv_w; a.conv_b = conv_b; a.norm_w = norm_w; a.eps = eps;
     a.norm_before_gate = norm_before_gate; a.conv_state = conv_state; a.ssm_state = ssm_state;
     a.batch = batch; a.state_idx = state_idx; a.has_init = has_init;
@@ -524,6 +542,247 @@ int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
     int st;
     if ((st = hip_status(m2::launch_decode_step(a, static_cast<hipStream_t>(stream)), "decode launch"))) return st;
     g_counters.decode++;
+    return M2_OK;
+}
+
+// Views of one packed in-projection row: z | x | B | C | raw dt, in that order.
+struct RowViews {
+    const char *z, *x, *B, *C, *dt;
+};
+RowViews row_views(const void* row, int es, int nheads, int headdim, int dstate, int ngroups) {
+    const int64_t di = (int64_t)nheads * headdim, gn = (int64_t)ngroups * dstate;
+    const char* r = static_cast<const char*>(row);
+    return RowViews{r, r + di * es, r + 2 * di * es, r + (2 * di + gn) * es, r + (2 * di + 2 * gn) * es};
+}
+
+int64_t row_width(int nheads, int headdim, int dstate, int ngroups) {
+    return 2 * (int64_t)nheads * headdim + 2 * (int64_t)ngroups * dstate + nheads;
+}
+
+size_t step_size_bytes(int64_t total_tokens, int nheads) {
+    return (size_t)round256((total_tokens > 0 ? total_tokens : 1) * (int64_t)nheads * 4);
+}
+
+// Prefill from packed rows: the step-size kernel writes fp32 dt after the
+// prefill's own workspace, then the chain runs with it.
+int prefill_inproj_run(const void* row, int64_t ld_row, int act_dtype, const float* dt_bias,
+                       const float* A, const float* D, const float* conv_w, const float* conv_b,
+                       const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                       float* ssm_state, int n_slots, const int32_t* cu_seqlens, int batch,
+                       int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                       const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                       int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
+                       size_t ws_bytes, void* stream, bool launch) {
+    if (!row) return fail(M2_ERR_NULL, "prefill_inproj: the in-projection rows are required");
+    if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "prefill_inproj: act_dtype must be M2_F32 or M2_BF16");
+    if (nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return fail(M2_ERR_SHAPE, "prefill_inproj: nheads, headdim, dstate, ngroups must be positive");
+    if (ld_row < row_width(nheads, headdim, dstate, ngroups))
+        return fail(M2_ERR_STRIDE, "prefill_inproj: ld_row %lld is below the row width %lld",
+                    (long long)ld_row, (long long)row_width(nheads, headdim, dstate, ngroups));
+    const size_t pws = mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim,
+                                                     dstate, ngroups, chunk_size, act_dtype);
+    const size_t need = pws + step_size_bytes(total_tokens, nheads);
+    if (!workspace || ws_bytes < need)
+        return fail(M2_ERR_WORKSPACE, "prefill_inproj: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (!aligned16(workspace)) return fail(M2_ERR_ALIGN, "prefill_inproj: workspace must be 16-byte aligned");
+    float* dt = reinterpret_cast<float*>(static_cast<char*>(workspace) + pws);
+    const RowViews v = row_views(row, elem_size(act_dtype), nheads, headdim, dstate, ngroups);
+    auto chain = [&](bool go) {
+        return prefill_run(v.x, ld_row, v.B, ld_row, v.C, ld_row, v.z, ld_row, act_dtype, dt, nheads,
+                           A, D, conv_w, conv_b, norm_w, eps, norm_before_gate, conv_state,
+                           ssm_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
+                           state_idx, has_init, nheads, headdim, dstate, ngroups, chunk_size, y,
+                           ld_y, y_dtype, workspace, pws, stream, go);
+    };
+    int st = chain(false);
+    if (st || !launch) return st;
+    if ((st = hip_status(m2::launch_step_size(v.dt, ld_row, act_dtype, dt_bias, nheads, total_tokens, dt,
+                                              static_cast<hipStream_t>(stream)),
+                         "step size launch")))
+        return st;
+    return chain(true);
+}
+
+int decode_inproj_run(const void* row, int64_t ld_row, int act_dtype, const float* dt_bias,
+                      const float* A, const float* D, const float* conv_w, const float* conv_b,
+                      const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                      float* ssm_state, int n_slots, int batch, const int32_t* state_idx,
+                      const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                      void* y, int64_t ld_y, int y_dtype, void* stream, bool launch) {
+    if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "decode_inproj: act_dtype must be M2_F32 or M2_BF16");
+    if (nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return fail(M2_ERR_SHAPE, "decode_inproj: nheads, headdim, dstate, ngroups must be positive");
+    if (ld_row < row_width(nheads, headdim, dstate, ngroups))
+        return fail(M2_ERR_STRIDE, "decode_inproj: ld_row %lld is below the row width %lld",
+                    (long long)ld_row, (long long)row_width(nheads, headdim, dstate, ngroups));
+    if (batch > 0 && !row) return fail(M2_ERR_NULL, "decode_inproj: the in-projection rows are required");
+    const RowViews v = row ? row_views(row, elem_size(act_dtype), nheads, headdim, dstate, ngroups)
+                           : RowViews{nullptr, nullptr, nullptr, nullptr, nullptr};
+    return decode_run(v.x, ld_row, v.B, ld_row, v.C, ld_row, v.z, ld_row, act_dtype, v.dt, ld_row, 1,
+                      dt_bias, A, D, conv_w, conv_b, norm_w, eps, norm_before_gate, conv_state,
+                      ssm_state, n_slots, batch, state_idx, has_init, nheads, headdim, dstate,
+                      ngroups, y, ld_y, y_dtype, stream, launch);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                   int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
+                   int64_t ld_dt, const float* A, const float* D, const float* conv_w,
+                   const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
+                   float* conv_state, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
+                   int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                   const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                   int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
+                   size_t ws_bytes, void* stream) {
+    const int st = prefill_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, A, D, conv_w,
+                               conv_b, norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots,
+                               cu_seqlens, batch, total_tokens, max_seqlen, state_idx, has_init,
+                               nheads, headdim, dstate, ngroups, chunk_size, y, ld_y, y_dtype,
+                               workspace, ws_bytes, stream, true);
+    return st ? st : ok();
+}
+
+int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                  int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
+                  int64_t ld_dt, const float* A, const float* D, const float* conv_w,
+                  const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
+                  float* conv_state, float* ssm_state, int n_slots, int batch,
+                  const int32_t* state_idx, const uint8_t* has_init, int nheads, int headdim,
+                  int dstate, int ngroups, void* y, int64_t ld_y, int y_dtype, void* stream) {
+    const int st = decode_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, 0, nullptr, A,
+                              D, conv_w, conv_b, norm_w, eps, norm_before_gate, conv_state,
+                              ssm_state, n_slots, batch, state_idx, has_init, nheads, headdim,
+                              dstate, ngroups, y, ld_y, y_dtype, stream, true);
+    return st ? st : ok();
+}
+
+size_t mamba2_prefill_inproj_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
+                                            int nheads, int headdim, int dstate, int ngroups,
+                                            int chunk_size, int act_dtype) {
+    const size_t pws = mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim,
+                                                     dstate, ngroups, chunk_size, act_dtype);
+    if (pws == 0 && (total_tokens < 0 || batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
+                     ngroups <= 0 || !valid_dtype(act_dtype)))
+        return 0;
+    return pws + step_size_bytes(total_tokens, nheads);
+}
+
+int mamba2_prefill_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,
+                          const float* A, const float* D, const float* conv_w, const float* conv_b,
+                          const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                          float* ssm_state, int n_slots, const int32_t* cu_seqlens, int batch,
+                          int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                          const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                          int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
+                          size_t ws_bytes, void* stream) {
+    const int st = prefill_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b,
+                                      norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots,
+                                      cu_seqlens, batch, total_tokens, max_seqlen, state_idx,
+                                      has_init, nheads, headdim, dstate, ngroups, chunk_size, y,
+                                      ld_y, y_dtype, workspace, ws_bytes, stream, true);
+    return st ? st : ok();
+}
+
+int mamba2_decode_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,
+                         const float* A, const float* D, const float* conv_w, const float* conv_b,
+                         const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                         float* ssm_state, int n_slots, int batch, const int32_t* state_idx,
+                         const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                         void* y, int64_t ld_y, int y_dtype, void* stream) {
+    const int st = decode_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w,
+                                     eps, norm_before_gate, conv_state, ssm_state, n_slots, batch,
+                                     state_idx, has_init, nheads, headdim, dstate, ngroups, y, ld_y,
+                                     y_dtype, stream, true);
+    return st ? st : ok();
+}
+
+size_t mamba2_mixed_inproj_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
+                                          int nheads, int headdim, int dstate, int ngroups,
+                                          int chunk_size, int act_dtype) {
+    const size_t pws = mamba2_prefill_inproj_workspace_size(total_tokens, batch, max_seqlen, nheads,
+                                                            headdim, dstate, ngroups, chunk_size,
+                                                            act_dtype);
+    if (pws == 0) return 0;
+    return (size_t)(round256((int64_t)(batch + 1) * 4) + round256((int64_t)batch * 4)) + pws;
+}
+
+int mamba2_mixed_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,
+                        const float* A, const float* D, const float* conv_w, const float* conv_b,
+                        const float* norm_w, float eps, int norm_before_gate, float* conv_state,
+                        float* ssm_state, int n_slots, const int32_t* cu_seqlens, int batch,
+                        int num_decodes, int64_t total_tokens, int max_seqlen,
+                        const int32_t* state_idx, const uint8_t* has_init, int nheads, int headdim,
+                        int dstate, int ngroups, int chunk_size, void* y, int64_t ld_y, int y_dtype,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    if (batch <= 0) return fail(M2_ERR_SHAPE, "mixed: batch must be positive (got %d)", batch);
+    if (num_decodes < 0 || num_decodes > batch)
+        return fail(M2_ERR_SHAPE, "mixed: num_decodes %d outside [0, batch=%d]", num_decodes, batch);
+    if (total_tokens < num_decodes)
+        return fail(M2_ERR_SHAPE, "mixed: total_tokens %lld is below num_decodes %d", (long long)total_tokens,
+                    num_decodes);
+    if (!cu_seqlens) return fail(M2_ERR_NULL, "mixed: cu_seqlens is required");
+    if (!state_idx && n_slots < batch) return fail(M2_ERR_SHAPE, "mixed: state_idx NULL needs n_slots >= batch");
+    if (!valid_dtype(act_dtype) || !valid_dtype(y_dtype))
+        return fail(M2_ERR_DTYPE, "mixed: act_dtype and y_dtype must be M2_F32 or M2_BF16");
+    const size_t need = mamba2_mixed_inproj_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim,
+                                                           dstate, ngroups, chunk_size, act_dtype);
+    if (need == 0) return fail(M2_ERR_SHAPE, "mixed: nheads, headdim, dstate, ngroups must be positive");
+    if (!workspace || ws_bytes < need)
+        return fail(M2_ERR_WORKSPACE, "mixed: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (!aligned16(workspace)) return fail(M2_ERR_ALIGN, "mixed: workspace must be 16-byte aligned");
+    if (debug_enabled()) {
+        int st = debug_check_indices(cu_seqlens, batch, total_tokens, max_seqlen, state_idx, n_slots);
+        if (st) return st;
+        std::vector<int32_t> hcu(num_decodes + 1);
+        if (hipMemcpy(hcu.data(), cu_seqlens, sizeof(int32_t) * (num_decodes + 1), hipMemcpyDeviceToHost) != hipSuccess)
+            return fail(M2_ERR_HIP, "debug: reading cu_seqlens failed");
+        for (int b = 0; b <= num_decodes; ++b)
+            if (hcu[b] != b) return fail(M2_ERR_SHAPE, "debug: decode sequence %d is not one row at row %d", b, b);
+    }
+    const int np = batch - num_decodes;
+    const int64_t tp = total_tokens - num_decodes;
+    const int es = elem_size(act_dtype);
+    char* wsb = static_cast<char*>(workspace);
+    int32_t* cu_p = reinterpret_cast<int32_t*>(wsb);
+    int32_t* slot_p = reinterpret_cast<int32_t*>(wsb + round256((int64_t)(batch + 1) * 4));
+    char* pws = wsb + round256((int64_t)(batch + 1) * 4) + round256((int64_t)batch * 4);
+    const size_t pws_bytes = ws_bytes - (size_t)(pws - wsb);
+    const char* row_p = zxbcdt ? static_cast<const char*>(zxbcdt) + (int64_t)num_decodes * ld_row * es : nullptr;
+    char* y_p = y ? static_cast<char*>(y) + (int64_t)num_decodes * ld_y * elem_size(y_dtype) : nullptr;
+    const int32_t* idx_p = state_idx ? state_idx + num_decodes : slot_p;
+    const uint8_t* init_p = has_init ? has_init + num_decodes : nullptr;
+    struct Scope {  // the parts skip per-call debug reads (checked above)
+        Scope() { g_parts_of_checked_batch = true; }
+        ~Scope() { g_parts_of_checked_batch = false; }
+    } scope;
+    auto decode_part = [&](bool go) {
+        return decode_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w, eps,
+                                 norm_before_gate, conv_state, ssm_state, n_slots, num_decodes,
+                                 state_idx, has_init, nheads, headdim, dstate, ngroups, y, ld_y,
+                                 y_dtype, stream, go);
+    };
+    auto prefill_part = [&](bool go) {
+        return prefill_inproj_run(row_p, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w, eps,
+                                  norm_before_gate, conv_state, ssm_state, n_slots, cu_p, np, tp,
+                                  max_seqlen, idx_p, init_p, nheads, headdim, dstate, ngroups,
+                                  chunk_size, y_p, ld_y, y_dtype, pws, pws_bytes, stream, go);
+    };
+    int st;
+    if (num_decodes > 0 && (st = decode_part(false))) return st;
+    if (np > 0 && (st = prefill_part(false))) return st;
+    if (num_decodes > 0 && (st = decode_part(true))) return st;
+    if (np > 0) {
+        if ((st = hip_status(m2::launch_rebase(cu_seqlens, num_decodes, np, (int32_t)tp, cu_p,
+                                               state_idx ? nullptr : slot_p,
+                                               static_cast<hipStream_t>(stream)),
+                             "mixed rebase launch")))
+            return st;
+        if ((st = prefill_part(true))) return st;
+    }
     return ok();
 }
 

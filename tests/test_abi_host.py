@@ -24,7 +24,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mamba2_conv_rows", "ssd_chunk_scan", "ssd_chunk_scan_workspace_size",
               "gated_rmsnorm_group", "mamba2_prefill", "mamba2_prefill_workspace_size",
-              "mamba2_decode", "m2_last_error", "m2_get_counters"):
+              "mamba2_decode", "mamba2_prefill_inproj", "mamba2_prefill_inproj_workspace_size",
+              "mamba2_decode_inproj", "mamba2_mixed_inproj", "mamba2_mixed_inproj_workspace_size",
+              "m2_last_error", "m2_get_counters"):
         assert n in names
 
 
@@ -143,3 +145,99 @@ def test_decode_empty_batch_is_a_no_op():
     lib = m2.load()
     assert _decode(lib, batch=0, x=None, B=None, C=None, z=None, y=None, ss=None, cs=None) == 0
     assert _decode(lib, batch=0, G=3) == -2
+
+
+# ---- packed in-projection rows and mixed batches (fake, never dereferenced pointers)
+
+_TINY_ROW = 2 * 64 + 2 * 2 * 16 + 4  # z | x | B | C | dt of H=4, P=16, N=16, G=2
+
+
+def test_inproj_workspace_queries():
+    lib = m2.load()
+    T, b = 1000, 3
+    pre = lib.mamba2_prefill_workspace_size(T, b, T, 64, 64, 128, 8, 128, 1)
+    n = lib.mamba2_prefill_inproj_workspace_size(T, b, T, 64, 64, 128, 8, 128, 1)
+    assert n == pre + (T * 64 * 4 + 255) // 256 * 256
+    # always nonzero for valid arguments (the step sizes need room even when the chain does not)
+    assert lib.mamba2_prefill_inproj_workspace_size(0, 1, 0, 4, 16, 16, 2, 16, 0) >= 256
+    assert lib.mamba2_prefill_inproj_workspace_size(10, 1, 10, 4, 16, 16, 2, 16, 7) == 0
+    mixed = lib.mamba2_mixed_inproj_workspace_size(T, b, T, 64, 64, 128, 8, 128, 1)
+    assert mixed == n + 256 + 256
+    assert lib.mamba2_mixed_inproj_workspace_size(T, 0, T, 64, 64, 128, 8, 128, 1) == 0
+
+
+def _prefill_inproj(lib, **kw):
+    a = dict(row=4096, ld=_TINY_ROW, act=0, bias=None, A=96, D=None, cw=112, cb=None, nw=128,
+             cs=144, ss=160, n_slots=2, cu=176, batch=2, T=10, maxlen=10, idx=None, init=None,
+             H=4, P=16, N=16, G=2, chunk=16, y=8192, ld_y=64, ydt=0, ws=16384, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.mamba2_prefill_inproj(a["row"], a["ld"], a["act"], a["bias"], a["A"], a["D"], a["cw"],
+                                     a["cb"], a["nw"], 1e-5, 1, a["cs"], a["ss"], a["n_slots"], a["cu"],
+                                     a["batch"], a["T"], a["maxlen"], a["idx"], a["init"], a["H"],
+                                     a["P"], a["N"], a["G"], a["chunk"], a["y"], a["ld_y"], a["ydt"],
+                                     a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(row=None), -1), (dict(A=None), -1), (dict(y=None), -1), (dict(cu=None), -1),
+    (dict(act=3), -3), (dict(ydt=9), -3),
+    (dict(ld=_TINY_ROW - 1), -5), (dict(ld_y=32), -5),
+    (dict(ws=None), -8), (dict(ws_bytes=100), -8), (dict(ws=16388), -6),
+    (dict(row=4100), -6), (dict(ld=_TINY_ROW + 1), -6),
+    (dict(chunk=24), -4), (dict(P=24, ld=264, ld_y=96), -7), (dict(G=3, ld=228), -2), (dict(batch=0), -2),
+])
+def test_prefill_inproj_rejects_bad_arguments(kw, code):
+    lib = m2.load()
+    assert _prefill_inproj(lib, **kw) == code
+    assert lib.m2_last_error().decode() != ""
+
+
+def _decode_inproj(lib, **kw):
+    a = dict(row=4096, ld=_TINY_ROW, act=0, bias=None, A=96, D=None, cw=112, cb=None, nw=128,
+             cs=144, ss=160, n_slots=2, batch=2, idx=None, init=None, H=4, P=16, N=16, G=2,
+             y=8192, ld_y=64, ydt=0)
+    a.update(kw)
+    return lib.mamba2_decode_inproj(a["row"], a["ld"], a["act"], a["bias"], a["A"], a["D"], a["cw"],
+                                    a["cb"], a["nw"], 1e-5, 1, a["cs"], a["ss"], a["n_slots"],
+                                    a["batch"], a["idx"], a["init"], a["H"], a["P"], a["N"], a["G"],
+                                    a["y"], a["ld_y"], a["ydt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(row=None), -1), (dict(ss=None), -1), (dict(act=2), -3), (dict(ld=_TINY_ROW - 1), -5),
+    (dict(n_slots=1), -2), (dict(G=3, ld=228), -2), (dict(P=24, ld=264, ld_y=96), -7), (dict(ss=168), -6),
+])
+def test_decode_inproj_rejects_bad_arguments(kw, code):
+    lib = m2.load()
+    assert _decode_inproj(lib, **kw) == code
+
+
+def test_decode_inproj_empty_batch_is_a_no_op():
+    lib = m2.load()
+    assert _decode_inproj(lib, batch=0, row=None, y=None, ss=None, cs=None) == 0
+
+
+def _mixed(lib, **kw):
+    a = dict(row=4096, ld=_TINY_ROW, act=0, bias=None, A=96, D=None, cw=112, cb=None, nw=128,
+             cs=144, ss=160, n_slots=4, cu=176, batch=4, nd=2, T=12, maxlen=10, idx=None, init=None,
+             H=4, P=16, N=16, G=2, chunk=16, y=8192, ld_y=64, ydt=0, ws=16384, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.mamba2_mixed_inproj(a["row"], a["ld"], a["act"], a["bias"], a["A"], a["D"], a["cw"],
+                                   a["cb"], a["nw"], 1e-5, 1, a["cs"], a["ss"], a["n_slots"], a["cu"],
+                                   a["batch"], a["nd"], a["T"], a["maxlen"], a["idx"], a["init"],
+                                   a["H"], a["P"], a["N"], a["G"], a["chunk"], a["y"], a["ld_y"],
+                                   a["ydt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nd=-1), -2), (dict(nd=5), -2), (dict(batch=0), -2), (dict(T=1), -2),
+    (dict(cu=None), -1), (dict(row=None), -1), (dict(n_slots=3), -2),
+    (dict(ws=None), -8), (dict(ws_bytes=1000), -8), (dict(ws=16392), -6),
+    (dict(act=4), -3), (dict(ld=_TINY_ROW - 2), -5), (dict(chunk=200), -4),
+    # a bad prefill-part argument is found before the decode part launches
+    (dict(P=24, ld=264, ld_y=96), -7), (dict(nd=4, T=4, P=24, ld=264, ld_y=96), -7),
+])
+def test_mixed_inproj_rejects_bad_arguments(kw, code):
+    lib = m2.load()
+    assert _mixed(lib, **kw) == code
+    assert lib.m2_last_error().decode() != ""
