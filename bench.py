@@ -15,6 +15,16 @@ Prints one JSON line on stdout (progress goes to stderr):
                launch stream during the timed steps), against 8 TB/s HBM
   cpu_baseline the fp64 oracle on a bounded sample of the same input, on the
                host cores, in a process pool over (sequence, group) slices
+
+--mode selects another step of the same layer (default: prefill, the line above):
+  prefill_inproj  the same prefill taking packed in-projection rows
+                  (z | x | B | C | raw dt) with dt = softplus(raw + bias) on the
+                  device (mamba2_prefill_inproj)
+  decode          one decode token for each of 256 sequences at cache slots of a
+                  256-slot fp32 state pool, from packed rows (mamba2_decode_inproj:
+                  the fused decode kernel, step size formed in it)
+  mixed           a serving step: 256 decode rows then 2 prefill sequences of
+                  4096 tokens, from packed rows (mamba2_mixed_inproj)
 """
 import argparse
 import json
@@ -105,20 +115,25 @@ def kernel_bytes(w, T, nseq):
     }
 
 
-def kernel_sources_sha1():
-    """sha1 over the kernel sources (name + bytes, sorted): ties a traffic record to a build."""
-    import glob
+# The device sources each measured kernel set is built from: a traffic record holds
+# their sha1 and counts only while the sources are unchanged.
+CHAIN_SOURCES = ("conv_rows.hip", "ssd_chunked.hip", "ssd_scan.hip", "gated_norm.hip",
+                 "device_common.h")
+DECODE_SOURCES = ("decode_step.hip", "step_size.h", "device_common.h")
+
+
+def kernel_sources_sha1(files=CHAIN_SOURCES):
+    """sha1 over the named kernel sources (name + bytes, sorted): ties a traffic record to a build."""
     import hashlib
     h = hashlib.sha1()
-    for f in sorted(glob.glob(os.path.join(ROOT, "mamba_ssd_selective_amd", "csrc", "*"))):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(os.path.basename(f).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+    for name in sorted(files):
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "mamba_ssd_selective_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, kernel, files=CHAIN_SOURCES):
     """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE / WRITE_SIZE record in
     profiles/, scaled by the copy calibration stored with it; None when no record matches
     the workload and the current kernel sources."""
@@ -130,7 +145,7 @@ def measured_traffic(workload, kernel):
                     continue
                 rec = json.loads(line.split(":", 1)[1])
                 k = rec["kernels"].get(kernel)
-                if rec["workload"] == workload and k and rec["sources_sha1"] == kernel_sources_sha1():
+                if rec["workload"] == workload and k and rec["sources_sha1"] == kernel_sources_sha1(files):
                     return int((k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024)
     return None
 
@@ -158,15 +173,26 @@ def main():
     # the GPU takes ~20 steps (~25 ms of this load) to reach its steady clocks
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("prefill", "prefill_inproj", "decode", "mixed"),
+                    default="prefill")
+    ap.add_argument("--print-sources-sha1", action="store_true",
+                    help="print the sha1 of the prefill-chain and decode kernel sources and exit")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
+    if args.print_sources_sha1:
+        print(json.dumps({"chain": kernel_sources_sha1(CHAIN_SOURCES),
+                          "decode": kernel_sources_sha1(DECODE_SOURCES)}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode != "prefill":
+        return run_other_mode(args)
 
     import numpy as np
     from workloads import WORKLOADS, make_inputs
@@ -266,6 +292,190 @@ def main():
                       "ngroups": s.ngroups, "conv_width": s.width, "chunk": w.chunk_size,
                       "activations": w.act, "output": "f32", "parallelism": "single-gpu"},
            "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------- other steps of the layer
+
+DECODE_BATCH = 256        # decode rows per step (one per sequence), at the nano shape
+MIXED_PREFILL = (4096, 4096)
+
+
+def decode_bytes(s, batch, act, dt_bytes=4):
+    """Algorithmic bytes of one decode launch: per sequence the SSM state and conv
+    state read and written (fp32), the new x|B|C and z row, the step size, y (fp32);
+    per launch the conv and norm weights and A, D."""
+    per_seq = (2 * s.nheads * s.headdim * s.dstate * 4 + 2 * 3 * s.conv_dim * 4 +
+               s.conv_dim * act + s.d_inner * act + s.nheads * dt_bytes + s.d_inner * 4)
+    return batch * per_seq + s.conv_dim * 5 * 4 + s.d_inner * 4 + 2 * s.nheads * 4
+
+
+def _oracle_rows(args):
+    inp, H, P, N, G = args
+    from oracle import inproj as IP
+    t = time.perf_counter()
+    IP.prefill_inproj(inp, H, P, N, G)
+    return time.perf_counter() - t
+
+
+def cpu_baseline_rows(inp, s, seqs, tokens, label):
+    """The oracle on the first `tokens` rows of each sequence in `seqs` (packed-row
+    inputs), one task per sequence, in a process pool on the host cores."""
+    import multiprocessing as mp
+    import concurrent.futures as cf
+    import numpy as np
+    cu = inp["cu_seqlens"]
+    items, ntok = [], 0
+    for b in seqs:
+        lo = int(cu[b])
+        n = min(tokens, int(cu[b + 1]) - lo)
+        slot = int(inp["state_idx"][b])
+        one = dict(inp, row=inp["row"][lo:lo + n], cu_seqlens=np.array([0, n], np.int32),
+                   conv_state=inp["conv_state"][slot:slot + 1],
+                   ssm_state=inp["ssm_state"][slot:slot + 1],
+                   state_idx=np.zeros(1, np.int32), has_init=inp["has_init"][b:b + 1])
+        items.append((one, s.nheads, s.headdim, s.dstate, s.ngroups))
+        ntok += n
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), len(items)))
+    os.environ["OMP_NUM_THREADS"] = "1"
+    t = time.perf_counter()
+    with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as ex:
+        busy = sum(ex.map(_oracle_rows, items))
+    wall = time.perf_counter() - t
+    return {"value": ntok / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{label}: {ntok} tokens in {len(items)} per-sequence tasks; fp64 oracle "
+                      f"(row split, softplus step size, token recurrence, gated norm); "
+                      f"wall {wall:.2f} s, summed task time {busy:.1f} s"}
+
+
+def run_other_mode(args):
+    import numpy as np
+    from workloads import NANO, WORKLOADS, inproj_inputs
+    s = NANO
+    mode = args.mode
+    if mode == "decode":
+        lens = [1] * DECODE_BATCH
+        nd = DECODE_BATCH
+    elif mode == "mixed":
+        lens = [1] * DECODE_BATCH + list(MIXED_PREFILL)
+        nd = DECODE_BATCH
+    else:
+        lens = list(WORKLOADS[WORKLOAD_ID].seqlens)
+        nd = 0
+    t0 = time.time()
+    inp = inproj_inputs(s, lens, seed=20 + ["prefill_inproj", "decode", "mixed"].index(mode),
+                        act="bf16", init="pool", n_slots=len(lens))
+    T, nseq = sum(lens), len(lens)
+    log(f"inputs: {mode} T={T} sequences={nseq} generated in {time.time() - t0:.1f}s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        if mode == "decode":
+            cpu = cpu_baseline_rows(inp, s, range(DECODE_BATCH), 1, "all 256 decode rows")
+        else:
+            pre = list(range(nd, nseq))
+            cpu = cpu_baseline_rows(inp, s, pre, 768,
+                                    f"first 768 tokens of the {len(pre)} prefill sequences")
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores ({time.time() - t0:.1f}s)")
+
+    import torch
+    import mamba_ssd_selective_amd as m2
+    m2.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    g = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)
+    row = g(inp["row"], torch.bfloat16)
+    dt_bias, A, D = g(inp["dt_bias"]), g(inp["A"]), g(inp["D"])
+    conv_w, conv_b, norm_w = g(inp["conv_w"]), g(inp["conv_b"]), g(inp["norm_w"])
+    conv_state, ssm_state = g(inp["conv_state"]), g(inp["ssm_state"])
+    cu = g(inp["cu_seqlens"], torch.int32)
+    sidx, hinit = g(inp["state_idx"], torch.int32), g(inp["has_init"], torch.uint8)
+    del inp
+    di = s.d_inner
+    y = torch.empty((T, di), dtype=torch.float32, device=dev)
+    maxlen = max(lens)
+    H, P, N, G = s.nheads, s.headdim, s.dstate, s.ngroups
+    if mode == "decode":
+        def step():
+            m2.mamba2_decode_inproj(row, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state,
+                                    ssm_state, H, P, N, G, sidx, hinit, 1e-5, True, y=y)
+    elif mode == "mixed":
+        ws = torch.empty(m2.mamba2_mixed_inproj_workspace_size(T, nseq, maxlen, H, P, N, G, 128, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        def step():
+            m2.mamba2_mixed_inproj(row, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                                   cu, nd, maxlen, H, P, N, G, 128, sidx, hinit, y=y, workspace=ws)
+    else:
+        ws = torch.empty(m2.mamba2_prefill_inproj_workspace_size(T, nseq, maxlen, H, P, N, G, 128, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        def step():
+            m2.mamba2_prefill_inproj(row, dt_bias, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                                     cu, maxlen, H, P, N, G, 128, sidx, hinit, y=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    stream = torch.cuda.current_stream()
+    chain = mode != "decode"
+    if chain:
+        m2.timing_enable(args.steps)
+    # one event pair per step on the launch stream: for decode that brackets the one kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    assert torch.isfinite(y).all().item(), "non-finite output"
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step")
+    if args.copy_calib_mib > 0:
+        src = torch.ones(args.copy_calib_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
+        del src, dst
+    cfg = {"workload": {"decode": "nano_decode_256", "mixed": "nano_mixed_256dec_2x4096",
+                        "prefill_inproj": "nano_8x4096_bf16_inproj"}[mode],
+           "decode_rows": nd, "prefill_lens": lens[nd:] if len(lens) - nd <= 8 else f"{len(lens) - nd} x 4096",
+           "total_tokens": T, "nheads": H, "headdim": P, "dstate": N, "ngroups": G,
+           "conv_width": 4, "chunk": 128, "activations": "bf16", "output": "f32",
+           "state_pool_slots": nseq, "parallelism": "single-gpu"}
+    if chain:
+        kt = m2.timing_read()
+        m2.timing_enable(0)
+        stages = ("conv", "conv_state", "scan_pass", "scan_out", "norm")
+        kms = {k: kt[k + "_ms"] / max(1, kt["calls"]) for k in stages}
+        from workloads import Workload
+        wl = Workload("x", s, tuple(lens[nd:]), "bf16", "pool")
+        kb = kernel_bytes(wl, T - nd, nseq - nd)
+        dom = max(kms, key=kms.get)
+        achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
+                "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
+        log("kernel ms/step (prefill chain): " + ", ".join(f"{k} {v:.3f}" for k, v in kms.items()))
+        metric = "SSD prefill tokens/s per Mamba-2 layer @chunk128" if mode == "prefill_inproj" else \
+            "Mixed decode+prefill step tokens/s per Mamba-2 layer @chunk128"
+    else:
+        kb = decode_bytes(s, T, 2, dt_bytes=2)
+        achieved = kb / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(cfg["workload"], "decode_step", DECODE_SOURCES),
+                "kernel": "decode_step",
+                "kernel_ms": round(ms, 4), "kernel_bytes": kb}
+        metric = "Decode tokens/s per Mamba-2 layer (one token per sequence at cache slots)"
+    out = {"metric": metric, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 
