@@ -63,13 +63,19 @@ def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=1536):
     s = w.shape
     items = []
     cu = inp["cu_seqlens"]
+    ntok = 0
     for b in seqs:
         lo = int(cu[b])
+        n = min(tokens, int(cu[b + 1]) - lo)
+        ntok += n
+        slot = int(inp["state_idx"][b])
         one = dict(inp)
         for k in ("xbc", "z", "dt"):
-            one[k] = inp[k][lo:lo + tokens]
-        one["cu_seqlens"] = np.array([0, tokens], dtype=np.int32)
-        one["state_idx"] = inp["state_idx"][b:b + 1]
+            one[k] = inp[k][lo:lo + n]
+        one["cu_seqlens"] = np.array([0, n], dtype=np.int32)
+        one["conv_state"] = inp["conv_state"][slot:slot + 1]
+        one["ssm_state"] = inp["ssm_state"][slot:slot + 1]
+        one["state_idx"] = np.zeros(1, dtype=np.int32)
         one["has_init"] = inp["has_init"][b:b + 1]
         for g in range(s.ngroups):
             sub, sh = slice_group(one, s, g)
@@ -80,7 +86,6 @@ def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=1536):
     with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as ex:
         busy = sum(ex.map(_oracle_item, items))
     wall = time.perf_counter() - t
-    ntok = tokens * len(seqs)
     return {"value": ntok / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {tokens} tokens of sequences {list(seqs)} ({ntok} tokens, all "
                       f"{s.ngroups} groups / {s.nheads} heads) of the same input; fp64 "
@@ -175,6 +180,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("prefill", "prefill_inproj", "decode", "mixed"),
                     default="prefill")
+    ap.add_argument("--workload", type=int, choices=(1, 2, 4), default=WORKLOAD_ID,
+                    help="prefill workload: 2 = 8 x 4096 nano (the headline), 1 = one 137-token "
+                         "nano prompt (a latency), 4 = 16 packed sequences of U[1, 8192] tokens "
+                         "at the 8B shape with states from a 64-slot pool")
     ap.add_argument("--print-sources-sha1", action="store_true",
                     help="print the sha1 of the prefill-chain and decode kernel sources and exit")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -196,18 +205,20 @@ def main():
 
     import numpy as np
     from workloads import WORKLOADS, make_inputs
-    w = WORKLOADS[WORKLOAD_ID]
+    w = WORKLOADS[args.workload]
     s = w.shape
     t0 = time.time()
-    inp = make_inputs(w, WORKLOAD_ID)
+    inp = make_inputs(w, args.workload)
     T = int(inp["cu_seqlens"][-1])
     nseq = len(inp["cu_seqlens"]) - 1
+    lens = [int(v) for v in np.diff(inp["cu_seqlens"])]
     log(f"inputs: {w.name} T={T} generated in {time.time() - t0:.1f}s")
 
     cpu = None
     if not args.no_cpu_baseline:   # before the GPU is touched: the pool spawns processes
         t0 = time.time()
-        cpu = cpu_baseline(inp, w)
+        cpu = cpu_baseline(inp, w, seqs=tuple(range(min(8, nseq))),
+                           tokens=1536 if s.nheads <= 64 else 768)
         log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores ({time.time() - t0:.1f}s)")
 
     import torch
@@ -227,7 +238,7 @@ def main():
     del inp
     di, gn = s.d_inner, s.ngroups * s.dstate
     x, B, C = xbc[:, :di], xbc[:, di:di + gn], xbc[:, di + gn:]
-    maxlen = 4096
+    maxlen = max(lens)
     ws = torch.empty(m2.mamba2_prefill_workspace_size(T, nseq, maxlen, s.nheads, s.headdim, s.dstate,
                                                       s.ngroups, w.chunk_size, at),
                      dtype=torch.uint8, device=dev)
@@ -287,7 +298,9 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": w.name, "batch": nseq, "seq_len": 4096, "total_tokens": T,
+           "config": {"workload": w.name, "batch": nseq,
+                      "seq_len": lens[0] if len(set(lens)) == 1 else f"varlen {min(lens)}..{max(lens)}",
+                      "total_tokens": T,
                       "nheads": s.nheads, "headdim": s.headdim, "dstate": s.dstate,
                       "ngroups": s.ngroups, "conv_width": s.width, "chunk": w.chunk_size,
                       "activations": w.act, "output": "f32", "parallelism": "single-gpu"},

@@ -180,9 +180,11 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
 
 /*
  * Bytes of device workspace ssd_chunk_scan needs for these sizes (0 when the
- * shape runs on a path without workspace, or on bad arguments):
- * (total_tokens/128 + batch) * nheads * headdim * dstate * 4 on the
- * chunk-parallel path.
+ * shape runs on a path without workspace, or on bad arguments): on the
+ * chunk-parallel path the state entering every chunk, (total_tokens/128 +
+ * batch) * nheads * headdim * dstate * 4 bytes, then the order in which the
+ * sequences' carries are dealt out (batch int32), each part rounded up to
+ * 256 bytes.
  */
 size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads, int headdim,
                                      int dstate, int ngroups, int chunk_size, int act_dtype);

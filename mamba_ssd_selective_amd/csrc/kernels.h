@@ -61,6 +61,7 @@ struct ScanArgs {
     int nheads, headdim, dstate, ngroups, chunk;
     float* y; int64_t ld_y;
     float* states;              // chunk-parallel path: entry state of every chunk
+    int32_t* order;             // chunk-parallel path: sequences by length, longest first [batch]
 };
 
 struct NormArgs {
@@ -133,8 +134,12 @@ bool scan_supported(int headdim, int dstate);
 // block in the state pass's accumulator order; sequence b's chunk c is slot
 // cu_seqlens[b]/128 + b + c) and the final states; the chunk
 // pass reads them and writes y.
+// The workspace holds the entry states (256-byte rounded) and then the int32
+// order of the sequences, longest first, that the state pass deals work in.
 bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, int dstate, int chunk);
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate);
+int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
+                            int dstate);
 hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream);
 

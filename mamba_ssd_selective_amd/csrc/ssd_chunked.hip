@@ -86,11 +86,52 @@ __device__ __forceinline__ void gamma_scan(float d0, float d1, float Ah, int lan
 
 __device__ __forceinline__ float expc(double v) { return __expf(static_cast<float>(fmin(v, 0.0))); }
 
-// Workgroup -> (sequence, head), with the heads of one group of one sequence on
-// one XCD (workgroups are dealt round-robin over the 8 XCDs), so the group's
-// B rows are shared through that XCD's L2.
-__device__ __forceinline__ int item_of(int lin, int total) {
-    return (total % 8 == 0) ? (lin % 8) * (total / 8) + lin / 8 : lin;
+// State-pass workgroup -> (sequence, head).  A (sequence, group) pair takes
+// wpp = hpg / ipw consecutive workgroups on one XCD (workgroups are dealt
+// round-robin over the 8 XCDs, lin % 8), so the group's B rows are shared
+// through that XCD's L2.  Pairs are dealt in the order of `order` -- the
+// sequences by length, longest first -- round-robin over the XCDs: a
+// workgroup walks its sequence's chunks one after another, so dispatching the
+// longest walks first keeps the short ones for the end, where they fill the
+// CUs the long ones leave idle, instead of leaving a long walk as the tail.
+__device__ __forceinline__ void state_item(int lin, const ScanArgs& a, int ipw, int sub, int& seq,
+                                           int& head) {
+    const int hpg = a.nheads / a.ngroups;
+    const int wpp = hpg / ipw;
+    int r, w;
+    if ((a.batch * a.ngroups) % 8 == 0) {
+        const int pos = lin >> 3;
+        r = 8 * (pos / wpp) + (lin & 7);
+        w = pos % wpp;
+    } else {
+        r = lin / wpp;
+        w = lin % wpp;
+    }
+    seq = a.order ? a.order[r / a.ngroups] : r / a.ngroups;
+    head = (r % a.ngroups) * hpg + ipw * w + sub;
+}
+
+// order[k] = the sequence of rank k by length, longest first (ties by index),
+// so the result is a permutation of 0 .. batch-1 whatever cu_seqlens holds.
+// Thread b ranks sequence b against every length, staged through LDS.
+constexpr int ORD_NT = 256;
+constexpr int ORD_TILE = 1024;
+__global__ __launch_bounds__(ORD_NT) void seq_order_kernel(const int32_t* cu, int batch, int32_t* order) {
+    __shared__ int32_t len[ORD_TILE];
+    const int b = blockIdx.x * ORD_NT + threadIdx.x;
+    const int Lb = b < batch ? cu[b + 1] - cu[b] : 0;
+    int rank = 0;
+    for (int j0 = 0; j0 < batch; j0 += ORD_TILE) {
+        const int n = min(ORD_TILE, batch - j0);
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += ORD_NT) len[j] = cu[j0 + j + 1] - cu[j0 + j];
+        __syncthreads();
+        for (int j = 0; j < n; ++j) {
+            const int Lj = len[j];
+            rank += (Lj > Lb || (Lj == Lb && j0 + j < b)) ? 1 : 0;
+        }
+    }
+    if (b < batch) order[rank] = b;
 }
 
 // Inputs come as bf16 (8 channels per 16-byte load, exact in bf16) or fp32 (4
@@ -219,8 +260,8 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     const int tid = threadIdx.x & (NT - 1);
     const int wave = tid >> 6, lane = tid & 63;
     const int gwave = (int)(threadIdx.x >> 6);                // wave within the workgroup
-    const int item = IPW * item_of(blockIdx.x, a.nheads * a.batch / IPW) + sub;
-    const int seq = item / a.nheads, head = item % a.nheads;
+    int seq, head;
+    state_item(blockIdx.x, a, IPW, sub, seq, head);
     const int grp = head / (a.nheads / a.ngroups);
     const int64_t s0 = a.cu_seqlens[seq];
     const int64_t L = a.cu_seqlens[seq + 1] - s0;
@@ -818,11 +859,30 @@ bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, in
            ngroups > 0 && nheads % ngroups == 0 && nheads / ngroups <= MAXHPG;
 }
 
+static size_t entry_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate) {
+    const size_t b = (size_t)(total_tokens / Q + batch) * (size_t)nheads * (size_t)headdim *
+                     (size_t)dstate * sizeof(float);
+    return (b + 255) / 256 * 256;
+}
+
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate) {
-    return (size_t)(total_tokens / Q + batch) * (size_t)nheads * (size_t)headdim * (size_t)dstate * sizeof(float);
+    return entry_states_bytes(total_tokens, batch, nheads, headdim, dstate) +
+           ((size_t)batch * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
+                            int dstate) {
+    return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(states) +
+                                      entry_states_bytes(total_tokens, batch, nheads, headdim, dstate));
 }
 
 hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream) {
+    if (a.order) {
+        hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((a.batch + ORD_NT - 1) / ORD_NT)), dim3(ORD_NT), 0,
+                           stream, a.cu_seqlens, a.batch, a.order);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const bool f = a.act_dtype == kF32;
     if (a.dstate == 128) return f ? launch_pass<128, float>(a, stream) : launch_pass<128, u16>(a, stream);
     if (a.dstate == 64) return f ? launch_pass<64, float>(a, stream) : launch_pass<64, u16>(a, stream);

@@ -99,11 +99,13 @@ def test_workspace_query_and_prefill_workspace_error():
 
 
 def test_scan_workspace_query():
-    """Chunk-parallel path: one fp32 state per chunk slot, slots = T // 128 + batch."""
+    """Chunk-parallel path: one fp32 state per chunk slot, slots = T // 128 + batch, then
+    the int32 dispatch order of the sequences, each part rounded up to 256 bytes."""
     lib = m2.load()
     per_slot = 64 * 64 * 128 * 4
-    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 1) == (1000 // 128 + 3) * per_slot
-    assert lib.ssd_chunk_scan_workspace_size(4096 * 8, 8, 64, 64, 128, 8, 128, 1) == (256 + 8) * per_slot
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 1) == (1000 // 128 + 3) * per_slot + 256
+    assert lib.ssd_chunk_scan_workspace_size(4096 * 8, 8, 64, 64, 128, 8, 128, 1) == (256 + 8) * per_slot + 256
+    assert lib.ssd_chunk_scan_workspace_size(1000, 100, 64, 64, 128, 8, 128, 1) == (1000 // 128 + 100) * per_slot + 512
     # paths without workspace: fp32 inputs, other chunk sizes, other shapes
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 0) == 0
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 64, 1) == 0
