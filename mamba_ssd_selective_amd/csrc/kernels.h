@@ -62,6 +62,13 @@ struct ScanArgs {
     float* y; int64_t ld_y;
     float* states;              // chunk-parallel path: entry state of every chunk
     int32_t* order;             // chunk-parallel path: sequences by length, longest first [batch]
+    // Chunk-parallel path, long sequences split into segments of `seg` chunks
+    // (0 = not split): segment k >= 1 of a sequence starts from a zero state.
+    int seg;
+    int seg_levels;             // segments of the longest sequence (state-pass grid levels)
+    double* lam;                // per (first chunk slot of a segment, head): its total log decay
+    double* cum;                // per (chunk slot, head): log decay from its segment's start
+    float* seg_end;             // [batch * nheads] local end states of last segments
 };
 
 struct NormArgs {
@@ -140,6 +147,9 @@ bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, in
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate);
 int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
                             int dstate);
+// Sets a.seg (and the buffers behind it) from the longest sequence: long
+// sequences are split when the (sequence, head) walks alone would leave CUs idle.
+void chunked_scan_plan(ScanArgs& a, int64_t total_tokens, int max_seqlen);
 hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream);
 

@@ -329,6 +329,8 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     a.chunk = chunk_size; a.y = y; a.ld_y = ld_y;
     a.states = need > 0 ? static_cast<float*>(workspace) : nullptr;
     a.order = a.states ? m2::chunked_scan_order(a.states, total_tokens, batch, nheads, headdim, dstate) : nullptr;
+    if (a.states) m2::chunked_scan_plan(a, total_tokens, max_seqlen);
+    if (batch == 1) a.order = nullptr;  // one sequence: no order to compute
     if ((st = launch_scan(a, total_tokens, static_cast<hipStream_t>(stream), nullptr))) return st;
     return ok();
 }
@@ -475,6 +477,8 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     sa.chunk = chunk_size; sa.y = ypre; sa.ld_y = ld_pre;
     sa.states = states_ws;
     sa.order = states_ws ? m2::chunked_scan_order(states_ws, total_tokens, batch, nheads, headdim, dstate) : nullptr;
+    if (states_ws) m2::chunked_scan_plan(sa, total_tokens, max_seqlen);
+    if (batch == 1) sa.order = nullptr;  // one sequence: no order to compute
     if ((st = launch_scan(sa, total_tokens, s, tev ? tev[3] : nullptr))) return st;
     mark(4);
 

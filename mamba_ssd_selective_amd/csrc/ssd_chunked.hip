@@ -260,11 +260,17 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     const int tid = threadIdx.x & (NT - 1);
     const int wave = tid >> 6, lane = tid & 63;
     const int gwave = (int)(threadIdx.x >> 6);                // wave within the workgroup
+    // grid: one level of batch * nheads / IPW workgroups per segment index
+    const int level = a.nheads * a.batch / IPW;
+    const int seg_k = (int)blockIdx.x / level;
     int seq, head;
-    state_item(blockIdx.x, a, IPW, sub, seq, head);
+    state_item((int)blockIdx.x % level, a, IPW, sub, seq, head);
     const int grp = head / (a.nheads / a.ngroups);
     const int64_t s0 = a.cu_seqlens[seq];
     const int64_t L = a.cu_seqlens[seq + 1] - s0;
+    // segment seg_k of this sequence has no chunk (uniform over the workgroup: both
+    // items share the sequence)
+    if (seg_k > 0 && (int64_t)seg_k * a.seg * Q >= L) return;
     const int slot = a.state_idx ? a.state_idx[seq] : seq;
     const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
     const float Ah = a.A[head];
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             float4 v = float4{0.f, 0.f, 0.f, 0.f};
-            if (init && L > 0) v = *reinterpret_cast<const float4*>(st + soff(i, m));
+            if (init && L > 0 && seg_k == 0) v = *reinterpret_cast<const float4*>(st + soff(i, m));
             acc[i][4 * m + 0] = v.x; acc[i][4 * m + 1] = v.y; acc[i][4 * m + 2] = v.z; acc[i][4 * m + 3] = v.w;
         }
     if (L <= 0) {
@@ -305,6 +311,10 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
 
     const int nch = (int)((L + Q - 1) / Q);
     const int64_t cbase = s0 / Q + seq;   // entry-state slot of the sequence's first chunk
+    // this workgroup's chunks: all of them, or segment seg_k's (a later segment
+    // starts from zero; its first entry slot belongs to the segment before)
+    const int cfirst = seg_k * a.seg;
+    const int cend = a.seg > 0 ? (cfirst + a.seg < nch ? cfirst + a.seg : nch) : nch;
     const Tin* Xg = static_cast<const Tin*>(a.x);
     const Tin* Bg = static_cast<const Tin*>(a.B);
 
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     // Loads of half h (0, 1) of chunk c, clamped to the last chunk so the call is
     // unconditional; rows beyond the chunk re-read its last row (zeroed later).
     auto load_half = [&](HalfBuf<Tin, TB, TX>& b, int c, int h) __attribute__((always_inline)) {
-        c = c < nch ? c : nch - 1;
+        c = c < cend ? c : cend - 1;
         const int64_t left = L - (int64_t)c * Q - h * QH;     // rows of the sequence from this half on
         const int S = (int)(left < QH ? left : QH);
         // an empty half (the chunk ends in its first half) reads the chunk's first row
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         load_rows_clamped<TX>(Xg + (r0 + rx) * a.ld_x + head * a.hs_x + x_cg * CPL, a.ld_x, S - rx, b.xr);
     };
     auto load_dt = [&](int c, float& d0, float& d1) __attribute__((always_inline)) {
-        c = c < nch ? c : nch - 1;
+        c = c < cend ? c : cend - 1;
         const int64_t r0 = s0 + (int64_t)c * Q;
         const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
         d0 = a.dt[(r0 + (2 * lane < S ? 2 * lane : S - 1)) * a.ld_dt + head];
@@ -410,13 +420,14 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     // order here would make every chunk wait for both halves at once.
     HalfBuf<Tin, TB, TX> buf0, buf1;
     float d0, d1;
-    load_dt(0, d0, d1);
+    load_dt(cfirst, d0, d1);
     __builtin_amdgcn_sched_barrier(0);
-    load_half(buf0, 0, 0);
+    load_half(buf0, cfirst, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_half(buf1, 0, 1);
+    load_half(buf1, cfirst, 1);
     __builtin_amdgcn_sched_barrier(0);
-    for (int c = 0; c < nch; ++c) {
+    double lrun = 0.0;   // log decay from the segment's start to the current chunk
+    for (int c = cfirst; c < cend; ++c) {
         const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
         if (2 * lane >= S) d0 = 0.f;
         if (2 * lane + 1 >= S) d1 = 0.f;
@@ -430,12 +441,17 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         // entry state of this chunk, then h <- e(gamma_S) h (the stores go out first,
         // so they are the oldest memory operations whenever a later load is awaited)
         float* he = a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N);
+        const bool store = seg_k == 0 || c > cfirst;
+        if (seg_k > 0 && c > cfirst && tid == 0) a.cum[(cbase + c) * a.nheads + head] = lrun;
+        lrun += gS;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
+            if (store) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<float4*>(he + eoff(i, m)) =
-                    float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+                for (int m = 0; m < 4; ++m)
+                    *reinterpret_cast<float4*>(he + eoff(i, m)) =
+                        float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+            }
             acc[i] *= decay;
         }
         load_dt(c + 1, d0, d1);
@@ -463,12 +479,82 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         multiply(S1 > 0 ? (S1 + 15) >> 4 : 0);
     }
 
+    // The end state: the sequence's final state when this is its only segment;
+    // otherwise a local end state, left in the next segment's first entry slot
+    // (for segment 0 that is already the true entry state there) or, for the
+    // last segment, in seg_end, for the carry kernel to complete.
+    if (cend == nch && seg_k == 0) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
+        for (int i = 0; i < TPW; ++i)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            *reinterpret_cast<float4*>(st + soff(i, m)) =
-                float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<float4*>(st + soff(i, m)) =
+                    float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+    } else {
+        float* he = cend < nch ? a.states + ((cbase + cend) * a.nheads + head) * (int64_t)(P * N)
+                               : a.seg_end + ((int64_t)seq * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<float4*>(he + eoff(i, m)) =
+                    float4{acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+        if (seg_k > 0 && tid == 0) a.lam[(cbase + cfirst) * a.nheads + head] = lrun;
+    }
+}
+
+// ------------------------------------------------------------------ segment carry
+//
+// For a sequence split into segments, one workgroup per (sequence, head) runs
+// the recurrence over segment boundaries: with E_k segment k's end state from a
+// zero start (E_0 from the true initial state) and lam_k its total log decay,
+// the true end states are T_0 = E_0, T_k = e(lam_k) T_{k-1} + E_k.  T_{k-1} is
+// the entry state of segment k's first chunk, written over E_{k-1} there; the
+// last T is the sequence's final state.  Elementwise over the P x N state, in
+// the accumulator order of the entry slots.
+template <int N>
+__global__ __launch_bounds__(256) void segment_carry_kernel(ScanArgs a) {
+    constexpr int F = P * N / 4;      // float4 per state
+    constexpr int PT = F / 256;       // float4 per thread
+    const int seq = (int)blockIdx.x / a.nheads, head = (int)blockIdx.x % a.nheads;
+    const int tid = threadIdx.x;
+    const int64_t s0 = a.cu_seqlens[seq];
+    const int64_t L = a.cu_seqlens[seq + 1] - s0;
+    if (L <= 0) return;
+    const int nch = (int)((L + Q - 1) / Q);
+    const int nseg = (nch + a.seg - 1) / a.seg;
+    if (nseg <= 1) return;
+    const int64_t cbase = s0 / Q + seq;
+    auto entry = [&](int c) {
+        return reinterpret_cast<float4*>(a.states + ((cbase + c) * a.nheads + head) * (int64_t)(P * N));
+    };
+    float4 T[PT];
+    const float4* e1 = entry(a.seg);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) T[j] = e1[tid + 256 * j];
+    for (int k = 1; k < nseg; ++k) {
+        const float d = expc(a.lam[(cbase + (int64_t)k * a.seg) * a.nheads + head]);
+        const bool last = k == nseg - 1;
+        float4* E = last ? reinterpret_cast<float4*>(a.seg_end + ((int64_t)seq * a.nheads + head) * (int64_t)(P * N))
+                         : entry((k + 1) * a.seg);
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const float4 e = E[tid + 256 * j];
+            T[j] = float4{fmaf(d, T[j].x, e.x), fmaf(d, T[j].y, e.y), fmaf(d, T[j].z, e.z), fmaf(d, T[j].w, e.w)};
+        }
+        if (!last) {
+#pragma unroll
+            for (int j = 0; j < PT; ++j) E[tid + 256 * j] = T[j];
+        }
+    }
+    const int slot = a.state_idx ? a.state_idx[seq] : seq;
+    float* st = a.ssm_state + ((int64_t)slot * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        int p, n;
+        state_pn(tid + 256 * j, p, n);
+        *reinterpret_cast<float4*>(st + p * N + n) = T[j];
+    }
 }
 
 // ------------------------------------------------------------------ chunk out
@@ -538,6 +624,13 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     const int tg = tid % 16;
     uint4 xr[8];
     float4 hr[NHV];
+    // In a split sequence, a chunk after the first of a later segment holds a
+    // local entry state: the true one adds e(log decay since the segment's start)
+    // times the segment's true entry state (its first chunk's slot).
+    const bool fix = a.seg > 0 && c >= a.seg && c % a.seg != 0;
+    const int64_t cslot0 = cslot - (fix ? c % a.seg : 0);
+    float4 hs[NHV];
+    float fcum = 0.f;
     float dr0 = 0.f, dr1 = 0.f;
     // x piece tg holds the chunk rows the intra products take as one K slot
     // group: rows 32 kb + 4 q + r (slots 0-3) and 32 kb + 16 + 4 q + r (slots
@@ -556,6 +649,12 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
         for (int k = 0; k < NHV; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + NT * k));
+        if (fix) {
+            const float* hf = a.states + (cslot0 * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+            for (int k = 0; k < NHV; ++k) hs[k] = *reinterpret_cast<const float4*>(hf + 4 * (tid + NT * k));
+            fcum = expc(a.cum[(int64_t)cslot * a.nheads + head]);
+        }
         if (wave == 0) {
             dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
             dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
@@ -688,6 +787,12 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             }
         }
         // h_in split planes: float4 k of the entry state covers (p, n .. n + 3)
+        if (fix) {
+#pragma unroll
+            for (int k = 0; k < NHV; ++k)
+                hr[k] = float4{fmaf(fcum, hs[k].x, hr[k].x), fmaf(fcum, hs[k].y, hr[k].y),
+                               fmaf(fcum, hs[k].z, hr[k].z), fmaf(fcum, hs[k].w, hr[k].w)};
+        }
 #pragma unroll
         for (int k = 0; k < NHV; ++k) {
             int p, n;
@@ -835,13 +940,21 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
 
 template <int N, typename Tin>
 hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
+    const unsigned levels = a.seg > 0 ? (unsigned)a.seg_levels : 1u;
     if constexpr (N == 128) {
         if ((a.nheads / a.ngroups) % 2 == 0) {
-            hipLaunchKernelGGL((ssd_state_pass_kernel<N, 2, Tin>), dim3(a.nheads * a.batch / 2), dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((ssd_state_pass_kernel<N, 2, Tin>), dim3(a.nheads * a.batch / 2 * levels), dim3(512),
+                               0, stream, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((ssd_state_pass_kernel<N, 1, Tin>), dim3(a.nheads * a.batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((ssd_state_pass_kernel<N, 1, Tin>), dim3(a.nheads * a.batch * levels), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_carry(const ScanArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(segment_carry_kernel<N>, dim3(a.nheads * a.batch), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -859,15 +972,54 @@ bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, in
            ngroups > 0 && nheads % ngroups == 0 && nheads / ngroups <= MAXHPG;
 }
 
+static size_t r256(size_t v) { return (v + 255) / 256 * 256; }
+
 static size_t entry_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate) {
-    const size_t b = (size_t)(total_tokens / Q + batch) * (size_t)nheads * (size_t)headdim *
-                     (size_t)dstate * sizeof(float);
-    return (b + 255) / 256 * 256;
+    return r256((size_t)(total_tokens / Q + batch) * (size_t)nheads * (size_t)headdim * (size_t)dstate *
+                sizeof(float));
+}
+
+// Splitting sequences into segments: only when the (sequence, head) walks fill
+// fewer than SEG_TARGET state-pass workgroups (one per CU), into segments of at
+// least SEG_MIN chunks.  Then batch * nheads < 2 * SEG_TARGET, which bounds the
+// end states the last segments leave for the carry kernel.  At one workgroup
+// per CU already (8 x 4096 tokens, 64 heads), splitting in two cost more in the
+// chunk output's extra entry-state reads (0.40 -> 0.45 ms) than it saved.
+constexpr int SEG_TARGET = 256;
+constexpr int SEG_MIN = 4;
+constexpr int SEG_END_MAX = 2 * SEG_TARGET;
+
+static size_t seg_end_bytes(int batch, int nheads, int headdim, int dstate) {
+    const int64_t n = (int64_t)batch * nheads < SEG_END_MAX ? (int64_t)batch * nheads : SEG_END_MAX;
+    return r256((size_t)n * headdim * dstate * sizeof(float));
 }
 
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate) {
+    const size_t slots = (size_t)(total_tokens / Q + batch) * (size_t)nheads;
     return entry_states_bytes(total_tokens, batch, nheads, headdim, dstate) +
-           ((size_t)batch * sizeof(int32_t) + 255) / 256 * 256;
+           r256((size_t)batch * sizeof(int32_t)) + seg_end_bytes(batch, nheads, headdim, dstate) +
+           2 * r256(slots * sizeof(double));
+}
+
+void chunked_scan_plan(ScanArgs& a, int64_t total_tokens, int max_seqlen) {
+    a.seg = 0;
+    a.seg_levels = 1;
+    char* p = reinterpret_cast<char*>(a.order) + r256((size_t)a.batch * sizeof(int32_t));
+    a.seg_end = reinterpret_cast<float*>(p);
+    p += seg_end_bytes(a.batch, a.nheads, a.headdim, a.dstate);
+    const size_t slots = (size_t)(total_tokens / Q + a.batch) * (size_t)a.nheads;
+    a.lam = reinterpret_cast<double*>(p);
+    a.cum = reinterpret_cast<double*>(p + r256(slots * sizeof(double)));
+    const int hpg = a.nheads / a.ngroups;
+    const int ipw = (a.dstate == 128 && hpg % 2 == 0) ? 2 : 1;
+    const int64_t level = (int64_t)a.nheads * a.batch / ipw;
+    const int nch = (int)(((int64_t)max_seqlen + Q - 1) / Q);
+    if (level >= SEG_TARGET || (int64_t)a.batch * a.nheads > SEG_END_MAX) return;
+    int nseg = (int)((SEG_TARGET + level - 1) / level);
+    if (nseg > nch / SEG_MIN) nseg = nch / SEG_MIN;
+    if (nseg < 2) return;
+    a.seg = (nch + nseg - 1) / nseg;
+    a.seg_levels = (nch + a.seg - 1) / a.seg;
 }
 
 int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
@@ -884,9 +1036,11 @@ hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const bool f = a.act_dtype == kF32;
-    if (a.dstate == 128) return f ? launch_pass<128, float>(a, stream) : launch_pass<128, u16>(a, stream);
-    if (a.dstate == 64) return f ? launch_pass<64, float>(a, stream) : launch_pass<64, u16>(a, stream);
-    return hipErrorInvalidValue;
+    hipError_t e = hipErrorInvalidValue;
+    if (a.dstate == 128) e = f ? launch_pass<128, float>(a, stream) : launch_pass<128, u16>(a, stream);
+    if (a.dstate == 64) e = f ? launch_pass<64, float>(a, stream) : launch_pass<64, u16>(a, stream);
+    if (e != hipSuccess || a.seg == 0) return e;
+    return a.dstate == 128 ? launch_carry<128>(a, stream) : launch_carry<64>(a, stream);
 }
 
 hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream) {

@@ -99,13 +99,20 @@ def test_workspace_query_and_prefill_workspace_error():
 
 
 def test_scan_workspace_query():
-    """Chunk-parallel path: one fp32 state per chunk slot, slots = T // 128 + batch, then
-    the int32 dispatch order of the sequences, each part rounded up to 256 bytes."""
+    """Chunk-parallel path: one fp32 state per chunk slot (slots = T // 128 + batch), the
+    int32 dispatch order of the sequences, the end states of split sequences' last
+    segments (at most 512 states) and two fp64 log decays per (chunk slot, head); each
+    part rounded up to 256 bytes."""
     lib = m2.load()
     per_slot = 64 * 64 * 128 * 4
-    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 1) == (1000 // 128 + 3) * per_slot + 256
-    assert lib.ssd_chunk_scan_workspace_size(4096 * 8, 8, 64, 64, 128, 8, 128, 1) == (256 + 8) * per_slot + 256
-    assert lib.ssd_chunk_scan_workspace_size(1000, 100, 64, 64, 128, 8, 128, 1) == (1000 // 128 + 100) * per_slot + 512
+    r = lambda v: (v + 255) // 256 * 256
+
+    def expect(T, b, H=64):
+        slots = T // 128 + b
+        return slots * per_slot + r(4 * b) + min(b * H, 512) * 64 * 128 * 4 + 2 * r(8 * slots * H)
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 1) == expect(1000, 3)
+    assert lib.ssd_chunk_scan_workspace_size(4096 * 8, 8, 64, 64, 128, 8, 128, 1) == expect(4096 * 8, 8)
+    assert lib.ssd_chunk_scan_workspace_size(1000, 100, 64, 64, 128, 8, 128, 1) == expect(1000, 100)
     # paths without workspace: fp32 inputs, other chunk sizes, other shapes
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 0) == 0
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 64, 1) == 0

@@ -104,6 +104,8 @@ SCAN_CASES = [
     (LayerShape(16, 64, 128, 1), [128, 0, 1, 257, 255], 128),
     (LayerShape(8, 64, 64, 4), [513, 3, 0], 128),
     (LayerShape(64, 64, 128, 8), [129, 384], 128),
+    # few long sequences: the state pass splits them into segments
+    (LayerShape(16, 64, 128, 2), [1500, 40], 128),
 ]
 
 
@@ -265,6 +267,31 @@ def _sampled(w, seed, pairs, act):
         assert rel_err(y[lo:hi][:, xch_t], ref["y"], "y", (hi - lo) * len(xch)) <= tol
         assert rel_err(ss[slot][heads_t], ref["ssm_state"][slot], "ssm_state") <= tol
         assert rel_err(cs[slot][:, ch_t], ref["conv_state"][slot], "conv_state") <= tol
+
+
+# Few long sequences leave most CUs idle if each (sequence, head) walks its
+# chunks alone, so the state pass splits them into segments that start from a
+# zero state and a carry pass joins them.  Cases: ragged last chunk and
+# segment, an empty and a one-row sequence next to long ones, an exact
+# multiple of the segment length, dstate 64 (one head per workgroup), a fresh
+# slot on a long sequence.
+SEGMENT_CASES = [
+    # (shape, lengths, has_init)
+    (LayerShape(16, 64, 128, 2), [2000, 700, 1, 0], [1, 0, 1, 1]),
+    (LayerShape(8, 64, 64, 4), [1029, 512], [1, 1]),
+    (LayerShape(16, 64, 128, 2), [4096], [1]),
+    (LayerShape(16, 64, 128, 2), [1300, 2600], [0, 1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SEGMENT_CASES)))
+def test_prefill_long_sequences_split_into_segments(case):
+    shape, lens, init = SEGMENT_CASES[case]
+    inp = small_shape_inputs(shape, lens, seed=60 + case, act="bf16", init="pool",
+                             n_slots=len(lens) + 3)
+    inp["has_init"] = np.array(init, dtype=np.uint8)
+    print(f" shape={shape} lens={lens} slots={inp['state_idx'].tolist()}")
+    check_all(inp, shape, "bf16")
 
 
 def test_prefill_decay_stress_full_size():
