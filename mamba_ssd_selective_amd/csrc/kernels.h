@@ -69,6 +69,7 @@ struct ScanArgs {
     double* lam;                // per (first chunk slot of a segment, head): its total log decay
     double* cum;                // per (chunk slot, head): log decay from its segment's start
     float* seg_end;             // [batch * nheads] local end states of last segments
+    int out_split;              // chunk output: workgroups per (chunk, group), each a run of heads
 };
 
 struct NormArgs {

@@ -599,8 +599,13 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
     const int G = a.ngroups;
     const int hpg = a.nheads / G;
-    const int cslot = blockIdx.x / G;
-    const int grp = blockIdx.x % G;
+    // a small grid splits each group's heads over out_split workgroups (each
+    // forms G^T itself): heads j0 .. j1-1 of the group
+    const int split = a.out_split > 1 ? a.out_split : 1;
+    const int cg = (int)blockIdx.x / split;
+    const int j0 = ((int)blockIdx.x % split) * (hpg / split), j1 = j0 + hpg / split;
+    const int cslot = cg / G;
+    const int grp = cg % G;
 
     // chunk slot -> (sequence, chunk): sequence b owns slots cu[b]/Q + b + c
     int lo = 0, hi = a.batch;
@@ -660,7 +665,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
         }
     };
-    prefetch(grp * hpg);
+    prefetch(grp * hpg + j0);
     // A and D of the group's heads, read once (a per-head load issued after the
     // next head's prefetch would make the compiler wait for that prefetch too)
     for (int e = tid; e < hpg; e += NT) {
@@ -925,15 +930,15 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     };
 
     __syncthreads();   // the G phase is done with the B / C slices
-    stage_head(0, 0);
-    prefetch(hpg > 1 ? grp * hpg + 1 : grp * hpg);
+    stage_head(0, j0);
+    prefetch(j0 + 1 < j1 ? grp * hpg + j0 + 1 : grp * hpg + j0);
     __syncthreads();
-    for (int j = 0; j < hpg; ++j) {
-        if (j + 1 < hpg) {
-            stage_head((j + 1) & 1, j + 1);
-            if (j + 2 < hpg) prefetch(grp * hpg + j + 2);
+    for (int j = j0; j < j1; ++j) {
+        if (j + 1 < j1) {
+            stage_head((j - j0 + 1) & 1, j + 1);
+            if (j + 2 < j1) prefetch(grp * hpg + j + 2);
         }
-        compute_head(j & 1, j);
+        compute_head((j - j0) & 1, j);
         __syncthreads();
     }
 }
@@ -961,7 +966,9 @@ hipError_t launch_carry(const ScanArgs& a, hipStream_t stream) {
 template <int N, typename Tin>
 hipError_t launch_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream) {
     const int64_t slots = total_tokens / Q + a.batch;
-    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Tin>), dim3((unsigned)(slots * a.ngroups)), dim3(512), 0, stream, a);
+    const int split = a.out_split > 1 ? a.out_split : 1;
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Tin>), dim3((unsigned)(slots * a.ngroups * split)), dim3(512), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -1002,6 +1009,15 @@ size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, in
 }
 
 void chunked_scan_plan(ScanArgs& a, int64_t total_tokens, int max_seqlen) {
+    // chunk output: fewer (chunk, group) workgroups than CUs split the group's
+    // heads over up to hpg workgroups (a 137-token prompt has 16 such pairs)
+    {
+        const int hpg = a.nheads / a.ngroups;
+        const int64_t wgs = (total_tokens / Q + a.batch) * (int64_t)a.ngroups;
+        int split = 1;
+        while (hpg % (2 * split) == 0 && wgs * 2 * split <= 256) split *= 2;
+        a.out_split = split;
+    }
     a.seg = 0;
     a.seg_levels = 1;
     char* p = reinterpret_cast<char*>(a.order) + r256((size_t)a.batch * sizeof(int32_t));
