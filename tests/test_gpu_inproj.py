@@ -161,3 +161,51 @@ def test_mixed_batch_identity_slots_and_repeatability():
     compare(d, y, ref, shape, "bf16", sum(lens))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_mixed_batch_full_size_sampled():
+    """The mixed step at the size the bench times: 256 decode rows, then two
+    4096-token prefills (which the state pass splits into segments), nano shape.
+    Every decode row is checked in full; the prefills on sampled (sequence,
+    group) slices, each an exact sub-problem of the mixer core."""
+    from oracle import recurrence as R
+    from workloads import group_channels, slice_group
+    s = NANO
+    H, P, N, G = s.nheads, s.headdim, s.dstate, s.ngroups
+    nd = 256
+    lens = [1] * nd + [4096, 4096]
+    inp = inproj_inputs(s, lens, seed=22, act="bf16", init="pool", n_slots=len(lens))
+    d = to_device(inp, "bf16")
+    y = m2.mamba2_mixed_inproj(d["row"], d["dt_bias"], d["A"], d["D"], d["conv_w"], d["conv_b"],
+                               d["norm_w"], d["conv_state"], d["ssm_state"], d["cu_seqlens"], nd,
+                               4096, H, P, N, G, 128, d["state_idx"], d["has_init"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    tol = TOL["bf16"]
+    cu = inp["cu_seqlens"]
+    # decode rows: the oracle over those sequences only
+    ref = IP.prefill_inproj(inp, H, P, N, G, seqs=range(nd))
+    slots = inp["state_idx"][:nd]
+    assert rel_err(y[:nd], ref["y"][:nd], "decode y", nd * s.d_inner) <= tol
+    assert rel_err(d["ssm_state"][torch.as_tensor(slots, device="cuda", dtype=torch.long)],
+                   ref["ssm_state"][slots], "decode ssm_state") <= tol
+    assert rel_err(d["conv_state"][torch.as_tensor(slots, device="cuda", dtype=torch.long)],
+                   ref["conv_state"][slots], "decode conv_state") <= tol
+    # prefill sequences: sampled groups
+    z, xbc, dt_raw = IP.split_inproj_row(inp["row"], H, P, N, G)
+    dt = IP.step_size(dt_raw, inp["dt_bias"])
+    for b, g in ((nd, 0), (nd, 5), (nd + 1, 7)):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        slot = int(inp["state_idx"][b])
+        one = {k: v for k, v in inp.items() if k not in ("row", "dt_bias")}
+        one.update(xbc=xbc[lo:hi], z=z[lo:hi], dt=dt[lo:hi], cu_seqlens=np.array([0, hi - lo], np.int32),
+                   conv_state=inp["conv_state"][slot:slot + 1], ssm_state=inp["ssm_state"][slot:slot + 1],
+                   state_idx=np.zeros(1, np.int32), has_init=inp["has_init"][b:b + 1])
+        sub_inp, sub = slice_group(one, s, g)
+        r = R.prefill(sub_inp, sub.nheads, sub.headdim, sub.dstate, 1)
+        heads, xch, ch = group_channels(s, g)
+        ht, xt, ct = (torch.as_tensor(v, device="cuda") for v in (heads, xch, ch))
+        print(f" prefill seq {b} (slot {slot}) group {g}", flush=True)
+        assert rel_err(y[lo:hi][:, xt], r["y"], "y", (hi - lo) * len(xch)) <= tol
+        assert rel_err(d["ssm_state"][slot][ht], r["ssm_state"][0], "ssm_state") <= tol
+        assert rel_err(d["conv_state"][slot][:, ct], r["conv_state"][0], "conv_state") <= tol
