@@ -244,7 +244,9 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
 /*
  * mamba2_decode -- one new token for each of `batch` sequences, at their cache
  * slots: the conv update, the selective state update with its readout and the
- * grouped gated RMSNorm, in one fused kernel (page "NemotronH decodes on the
+ * grouped gated RMSNorm, in one fused kernel (for a small batch with an fp32
+ * y: the state update split over more workgroups, then one launch for the conv
+ * state and the norm) (page "NemotronH decodes on the
  * single-step recurrent kernels", PR description: decode rows take the
  * single-step conv update and state update at their slots, in place, with no
  * gather or scatter; page "Nemotron-H", section 4.1 for the recurrence and the

@@ -78,7 +78,13 @@ __device__ __forceinline__ int reduce_rows(float (&v)[KB], int lane) {
     return S;
 }
 
-template <int P, int N, typename Tin, typename Tout>
+// PART = false: the fused step, one workgroup per (sequence, group).
+// PART = true (a small batch): a.split workgroups per (sequence, group), each
+// taking a run of the group's heads: it convolves its heads' x channels and the
+// group's B and C from the OLD conv state (which it does not write), advances
+// its heads' SSM states and writes y before the norm (fp32) into y;
+// decode_finish_kernel then advances the conv state and applies the norm.
+template <int P, int N, typename Tin, typename Tout, bool PART>
 __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
     constexpr int RQ = N / 4;  // float4s per state row (head j, row p)
     constexpr int HS = ilog2(RQ) < ilog2(KB) ? ilog2(RQ) : ilog2(KB);
@@ -86,25 +92,29 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
     constexpr int WM = (RQ >> HS) - 1; // lanes with these bits zero write them
     static_assert(RQ <= 64 && NT % RQ == 0, "decode tile");
 
-    const int b = blockIdx.x / a.ngroups, g = blockIdx.x % a.ngroups;
+    const int S = PART ? a.split : 1;
+    const int b = blockIdx.x / (a.ngroups * S), g = (blockIdx.x / S) % a.ngroups;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hpg = a.nheads / a.ngroups;
     const int gw = hpg * P;
-    const int ch = gw + 2 * N;
+    // this workgroup's heads j0 .. j0+nh-1 of the group and their x channels
+    const int nh = hpg / S, j0 = (int)(blockIdx.x % S) * nh;
+    const int xw = nh * P, xoff = j0 * P;
+    const int ch = xw + 2 * N;
     const int d_x = a.nheads * P, d_b = a.ngroups * N;
     const int64_t conv_dim = d_x + 2 * d_b;
     const int slot = a.state_idx ? a.state_idx[b] : b;
     const bool init = a.has_init ? (a.has_init[b] != 0) : true;
 
     extern __shared__ float smem[];
-    float* sdx = smem;            // dt * x            [gw]
-    float* sxd = sdx + gw;        // D * x             [gw]
-    float* sy = sxd + gw;         // y before the norm [gw]
-    float* sg = sy + gw;          // SiLU(z)           [gw]
-    float* sw = sg + gw;          // norm weight       [gw]
-    float* sbc = sw + gw;         // post-conv B | C   [2N]
-    float* sdA = sbc + 2 * N;     // e(dt A) per head  [hpg]
-    float* red = sdA + hpg;       // [NT / 64]
+    float* sdx = smem;            // dt * x            [xw]
+    float* sxd = sdx + xw;        // D * x             [xw]
+    float* sy = sxd + xw;         // y before the norm [xw]
+    float* sg = sy + xw;          // SiLU(z)           [xw]
+    float* sw = sg + xw;          // norm weight       [xw]
+    float* sbc = sw + xw;         // post-conv B | C   [2N]
+    float* sdA = sbc + 2 * N;     // e(dt A) per head  [nh]
+    float* red = sdA + nh;        // [NT / 64]
 
     // Step size of head g*hpg + j: given in fp32, or softplus(raw + bias) of the
     // raw value in the activation type (the in-projection row's tail).
@@ -133,15 +143,15 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
             const int k = min(k0 + tid + NT * u, ch - 1);
             int64_t cg;
             const Tin* src;
-            if (k < gw) {
-                cg = (int64_t)g * gw + k;
+            if (k < xw) {
+                cg = (int64_t)g * gw + xoff + k;
                 src = static_cast<const Tin*>(a.x) + (int64_t)b * a.ld_x + cg;
-            } else if (k < gw + N) {
-                const int64_t n = (int64_t)g * N + (k - gw);
+            } else if (k < xw + N) {
+                const int64_t n = (int64_t)g * N + (k - xw);
                 cg = d_x + n;
                 src = static_cast<const Tin*>(a.B) + (int64_t)b * a.ld_B + n;
             } else {
-                const int64_t n = (int64_t)g * N + (k - gw - N);
+                const int64_t n = (int64_t)g * N + (k - xw - N);
                 cg = d_x + d_b + n;
                 src = static_cast<const Tin*>(a.C) + (int64_t)b * a.ld_C + n;
             }
@@ -152,11 +162,13 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
             xin[u] = Act<Tin>::load(src);
             w[u] = *reinterpret_cast<const f32x4_t*>(a.conv_w + cg * 4);
             cb[u] = (has_b ? a.conv_b : a.conv_w)[cg];
-            const int kx = min(k, gw - 1);
-            dtv[u] = step(kx / P);
-            dv[u] = Dg[kx / P];
-            zv[u] = Act<Tin>::load(zr + kx);
-            wv[u] = nw[kx];
+            const int kx = min(k, xw - 1);
+            dtv[u] = step(j0 + kx / P);
+            dv[u] = Dg[j0 + kx / P];
+            if constexpr (!PART) {
+                zv[u] = Act<Tin>::load(zr + kx);
+                wv[u] = nw[kx];
+            }
         }
 #pragma unroll
         for (int u = 0; u < CU; ++u) {
@@ -168,28 +180,32 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
             acc = fmaf(w[u][2], t2, acc);
             acc = fmaf(w[u][3], xin[u], acc);
             const float v = silu(acc);
-            if (k < gw) {
+            if (k < xw) {
                 sdx[k] = dtv[u] * v;
                 sxd[k] = has_d ? dv[u] * v : 0.f;
-                sg[k] = silu(zv[u]);
-                sw[k] = wv[u];
+                if constexpr (!PART) {
+                    sg[k] = silu(zv[u]);
+                    sw[k] = wv[u];
+                }
             } else if (k < ch) {
-                sbc[k - gw] = v;
+                sbc[k - xw] = v;
             }
-            if (k < ch) {
-                stp[u][0] = t1;
-                stp[u][conv_dim] = t2;
-                stp[u][2 * conv_dim] = xin[u];
+            if constexpr (!PART) {
+                if (k < ch) {
+                    stp[u][0] = t1;
+                    stp[u][conv_dim] = t2;
+                    stp[u][2 * conv_dim] = xin[u];
+                }
             }
         }
     }
-    for (int j = tid; j < hpg; j += NT) sdA[j] = expf(fminf(step(j) * Ag[j], 0.f));
+    for (int j = tid; j < nh; j += NT) sdA[j] = expf(fminf(step(j0 + j) * Ag[j0 + j], 0.f));
     __syncthreads();
 
     // 2. State update and readout over the group's state, a contiguous run of
     //    F float4s; thread t takes float4s base + t + NT k, k < KB, per batch.
-    const int F = hpg * P * RQ;
-    gf4 sp = (gf4)(a.ssm_state + ((int64_t)slot * a.nheads + (int64_t)g * hpg) * (P * N));
+    const int F = nh * P * RQ;
+    gf4 sp = (gf4)(a.ssm_state + ((int64_t)slot * a.nheads + (int64_t)g * hpg + j0) * (P * N));
     const int n0 = (tid % RQ) * 4;
     const f32x4_t Bq = *reinterpret_cast<const f32x4_t*>(sbc + n0);
     const f32x4_t Cq = *reinterpret_cast<const f32x4_t*>(sbc + N + n0);
@@ -204,7 +220,7 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const int f = base + tid + NT * k;
-            const int row = min(f / RQ, gw - 1);  // j * P + p
+            const int row = min(f / RQ, xw - 1);  // j * P + p of this workgroup's heads
             const float dA = sdA[row / P];
             const float dx = sdx[row];
             f32x4_t h = init ? v[k] : f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -221,7 +237,7 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < CF; ++i) {
                 const int row = (base + NT * (i + CF * S)) / RQ + tid / RQ;
-                if (row < gw) sy[row] = part[i] + sxd[row];
+                if (row < xw) sy[row] = part[i] + sxd[row];
             }
         }
     };
@@ -237,6 +253,11 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
         update_batch(buf1, base + NT * KB);
     }
     __syncthreads();
+    if constexpr (PART) {
+        float* yo = static_cast<float*>(a.y) + (int64_t)b * a.ld_y + (int64_t)g * gw + xoff;
+        for (int c = tid; c < xw; c += NT) yo[c] = sy[c];
+        return;
+    }
 
     // 3. Grouped gated RMSNorm over the group's gw channels.
     float ss = 0.f;
@@ -259,17 +280,107 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(DecodeArgs a) {
     }
 }
 
+// After the PART kernel: one workgroup per (sequence, group) advances the conv
+// state of the group's channels (the rows were read by every PART workgroup
+// before this launch) and applies the grouped gated RMSNorm to y in place.
+template <int P, int N, typename Tin>
+__global__ __launch_bounds__(NT) void decode_finish_kernel(DecodeArgs a) {
+    __shared__ float red[NT / 64];
+    const int b = blockIdx.x / a.ngroups, g = blockIdx.x % a.ngroups;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hpg = a.nheads / a.ngroups;
+    const int gw = hpg * P;
+    const int d_x = a.nheads * P, d_b = a.ngroups * N;
+    const int64_t conv_dim = d_x + 2 * d_b;
+    const int slot = a.state_idx ? a.state_idx[b] : b;
+    const bool init = a.has_init ? (a.has_init[b] != 0) : true;
+    for (int k = tid; k < gw + 2 * N; k += NT) {
+        int64_t cg;
+        const Tin* src;
+        if (k < gw) {
+            cg = (int64_t)g * gw + k;
+            src = static_cast<const Tin*>(a.x) + (int64_t)b * a.ld_x + cg;
+        } else if (k < gw + N) {
+            const int64_t n = (int64_t)g * N + (k - gw);
+            cg = d_x + n;
+            src = static_cast<const Tin*>(a.B) + (int64_t)b * a.ld_B + n;
+        } else {
+            const int64_t n = (int64_t)g * N + (k - gw - N);
+            cg = d_x + d_b + n;
+            src = static_cast<const Tin*>(a.C) + (int64_t)b * a.ld_C + n;
+        }
+        float* st = a.conv_state + (int64_t)slot * 3 * conv_dim + cg;
+        const float t1 = init ? st[conv_dim] : 0.f, t2 = init ? st[2 * conv_dim] : 0.f;
+        const float xin = Act<Tin>::load(src);
+        st[0] = t1;
+        st[conv_dim] = t2;
+        st[2 * conv_dim] = xin;
+    }
+    float* yo = static_cast<float*>(a.y) + (int64_t)b * a.ld_y + (int64_t)g * gw;
+    const Tin* zr = static_cast<const Tin*>(a.z) + (int64_t)b * a.ld_z + (int64_t)g * gw;
+    const float* nw = a.norm_w + (int64_t)g * gw;
+    constexpr int MAXC = MAXGW / NT;   // channels per thread
+    float yv[MAXC], gv[MAXC];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + NT * i;
+        yv[i] = c < gw ? yo[c] : 0.f;
+        gv[i] = c < gw ? silu(Act<Tin>::load(zr + c)) : 0.f;
+        const float v = a.norm_before_gate ? yv[i] : yv[i] * gv[i];
+        ss = fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) tot += red[k];
+    const float rstd = __builtin_amdgcn_rsqf(tot / (float)gw + a.eps);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + NT * i;
+        if (c < gw)
+            yo[c] = a.norm_before_gate ? yv[i] * rstd * nw[c] * gv[i] : yv[i] * gv[i] * rstd * nw[c];
+    }
+}
+
 size_t lds_bytes(int gw, int hpg, int N) { return sizeof(float) * (5 * (size_t)gw + 2 * N + hpg + NT / 64); }
 
-template <int P, int N, typename Tin>
-hipError_t launch_pn(const DecodeArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.batch * a.ngroups));
+// Workgroups per (sequence, group) for a small batch with an fp32 output: the
+// largest power of two dividing the heads per group that keeps the grid within
+// one workgroup per CU; 1 = the fused kernel.
+int decode_split(const DecodeArgs& a) {
+    if (a.y_dtype != kF32) return 1;
     const int hpg = a.nheads / a.ngroups;
+    const int64_t wgs = (int64_t)a.batch * a.ngroups;
+    int s = 1;
+    while (hpg % (2 * s) == 0 && wgs * 2 * s <= 256) s *= 2;
+    return s;
+}
+
+template <int P, int N, typename Tin>
+hipError_t launch_pn(const DecodeArgs& a0, hipStream_t stream) {
+    DecodeArgs a = a0;
+    a.split = decode_split(a0);
+    const int hpg = a.nheads / a.ngroups;
+    if (a.split > 1) {
+        const int nh = hpg / a.split;
+        hipLaunchKernelGGL((decode_step_kernel<P, N, Tin, float, true>), dim3((unsigned)(a.batch * a.ngroups * a.split)),
+                           dim3(NT), lds_bytes(nh * P, nh, N), stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((decode_finish_kernel<P, N, Tin>), dim3((unsigned)(a.batch * a.ngroups)), dim3(NT), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)(a.batch * a.ngroups));
     const size_t lds = lds_bytes(hpg * P, hpg, N);
     if (a.y_dtype == kBF16)
-        hipLaunchKernelGGL((decode_step_kernel<P, N, Tin, uint16_t>), grid, dim3(NT), lds, stream, a);
+        hipLaunchKernelGGL((decode_step_kernel<P, N, Tin, uint16_t, false>), grid, dim3(NT), lds, stream, a);
     else
-        hipLaunchKernelGGL((decode_step_kernel<P, N, Tin, float>), grid, dim3(NT), lds, stream, a);
+        hipLaunchKernelGGL((decode_step_kernel<P, N, Tin, float, false>), grid, dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 

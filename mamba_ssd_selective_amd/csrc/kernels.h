@@ -111,6 +111,7 @@ struct DecodeArgs {
     const uint8_t* has_init;    // or null
     int nheads, headdim, dstate, ngroups;
     void* y; int64_t ld_y; int y_dtype;
+    int split;                  // set by the launcher: workgroups per (sequence, group)
 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
