@@ -10,7 +10,8 @@
 // The conv is HBM-bound (4 multiply-adds per element read), so the kernel is a
 // streaming pass: a thread owns CPT = 4 adjacent channels (an 8-byte bf16 load,
 // a 16-byte fp32 one, one 16-byte store per fp32 output row) and a run of TOK
-// consecutive packed rows.  It issues the
+// consecutive packed rows (24; 8 when runs of 24 would leave most CUs idle, as
+// for a single short prompt).  It issues the
 // loads of the run's rows and 3-row halo first, then slides a window over
 // registers; a run that starts a sequence or crosses into another one goes row
 // by row instead, refilling the window from the slot's conv state (or zeros).
@@ -24,8 +25,9 @@
 namespace m2 {
 namespace {
 
-constexpr int TOK = 24;    // rows per thread
-constexpr int CPT = 4;     // channels per thread
+constexpr int TOK_LONG = 24;   // rows per thread
+constexpr int TOK_SHORT = 8;   // rows per thread when the grid would be small
+constexpr int CPT = 4;         // channels per thread
 constexpr int BLOCK = 128;
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int batch, int64_t t) {
@@ -125,7 +127,7 @@ __device__ __forceinline__ void store_out(double* p, const double (&v)[N]) {
 }
 
 // Computes in fp64 when the output is fp64 (the fp32-input prefill path), else fp32.
-template <typename Tin, typename Tout>
+template <typename Tin, typename Tout, int TOK>
 __global__ __launch_bounds__(BLOCK) void conv_rows_kernel(ConvArgs a) {
     using T = typename std::conditional<std::is_same<Tout, double>::value, double, float>::type;
     const BlockSeg bs = block_seg(a, blockIdx.y, BLOCK * CPT);
@@ -303,26 +305,33 @@ __global__ __launch_bounds__(BLOCK) void conv_state_kernel(ConvArgs a) {
 
 }  // namespace
 
-hipError_t launch_conv_rows(const ConvArgs& a, hipStream_t stream) {
+template <int TOK>
+hipError_t launch_rows(const ConvArgs& a, hipStream_t stream) {
     const int64_t tok_blocks = (a.total_tokens + TOK - 1) / TOK;
-    const int ch_blocks = conv_channel_blocks(a, BLOCK * CPT);
-    const dim3 grid((unsigned)tok_blocks, ch_blocks);
+    const dim3 grid((unsigned)tok_blocks, conv_channel_blocks(a, BLOCK * CPT));
     if (a.act_dtype == kBF16) {
         if (a.out_dtype == kBF16)
-            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
+            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, uint16_t, TOK>), grid, dim3(BLOCK), 0, stream, a);
         else if (a.out_dtype == kF64)
-            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, double>), grid, dim3(BLOCK), 0, stream, a);
+            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, double, TOK>), grid, dim3(BLOCK), 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, float>), grid, dim3(BLOCK), 0, stream, a);
+            hipLaunchKernelGGL((conv_rows_kernel<uint16_t, float, TOK>), grid, dim3(BLOCK), 0, stream, a);
     } else {
         if (a.out_dtype == kBF16)
-            hipLaunchKernelGGL((conv_rows_kernel<float, uint16_t>), grid, dim3(BLOCK), 0, stream, a);
+            hipLaunchKernelGGL((conv_rows_kernel<float, uint16_t, TOK>), grid, dim3(BLOCK), 0, stream, a);
         else if (a.out_dtype == kF64)
-            hipLaunchKernelGGL((conv_rows_kernel<float, double>), grid, dim3(BLOCK), 0, stream, a);
+            hipLaunchKernelGGL((conv_rows_kernel<float, double, TOK>), grid, dim3(BLOCK), 0, stream, a);
         else
-            hipLaunchKernelGGL((conv_rows_kernel<float, float>), grid, dim3(BLOCK), 0, stream, a);
+            hipLaunchKernelGGL((conv_rows_kernel<float, float, TOK>), grid, dim3(BLOCK), 0, stream, a);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_conv_rows(const ConvArgs& a, hipStream_t stream) {
+    // runs of 24 rows unless that leaves fewer workgroups than CUs
+    const int64_t long_blocks = (a.total_tokens + TOK_LONG - 1) / TOK_LONG;
+    if (long_blocks * conv_channel_blocks(a, BLOCK * CPT) < 256) return launch_rows<TOK_SHORT>(a, stream);
+    return launch_rows<TOK_LONG>(a, stream);
 }
 
 hipError_t launch_conv_state_update(const ConvArgs& a, hipStream_t stream) {
