@@ -24,7 +24,9 @@ Prints one JSON line on stdout (progress goes to stderr):
                   256-slot fp32 state pool, from packed rows (mamba2_decode_inproj:
                   the fused decode kernel, step size formed in it)
   mixed           a serving step: 256 decode rows then 2 prefill sequences of
-                  4096 tokens, from packed rows (mamba2_mixed_inproj)
+                  4096 tokens, from packed rows (mamba2_mixed_inproj); its
+                  roofline is the whole step's algorithmic bytes over its time,
+                  since the decode rows overlap the prefill chain
 """
 import argparse
 import json
@@ -467,12 +469,23 @@ def run_other_mode(args):
         from workloads import Workload
         wl = Workload("x", s, tuple(lens[nd:]), "bf16", "pool")
         kb = kernel_bytes(wl, T - nd, nseq - nd)
-        dom = max(kms, key=kms.get)
-        achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-                "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
-                "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
+        if mode == "mixed":
+            # the decode rows run on a second stream beside the prefill chain, so
+            # the chain's kernel times overlap them: the whole step is the unit
+            step_b = decode_bytes(s, nd, 2, dt_bytes=2) + sum(kb.values())
+            achieved = step_b / (ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "whole step (decode rows and prefill chain, overlapped)",
+                    "kernel_ms": round(ms, 4), "kernel_bytes": step_b,
+                    "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
+        else:
+            dom = max(kms, key=kms.get)
+            achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
+                    "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
         log("kernel ms/step (prefill chain): " + ", ".join(f"{k} {v:.3f}" for k, v in kms.items()))
         metric = "SSD prefill tokens/s per Mamba-2 layer @chunk128" if mode == "prefill_inproj" else \
             "Mixed decode+prefill step tokens/s per Mamba-2 layer @chunk128"

@@ -362,9 +362,11 @@ size_t mamba2_mixed_inproj_workspace_size(int64_t total_tokens, int batch, int m
  * exactly one row each, rows 0 .. num_decodes-1 (cu_seqlens[b] == b for
  * b <= num_decodes: a contract on device data, checked only with
  * M2SSD_DEBUG=1); sequences num_decodes .. batch-1 are prefills.  The decode
- * rows run the fused decode kernel, the prefill sequences the prefill chain,
- * both on `stream`; the result equals mamba2_prefill_inproj over the whole
- * batch up to rounding.  cu_seqlens, state_idx, has_init cover all `batch`
+ * rows run the decode kernel, the prefill sequences the prefill chain; when
+ * both are present the decode rows run on a second stream the library keeps
+ * per thread and device (default priority), forked from `stream` and joined
+ * back into it before the call's work is complete on `stream`; the result
+ * equals mamba2_prefill_inproj over the whole batch up to rounding.  cu_seqlens, state_idx, has_init cover all `batch`
  * sequences; state_idx NULL means slot b for sequence b (needs n_slots >= batch).
  * 0 <= num_decodes <= batch; workspace is required.
  */

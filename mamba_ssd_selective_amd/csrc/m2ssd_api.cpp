@@ -561,6 +561,35 @@ RowViews row_views(const void* row, int es, int nheads, int headdim, int dstate,
     return RowViews{r, r + di * es, r + 2 * di * es, r + (2 * di + gn) * es, r + (2 * di + 2 * gn) * es};
 }
 
+// A second stream for the decode rows of a mixed batch, so that they stream
+// their states while the prefill chain runs its latency-bound phases.  One per
+// thread and device, created on first use at the default priority (with the
+// fork / join events) and kept until the process ends; nullptr when it cannot
+// be made, and the decode rows then run on the caller's stream.
+struct SideStream {
+    hipStream_t s;
+    hipEvent_t fork, join;
+};
+SideStream* side_stream() {
+    thread_local std::vector<SideStream> sides;   // by device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+    if ((int)sides.size() <= dev) sides.resize(dev + 1, SideStream{nullptr, nullptr, nullptr});
+    SideStream& sd = sides[dev];
+    if (sd.s) return &sd;
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+        if (f) (void)hipEventDestroy(f);
+        (void)hipStreamDestroy(st);
+        return nullptr;
+    }
+    sd = SideStream{st, f, j};
+    return &sd;
+}
+
 int64_t row_width(int nheads, int headdim, int dstate, int ngroups) {
     return 2 * (int64_t)nheads * headdim + 2 * (int64_t)ngroups * dstate + nheads;
 }
@@ -765,11 +794,11 @@ int mamba2_mixed_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const
         Scope() { g_parts_of_checked_batch = true; }
         ~Scope() { g_parts_of_checked_batch = false; }
     } scope;
-    auto decode_part = [&](bool go) {
+    auto decode_part = [&](bool go, void* strm) {
         return decode_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w, eps,
                                  norm_before_gate, conv_state, ssm_state, n_slots, num_decodes,
                                  state_idx, has_init, nheads, headdim, dstate, ngroups, y, ld_y,
-                                 y_dtype, stream, go);
+                                 y_dtype, strm, go);
     };
     auto prefill_part = [&](bool go) {
         return prefill_inproj_run(row_p, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w, eps,
@@ -778,18 +807,33 @@ int mamba2_mixed_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const
                                   chunk_size, y_p, ld_y, y_dtype, pws, pws_bytes, stream, go);
     };
     int st;
-    if (num_decodes > 0 && (st = decode_part(false))) return st;
+    if (num_decodes > 0 && (st = decode_part(false, stream))) return st;
     if (np > 0 && (st = prefill_part(false))) return st;
-    if (num_decodes > 0 && (st = decode_part(true))) return st;
-    if (np > 0) {
-        if ((st = hip_status(m2::launch_rebase(cu_seqlens, num_decodes, np, (int32_t)tp, cu_p,
-                                               state_idx ? nullptr : slot_p,
-                                               static_cast<hipStream_t>(stream)),
-                             "mixed rebase launch")))
-            return st;
-        if ((st = prefill_part(true))) return st;
+    // The two parts touch disjoint rows, slots and workspace: with both present
+    // the decode rows go to the side stream, forked from and joined back into
+    // the caller's stream.
+    hipStream_t cs = static_cast<hipStream_t>(stream);
+    SideStream* sd = (num_decodes > 0 && np > 0) ? side_stream() : nullptr;
+    if (sd) {
+        if ((st = hip_status(hipEventRecord(sd->fork, cs), "mixed fork record"))) return st;
+        if ((st = hip_status(hipStreamWaitEvent(sd->s, sd->fork, 0), "mixed fork wait"))) return st;
+        if ((st = decode_part(true, sd->s))) return st;
+        if ((st = hip_status(hipEventRecord(sd->join, sd->s), "mixed join record"))) return st;
+    } else if (num_decodes > 0 && (st = decode_part(true, stream))) {
+        return st;
     }
-    return ok();
+    if (np > 0) {
+        st = hip_status(m2::launch_rebase(cu_seqlens, num_decodes, np, (int32_t)tp, cu_p,
+                                          state_idx ? nullptr : slot_p, cs),
+                        "mixed rebase launch");
+        if (!st) st = prefill_part(true);
+    }
+    // join even after a failed prefill launch, so the caller's stream never runs ahead
+    if (sd) {
+        const int sj = hip_status(hipStreamWaitEvent(cs, sd->join, 0), "mixed join wait");
+        if (!st) st = sj;
+    }
+    return st ? st : ok();
 }
 
 int m2_timing_enable(int max_calls) {
