@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD prefill tokens/s per Mamba-2 layer @chunk128; HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 WORKLOAD_ID = 2   # 8 x 4096 tokens, the Nemotron-nano layer shape
 
 
@@ -173,6 +174,42 @@ def scan_flops(w, T):
     return per_chunk * T / Q
 
 
+def scan_mfma_flops(w, lens):
+    """Executed matrix-core flops of the two scan kernels on the chunk-parallel path
+    when every sequence is a whole number of 128-row chunks (None otherwise), with
+    fp32 post-conv operands split in (hi, lo) bf16 pairs, 3 products each:
+      state pass   per (chunk, head): 4 waves x (dstate / 64) 32x32 tiles x 8 K
+                   blocks x 3 products of 32x32x16 (32,768 flop each)
+      chunk output per (chunk, group): C B^T over the causal 16x16 tiles, 36 tile
+                   columns x (dstate / 32) K blocks x 3, and per head 8 waves x
+                   (dstate / 32 x 4 p tiles x 3) for h_in C^T plus 12 x 20 for the
+                   causal X^T M^T, all 16x16x32 (16,384 flop each)
+    The counts match SQ_INSTS_MFMA on the 8 x 4096 workload."""
+    s = w.shape
+    if any(L % 128 for L in lens) or s.headdim != 64 or s.dstate != 128:
+        return None
+    chunks = sum(L // 128 for L in lens)
+    hpg = s.nheads // s.ngroups
+    kb = s.dstate // 32
+    state = chunks * s.nheads * 4 * (s.dstate // 64) * 8 * 3 * 32768
+    out = chunks * s.ngroups * (36 * kb * 3 + hpg * (8 * kb * 4 * 3 + 12 * 20)) * 16384
+    return state, out
+
+
+def mfma_line(w, lens, kms):
+    """Matrix-core utilisation of the scan kernels: executed bf16 MFMA flops over
+    kernel time and the 2.5 PFLOP/s dense bf16 peak (and algorithmic flops)."""
+    ex = scan_mfma_flops(w, lens)
+    if ex is None:
+        return None
+    sp, so = ex
+    t_sp, t_so = kms["scan_pass"] * 1e-3, kms["scan_out"] * 1e-3
+    return {"peak_tflops": MFMA_PEAK_TFLOPS,
+            "state_pass_exec_frac": round(sp / t_sp / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "chunk_out_exec_frac": round(so / t_so / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "scan_alg_frac": round(scan_flops(w, sum(lens)) / (t_sp + t_so) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +332,7 @@ def main():
             "step_bytes": fused_bytes(w, T, nseq),
             "step_frac": round(fused_bytes(w, T, nseq) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "scan_tflops_alg": round(scan_flops(w, T) / ((kms["scan_pass"] + kms["scan_out"]) * 1e-3) / 1e12, 2),
+            "mfma": mfma_line(w, lens, kms),
             "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
     out = {"metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
