@@ -209,3 +209,38 @@ def test_mixed_batch_full_size_sampled():
         assert rel_err(y[lo:hi][:, xt], r["y"], "y", (hi - lo) * len(xch)) <= tol
         assert rel_err(d["ssm_state"][slot][ht], r["ssm_state"][0], "ssm_state") <= tol
         assert rel_err(d["conv_state"][slot][:, ct], r["conv_state"][0], "conv_state") <= tol
+
+
+def test_mixed_batch_debug_checks(monkeypatch):
+    """With M2SSD_DEBUG=1 the host reads the index arrays before any launch: a
+    'decode' sequence of two rows and a repeated slot are refused with
+    M2_ERR_SHAPE and leave the states untouched; a valid batch still matches."""
+    monkeypatch.setenv("M2SSD_DEBUG", "1")
+    shape = LayerShape(4, 16, 16, 2)
+    H, P, N, G = shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    lens = [1, 1, 9, 20]
+    inp = inproj_inputs(shape, lens, seed=31, act="f32", init="pool", n_slots=6)
+
+    def call(d, nd, cu=None, idx=None):
+        return m2.mamba2_mixed_inproj(d["row"], d["dt_bias"], d["A"], d["D"], d["conv_w"], d["conv_b"],
+                                      d["norm_w"], d["conv_state"], d["ssm_state"],
+                                      d["cu_seqlens"] if cu is None else cu, nd, max(lens), H, P, N, G, 16,
+                                      d["state_idx"] if idx is None else idx, d["has_init"])
+
+    d = to_device(inp, "f32")
+    ss0, cs0 = d["ssm_state"].clone(), d["conv_state"].clone()
+    # sequence 1 declared a decode row but given two rows
+    bad_cu = tdev(np.array([0, 1, 3, 11, 31], np.int32), torch.int32)
+    with pytest.raises(m2.M2Error) as e:
+        call(d, 2, cu=bad_cu)
+    assert e.value.status == -2
+    rep = tdev(np.array([0, 1, 1, 2], np.int32), torch.int32)
+    with pytest.raises(m2.M2Error) as e:
+        call(d, 2, idx=rep)
+    assert e.value.status == -2
+    torch.cuda.synchronize()
+    assert torch.equal(d["ssm_state"], ss0) and torch.equal(d["conv_state"], cs0)
+    y = call(d, 2)
+    torch.cuda.synchronize()
+    ref = IP.mixed_batch(inp, 2, H, P, N, G)
+    compare(d, y, ref, shape, "f32", sum(lens))
