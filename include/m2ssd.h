@@ -39,7 +39,10 @@
  *   cu_seqlens[b+1]-1 of every token-indexed array.  cu_seqlens is int32
  *   [batch+1] in device memory, non-decreasing, cu_seqlens[0] == 0,
  *   cu_seqlens[batch] == total_tokens, and no sequence is longer than
- *   max_seqlen (a host value).  Empty sequences are allowed.
+ *   max_seqlen (a host value).  Empty sequences are allowed; with
+ *   total_tokens == 0 the token-indexed arrays (x, B, C, z, dt, y, the
+ *   in-projection rows) are not read and may be NULL, and the call only
+ *   resets the states of fresh slots (has_init == 0).
  * - Recurrent states live in caller pools indexed by slot:
  *     conv_state [n_slots, width-1, conv_dim] fp32, row j = the raw xBC input
  *       that is (width-1-j) steps older than the next new row (oldest first);

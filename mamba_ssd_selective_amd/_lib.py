@@ -120,6 +120,8 @@ def _rows(t: torch.Tensor, name: str) -> int:
     """Row stride (elements) of a 2-D tensor with unit inner stride on the GPU."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() == 2 and t.numel() == 0:
+        return t.size(1)   # no rows to read: any stride will do (torch may report 0)
     if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit inner stride")
     return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))

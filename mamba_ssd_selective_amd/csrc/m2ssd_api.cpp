@@ -124,8 +124,10 @@ int validate_conv(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
                   const float* conv_b, int width, float* conv_state, int n_slots,
                   const int32_t* cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
                   const int32_t* state_idx, const void* out, int64_t ld_out, int out_dtype) {
-    if (!x || !conv_w || !conv_state || !out) return fail(M2_ERR_NULL, "conv: x, conv_w, conv_state and out are required");
-    if (d_b > 0 && (!B || !C)) return fail(M2_ERR_NULL, "conv: B and C are required when d_b > 0");
+    const bool rows = total_tokens > 0;   // token-indexed arrays are read only when there are rows
+    if ((rows && (!x || !out)) || !conv_w || !conv_state)
+        return fail(M2_ERR_NULL, "conv: x, conv_w, conv_state and out are required");
+    if (rows && d_b > 0 && (!B || !C)) return fail(M2_ERR_NULL, "conv: B and C are required when d_b > 0");
     if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype)) return fail(M2_ERR_DTYPE, "conv: dtype must be M2_F32 or M2_BF16");
     if (width != 4) return fail(M2_ERR_UNSUPPORTED, "conv: width must be 4 (got %d)", width);
     if (d_x <= 0 || d_b < 0 || d_x % 8 || d_b % 8)
@@ -161,7 +163,7 @@ int validate_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
                   int nheads, int headdim, int dstate, int ngroups, int chunk_size,
                   const float* y, int64_t ld_y) {
     (void)D;
-    if (!x || !B || !C || !dt || !A || !ssm_state || !y)
+    if ((total_tokens > 0 && (!x || !B || !C || !dt || !y)) || !A || !ssm_state)
         return fail(M2_ERR_NULL, "scan: x, B, C, dt, A, ssm_state and y are required");
     if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "scan: act_dtype must be M2_F32 or M2_BF16");
     int st = validate_scan_dims(nheads, headdim, dstate, ngroups, chunk_size);
@@ -180,7 +182,8 @@ int validate_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
 int validate_norm(const float* y, int64_t ld_y, const void* z, int64_t ld_z, int z_dtype,
                   const float* norm_w, int ngroups, int64_t total_tokens, int d_inner,
                   const void* out, int64_t ld_out, int out_dtype) {
-    if (!y || !z || !norm_w || !out) return fail(M2_ERR_NULL, "norm: y, z, norm_w and out are required");
+    if ((total_tokens > 0 && (!y || !z || !out)) || !norm_w)
+        return fail(M2_ERR_NULL, "norm: y, z, norm_w and out are required");
     if (!valid_dtype(z_dtype) || !valid_dtype(out_dtype)) return fail(M2_ERR_DTYPE, "norm: dtype must be M2_F32 or M2_BF16");
     if (d_inner <= 0 || ngroups <= 0 || d_inner % ngroups || total_tokens < 0)
         return fail(M2_ERR_SHAPE, "norm: need d_inner > 0 divisible by ngroups > 0, total_tokens >= 0");
@@ -389,7 +392,7 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     if (st) return st;
     const int d_x = nheads * headdim, d_b = ngroups * dstate;
     const int conv_dim = d_x + 2 * d_b;
-    if (!z || !norm_w || !y) return fail(M2_ERR_NULL, "prefill: z, norm_w and y are required");
+    if ((total_tokens > 0 && (!z || !y)) || !norm_w) return fail(M2_ERR_NULL, "prefill: z, norm_w and y are required");
     if (!valid_dtype(y_dtype)) return fail(M2_ERR_DTYPE, "prefill: y_dtype must be M2_F32 or M2_BF16");
     if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "prefill: act_dtype must be M2_F32 or M2_BF16");
     const size_t need = mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads,
@@ -414,7 +417,7 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
                             conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
                             state_idx, u ? u : y, conv_dim, M2_F32)))
         return st;
-    if (!dt || !A || !ssm_state) return fail(M2_ERR_NULL, "prefill: dt, A and ssm_state are required");
+    if ((total_tokens > 0 && !dt) || !A || !ssm_state) return fail(M2_ERR_NULL, "prefill: dt, A and ssm_state are required");
     if (ld_dt < nheads) return fail(M2_ERR_STRIDE, "prefill: ld_dt < nheads");
     if (!aligned16(ssm_state)) return fail(M2_ERR_ALIGN, "prefill: ssm_state must be 16-byte aligned");
     if ((st = validate_norm(static_cast<const float*>(u ? u : y), d_x, z, ld_z, act_dtype, norm_w,
@@ -608,7 +611,7 @@ int prefill_inproj_run(const void* row, int64_t ld_row, int act_dtype, const flo
                        const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
                        int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
                        size_t ws_bytes, void* stream, bool launch) {
-    if (!row) return fail(M2_ERR_NULL, "prefill_inproj: the in-projection rows are required");
+    if (!row && total_tokens > 0) return fail(M2_ERR_NULL, "prefill_inproj: the in-projection rows are required");
     if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "prefill_inproj: act_dtype must be M2_F32 or M2_BF16");
     if (nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
         return fail(M2_ERR_SHAPE, "prefill_inproj: nheads, headdim, dstate, ngroups must be positive");
@@ -622,7 +625,8 @@ int prefill_inproj_run(const void* row, int64_t ld_row, int act_dtype, const flo
         return fail(M2_ERR_WORKSPACE, "prefill_inproj: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (!aligned16(workspace)) return fail(M2_ERR_ALIGN, "prefill_inproj: workspace must be 16-byte aligned");
     float* dt = reinterpret_cast<float*>(static_cast<char*>(workspace) + pws);
-    const RowViews v = row_views(row, elem_size(act_dtype), nheads, headdim, dstate, ngroups);
+    const RowViews v = row ? row_views(row, elem_size(act_dtype), nheads, headdim, dstate, ngroups)
+                           : RowViews{nullptr, nullptr, nullptr, nullptr, nullptr};
     auto chain = [&](bool go) {
         return prefill_run(v.x, ld_row, v.B, ld_row, v.C, ld_row, v.z, ld_row, act_dtype, dt, nheads,
                            A, D, conv_w, conv_b, norm_w, eps, norm_before_gate, conv_state,

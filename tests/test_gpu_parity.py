@@ -294,6 +294,41 @@ def test_prefill_long_sequences_split_into_segments(case):
     check_all(inp, shape, "bf16")
 
 
+def test_prefill_bf16_decay_stress_split_sequences():
+    """|dt A| log-uniform in [1e-3, 1e6] (5% at 1e6) on the bf16 chunk-parallel
+    path, with a sequence long enough to be split into segments: every clamped
+    exponent (in-chunk, chunk totals, segment totals, segment-relative decays)
+    must stay finite and the outputs match the oracle."""
+    shape = LayerShape(16, 64, 128, 2)
+    inp = small_shape_inputs(shape, [1500, 200], seed=71, act="bf16", init="random",
+                             dt_mode="stress")
+    check_all(inp, shape, "bf16")
+
+
+def test_prefill_all_sequences_empty():
+    """total_tokens = 0: no rows to convolve or scan; a fresh slot (has_init = 0)
+    is reset to zero states, a carried one is left as it was."""
+    shape = LayerShape(16, 64, 128, 2)
+    inp = small_shape_inputs(shape, [0, 0, 0], seed=72, act="bf16", init="pool", n_slots=5)
+    inp["has_init"] = np.array([0, 1, 0], dtype=np.uint8)
+    y, cs, ss = gpu_prefill(inp, shape, "bf16")
+    ref = oracle_prefill(inp, shape)
+    assert y.shape[0] == 0
+    fresh = [int(inp["state_idx"][b]) for b in (0, 2)]
+    assert float(ss[fresh].abs().max()) == 0.0 and float(cs[fresh].abs().max()) == 0.0
+    assert rel_err(ss, ref["ssm_state"], "ssm_state") == 0.0
+    assert rel_err(cs, ref["conv_state"], "conv_state") == 0.0
+
+
+def test_prefill_many_heads_per_group():
+    """32 heads per group: the widest norm group the library takes (32 x 64 =
+    2048 channels), 32-head loops in the scan kernels, and the head split of
+    the chunk output on a small grid."""
+    shape = LayerShape(64, 64, 128, 2)
+    inp = small_shape_inputs(shape, [300, 5], seed=73, act="bf16", init="random")
+    check_all(inp, shape, "bf16")
+
+
 def test_prefill_decay_stress_full_size():
     w = WORKLOADS[3]
     _sampled(w, 3, [(0, 0), (0, 7), (1, 3), (1, 4)], "f32")
