@@ -351,3 +351,38 @@ def test_varlen_batch_equals_per_sequence_runs():
         slot = inp["state_idx"][b]
         np.testing.assert_array_equal(o["ssm_state"][slot], full["ssm_state"][slot])
         np.testing.assert_array_equal(o["conv_state"][slot], full["conv_state"][slot])
+
+
+# ---------------------------------------------------------------- segment carry
+
+@pytest.mark.parametrize("cuts", [(7,), (5, 13), (1, 2, 20)])
+def test_segment_carry_identity(cuts):
+    """A sequence cut into segments, each later segment run from a zero state,
+    joined back: with E_k the segment's end state from its own start and
+    lambda_k = sum of dt*A over it, T_0 = E_0, T_k = exp(lambda_k) T_{k-1} + E_k
+    is the true end state, and the true outputs of segment k add
+    exp(sum of dt*A from the segment's start through t) * C_t . T_{k-1} to
+    the local ones.  This is the carry the state pass uses for long sequences
+    and the rank-level carry of a sequence split over devices."""
+    rng = np.random.default_rng(81)
+    L, H, P, N, G = 24, 4, 3, 5, 2
+    x, B, C, dt, A, D, h0 = _rand_scan_inputs(rng, L, H, P, N, G)
+    y_ref, h_ref = R.ssd_recurrence_seq(x, B, C, dt, A, D, h0)
+    grp = np.arange(H) // (H // G)
+    bounds = [0, *cuts, L]
+    T = None
+    y = np.zeros_like(y_ref)
+    for k in range(len(bounds) - 1):
+        lo, hi = bounds[k], bounds[k + 1]
+        start = h0 if k == 0 else np.zeros_like(h0)
+        yk, Ek = R.ssd_recurrence_seq(x[lo:hi], B[lo:hi], C[lo:hi], dt[lo:hi], A, D, start)
+        if k > 0:
+            a = dt[lo:hi] * A[None, :]                       # [S, H]
+            decay_t = np.exp(np.cumsum(a, axis=0))           # through row t, inclusive
+            inter = np.einsum("hpn,thn->thp", T, C[lo:hi][:, grp])
+            yk = yk + decay_t[:, :, None] * inter
+            Ek = np.exp(a.sum(axis=0))[:, None, None] * T + Ek
+        y[lo:hi] = yk
+        T = Ek
+    np.testing.assert_allclose(y, y_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(T, h_ref, rtol=1e-11, atol=1e-12)
