@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SSD prefill tokens/s per Mamba-2 layer @chunk128; HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
+FP64_PEAK_TFLOPS = 78.6     # fp64 matrix
 WORKLOAD_ID = 2   # 8 x 4096 tokens, the Nemotron-nano layer shape
 
 
@@ -113,6 +114,16 @@ def kernel_bytes(w, T, nseq):
     act = 2 if w.act == "bf16" else 4
     di, cd, gn = s.d_inner, s.conv_dim, s.ngroups * s.dstate
     state = s.nheads * s.headdim * s.dstate * 4
+    if w.act != "bf16":
+        # fp32 inputs: post-conv activations in fp64 and the one-pass scan, which
+        # reads x, B, C and dt and writes y with the state held on chip
+        return {
+            "conv": T * (cd * 4 + cd * 8),
+            "conv_state": nseq * 2 * 3 * cd * 4,
+            "scan_pass": T * (cd * 8 + s.nheads * 4 + di * 4) + nseq * 2 * state,
+            "scan_out": 0,
+            "norm": T * (di * 4 + di * act + di * 4),
+        }
     slots = T // w.chunk_size + nseq
     return {
         "conv": T * (cd * act + cd * 4),
@@ -186,7 +197,7 @@ def scan_mfma_flops(w, lens):
                    causal X^T M^T, all 16x16x32 (16,384 flop each)
     The counts match SQ_INSTS_MFMA on the 8 x 4096 workload."""
     s = w.shape
-    if any(L % 128 for L in lens) or s.headdim != 64 or s.dstate != 128:
+    if w.act != "bf16" or any(L % 128 for L in lens) or s.headdim != 64 or s.dstate != 128:
         return None
     chunks = sum(L // 128 for L in lens)
     hpg = s.nheads // s.ngroups
@@ -219,10 +230,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("prefill", "prefill_inproj", "decode", "mixed"),
                     default="prefill")
-    ap.add_argument("--workload", type=int, choices=(1, 2, 4), default=WORKLOAD_ID,
+    ap.add_argument("--workload", type=int, choices=(1, 2, 3, 4), default=WORKLOAD_ID,
                     help="prefill workload: 2 = 8 x 4096 nano (the headline), 1 = one 137-token "
-                         "nano prompt (a latency), 4 = 16 packed sequences of U[1, 8192] tokens "
-                         "at the 8B shape with states from a 64-slot pool")
+                         "nano prompt (a latency), 3 = 2 x 2048 fp32 decay stress (the fp64 "
+                         "path), 4 = 16 packed sequences of U[1, 8192] tokens at the 8B shape "
+                         "with states from a 64-slot pool")
     ap.add_argument("--print-sources-sha1", action="store_true",
                     help="print the sha1 of the prefill-chain and decode kernel sources and exit")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -324,19 +336,28 @@ def main():
 
     kb = kernel_bytes(w, T, nseq)
     dom = max(kms, key=kms.get)
-    achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, dom),
-            "kernel": dom,
+    if w.act == "bf16":
+        achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, dom)}
+    else:
+        # fp32 inputs: the one-pass scan on fp64 matrix instructions dominates,
+        # against the fp64 peak (algorithmic flops over its time)
+        achieved = scan_flops(w, T) / (kms["scan_pass"] * 1e-3) / 1e12
+        roof = {"bound": "fp64", "achieved": round(achieved, 2), "peak": FP64_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP64_PEAK_TFLOPS, 4), "traffic": None}
+        dom = "scan_pass"
+    roof.update({"kernel": dom,
             "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
             "step_bytes": fused_bytes(w, T, nseq),
             "step_frac": round(fused_bytes(w, T, nseq) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "scan_tflops_alg": round(scan_flops(w, T) / ((kms["scan_pass"] + kms["scan_out"]) * 1e-3) / 1e12, 2),
             "mfma": mfma_line(w, lens, kms),
-            "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}}
+            "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}})
     out = {"metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.act == "bf16" else "f64",
            "data": "synthetic",
            "config": {"workload": w.name, "batch": nseq,
                       "seq_len": lens[0] if len(set(lens)) == 1 else f"varlen {min(lens)}..{max(lens)}",
