@@ -22,6 +22,16 @@
 //              M^T[i, t] = G^T[i, t] dt_i e(gamma_t - gamma_i) (i <= t) and D on
 //              the diagonal, and stores y.
 //
+// Three choices depend on the batch's shape.  The state pass deals its
+// (sequence, group) pairs longest sequence first (seq_order_kernel ranks them),
+// so that long chunk walks never start last.  When the walks would fill fewer
+// workgroups than CUs, long sequences are split into segments: a segment after
+// the first starts from a zero state, segment_carry_kernel joins the segments
+// (T_k = e(lambda_k) T_{k-1} + E_k), and the chunk output adds
+// e(log decay since the segment's start) T_{k-1} to the local entry states of
+// the segment's later chunks.  And a chunk-output grid smaller than the CU
+// count splits each group's heads over several workgroups.
+//
 // Operands: x, B and C come as fp32 (the prefill's post-conv activations) or
 // as bf16 (given to the scan directly, then exact in bf16).  Every fp32 operand,
 // input or computed (dt-weighted x, M^T, h_in), is split as v = hi + lo (hi =
