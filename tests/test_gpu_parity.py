@@ -13,7 +13,7 @@ import torch
 
 import mamba_ssd_selective_amd as m2
 from oracle import recurrence as R
-from workloads import LayerShape, WORKLOADS, make_inputs, round_bf16, small_shape_inputs
+from workloads import LayerShape, Workload, WORKLOADS, make_inputs, round_bf16, small_shape_inputs
 from parity_util import TOL, group_channels, rel_err, slice_group, split_views, tdev, to_device
 
 pytestmark = pytest.mark.gpu
@@ -248,6 +248,12 @@ def _sampled(w, seed, pairs, act):
     s = w.shape
     y, cs, ss = gpu_prefill(inp, s, act, w.chunk_size)
     assert torch.isfinite(y).all() and torch.isfinite(ss).all() and torch.isfinite(cs).all()
+    _check_pairs(inp, s, y, cs, ss, pairs, act)
+
+
+def _check_pairs(inp, s, y, cs, ss, pairs, act):
+    """Each (sequence, group) pair of the device results against the oracle run
+    on that sequence's rows and that group alone."""
     cu = inp["cu_seqlens"]
     tol = TOL[act]
     for b, g in pairs:
@@ -342,6 +348,41 @@ def test_prefill_nano_8x4096_full_size_sampled():
 def test_prefill_h8b_varlen_full_size_sampled():
     w = WORKLOADS[4]
     _sampled(w, 4, [(0, 0), (2, 3), (12, 7)], "bf16")
+
+
+def test_prefill_offsets_past_4_gib():
+    """88 sequences of 4096 tokens at the 8 x 4096 layer shape (360,448 tokens):
+    the last sequence's xBC rows start 4.4 GB into the input, its y rows 5.8 GB
+    into the output, and its post-conv x blocks and entry states lie more than
+    4 GiB into the workspace, so every offset past 32 bits is taken.  The last
+    sequence is drawn by the workload generator and checked on two groups; the
+    others are filler drawn on the device (finite, their own slots)."""
+    s = WORKLOADS[2].shape
+    lens = [4096] * 88
+    last = len(lens) - 1
+    w = Workload("offsets", s, tuple(lens), "bf16", "random")
+    inp = make_inputs(w, 81, only_seq=last)      # token arrays of the last sequence only
+    cu = inp["cu_seqlens"]
+    T, lo, hi = int(cu[-1]), int(cu[last]), int(cu[last + 1])
+    assert lo * s.conv_dim * 2 > 2 ** 32 and lo * s.d_inner * 4 > 2 ** 32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(81)
+    xbc = torch.randn((T, s.conv_dim), generator=gen, device="cuda", dtype=torch.bfloat16)
+    z = torch.randn((T, s.d_inner), generator=gen, device="cuda", dtype=torch.bfloat16)
+    dt = torch.nn.functional.softplus(torch.randn((T, s.nheads), generator=gen, device="cuda") - 3.0)
+    xbc[lo:hi] = tdev(inp["xbc"][lo:hi], torch.bfloat16)
+    z[lo:hi] = tdev(inp["z"][lo:hi], torch.bfloat16)
+    dt[lo:hi] = tdev(inp["dt"][lo:hi])
+    d = {k: tdev(inp[k]) for k in ("A", "D", "conv_w", "conv_b", "norm_w", "conv_state", "ssm_state")}
+    x, B, C = split_views(xbc, s)
+    y = m2.mamba2_prefill(x, B, C, z, dt, d["A"], d["D"], d["conv_w"], d["conv_b"], d["norm_w"],
+                          d["conv_state"], d["ssm_state"], tdev(cu, torch.int32), 4096, s.nheads,
+                          s.headdim, s.dstate, s.ngroups, 128, tdev(inp["state_idx"], torch.int32),
+                          tdev(inp["has_init"], torch.uint8))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(d["ssm_state"]).all()
+    del xbc, z, dt
+    _check_pairs(inp, s, y, d["conv_state"], d["ssm_state"], [(last, 0), (last, 6)], "bf16")
 
 
 # ------------------------------------------------------------------ properties
