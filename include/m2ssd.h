@@ -61,6 +61,14 @@
  *   are not read by the host; violating their contracts gives unspecified
  *   results but never out-of-bounds access for cu_seqlens within
  *   [0, total_tokens] and state_idx within [0, n_slots).
+ * - Debug mode (environment variable M2SSD_DEBUG=1, read at every call): after
+ *   the argument checks and before any launch, the call copies its device
+ *   metadata to the host (synchronously) and returns M2_ERR_SHAPE, with no
+ *   side effects, for: cu_seqlens not starting at 0 and ending at
+ *   total_tokens, or a length outside [0, max_seqlen]; a state_idx entry
+ *   outside [0, n_slots) or repeated; an A entry above 0 or not finite; and,
+ *   where the entry takes the final step size (mamba2_prefill,
+ *   ssd_chunk_scan, mamba2_decode), a dt entry below 0 or not finite.
  * - Results are deterministic: equal inputs give bitwise-equal outputs.
  */
 #ifndef M2SSD_H

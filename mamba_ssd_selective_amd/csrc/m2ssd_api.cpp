@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -109,6 +110,32 @@ int check_batch(const int32_t* cu, int batch, int64_t total, int max_seqlen, con
     if (n_slots <= 0) return fail(M2_ERR_SHAPE, "n_slots must be positive");
     if (!idx && n_slots < batch) return fail(M2_ERR_SHAPE, "state_idx NULL needs n_slots >= batch");
     if (debug_enabled()) return debug_check_indices(cu, batch, total, max_seqlen, idx, n_slots);
+    return M2_OK;
+}
+
+// Debug check of the step sizes and decay rates the exponents are built from:
+// A finite and <= 0 for every head; dt (when given final, rows x nheads with
+// row stride ld_dt) finite and >= 0.  A decay rate above 0 or a negative step
+// would be clamped silently by the kernels.
+int debug_check_dt_A(const float* dt, int64_t ld_dt, int64_t rows, int nheads, const float* A) {
+    std::vector<float> hA(nheads);
+    if (hipMemcpy(hA.data(), A, sizeof(float) * nheads, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(M2_ERR_HIP, "debug: reading A failed");
+    for (int h = 0; h < nheads; ++h)
+        if (!(hA[h] <= 0.f) || !std::isfinite(hA[h]))
+            return fail(M2_ERR_SHAPE, "debug: A[%d]=%g must be finite and <= 0", h, (double)hA[h]);
+    if (!dt || rows <= 0) return M2_OK;
+    std::vector<float> hdt((size_t)rows * nheads);
+    if (hipMemcpy2D(hdt.data(), sizeof(float) * nheads, dt, sizeof(float) * ld_dt, sizeof(float) * nheads,
+                    (size_t)rows, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(M2_ERR_HIP, "debug: reading dt failed");
+    for (int64_t t = 0; t < rows; ++t)
+        for (int h = 0; h < nheads; ++h) {
+            const float v = hdt[(size_t)t * nheads + h];
+            if (!(v >= 0.f) || !std::isfinite(v))
+                return fail(M2_ERR_SHAPE, "debug: dt[%lld][%d]=%g must be finite and >= 0", (long long)t, h,
+                            (double)v);
+        }
     return M2_OK;
 }
 
@@ -317,6 +344,7 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
                            n_slots, cu_seqlens, batch, total_tokens, max_seqlen, state_idx, nheads,
                            headdim, dstate, ngroups, chunk_size, y, ld_y);
     if (st) return st;
+    if (debug_enabled() && (st = debug_check_dt_A(dt, ld_dt, total_tokens, nheads, A))) return st;
     const size_t need = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(M2_ERR_WORKSPACE, "scan: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
@@ -677,11 +705,18 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
                    const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
                    int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
                    size_t ws_bytes, void* stream) {
-    const int st = prefill_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, A, D, conv_w,
-                               conv_b, norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots,
-                               cu_seqlens, batch, total_tokens, max_seqlen, state_idx, has_init,
-                               nheads, headdim, dstate, ngroups, chunk_size, y, ld_y, y_dtype,
-                               workspace, ws_bytes, stream, true);
+    auto run = [&](bool launch) {
+        return prefill_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, A, D, conv_w, conv_b,
+                           norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots, cu_seqlens,
+                           batch, total_tokens, max_seqlen, state_idx, has_init, nheads, headdim,
+                           dstate, ngroups, chunk_size, y, ld_y, y_dtype, workspace, ws_bytes, stream,
+                           launch);
+    };
+    int st;
+    if (debug_enabled()) {  // the arguments are checked before dt and A are read
+        if ((st = run(false)) || (st = debug_check_dt_A(dt, ld_dt, total_tokens, nheads, A))) return st;
+    }
+    st = run(true);
     return st ? st : ok();
 }
 
@@ -692,10 +727,17 @@ int mamba2_decode(const void* x, int64_t ld_x, const void* B, int64_t ld_B, cons
                   float* conv_state, float* ssm_state, int n_slots, int batch,
                   const int32_t* state_idx, const uint8_t* has_init, int nheads, int headdim,
                   int dstate, int ngroups, void* y, int64_t ld_y, int y_dtype, void* stream) {
-    const int st = decode_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, 0, nullptr, A,
-                              D, conv_w, conv_b, norm_w, eps, norm_before_gate, conv_state,
-                              ssm_state, n_slots, batch, state_idx, has_init, nheads, headdim,
-                              dstate, ngroups, y, ld_y, y_dtype, stream, true);
+    auto run = [&](bool launch) {
+        return decode_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, 0, nullptr, A, D,
+                          conv_w, conv_b, norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots,
+                          batch, state_idx, has_init, nheads, headdim, dstate, ngroups, y, ld_y,
+                          y_dtype, stream, launch);
+    };
+    int st;
+    if (debug_enabled() && batch > 0) {
+        if ((st = run(false)) || (st = debug_check_dt_A(dt, ld_dt, batch, nheads, A))) return st;
+    }
+    st = run(true);
     return st ? st : ok();
 }
 
@@ -718,11 +760,18 @@ int mamba2_prefill_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, con
                           const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
                           int chunk_size, void* y, int64_t ld_y, int y_dtype, void* workspace,
                           size_t ws_bytes, void* stream) {
-    const int st = prefill_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b,
-                                      norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots,
-                                      cu_seqlens, batch, total_tokens, max_seqlen, state_idx,
-                                      has_init, nheads, headdim, dstate, ngroups, chunk_size, y,
-                                      ld_y, y_dtype, workspace, ws_bytes, stream, true);
+    auto run = [&](bool launch) {
+        return prefill_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w, eps,
+                                  norm_before_gate, conv_state, ssm_state, n_slots, cu_seqlens, batch,
+                                  total_tokens, max_seqlen, state_idx, has_init, nheads, headdim, dstate,
+                                  ngroups, chunk_size, y, ld_y, y_dtype, workspace, ws_bytes, stream,
+                                  launch);
+    };
+    int st;
+    if (debug_enabled()) {  // raw step sizes take any sign; A is checked
+        if ((st = run(false)) || (st = debug_check_dt_A(nullptr, 0, 0, nheads, A))) return st;
+    }
+    st = run(true);
     return st ? st : ok();
 }
 
@@ -732,10 +781,17 @@ int mamba2_decode_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, cons
                          float* ssm_state, int n_slots, int batch, const int32_t* state_idx,
                          const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
                          void* y, int64_t ld_y, int y_dtype, void* stream) {
-    const int st = decode_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w,
-                                     eps, norm_before_gate, conv_state, ssm_state, n_slots, batch,
-                                     state_idx, has_init, nheads, headdim, dstate, ngroups, y, ld_y,
-                                     y_dtype, stream, true);
+    auto run = [&](bool launch) {
+        return decode_inproj_run(zxbcdt, ld_row, act_dtype, dt_bias, A, D, conv_w, conv_b, norm_w, eps,
+                                 norm_before_gate, conv_state, ssm_state, n_slots, batch, state_idx,
+                                 has_init, nheads, headdim, dstate, ngroups, y, ld_y, y_dtype, stream,
+                                 launch);
+    };
+    int st;
+    if (debug_enabled() && batch > 0) {
+        if ((st = run(false)) || (st = debug_check_dt_A(nullptr, 0, 0, nheads, A))) return st;
+    }
+    st = run(true);
     return st ? st : ok();
 }
 
@@ -781,6 +837,7 @@ int mamba2_mixed_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const
             return fail(M2_ERR_HIP, "debug: reading cu_seqlens failed");
         for (int b = 0; b <= num_decodes; ++b)
             if (hcu[b] != b) return fail(M2_ERR_SHAPE, "debug: decode sequence %d is not one row at row %d", b, b);
+        if (A && (st = debug_check_dt_A(nullptr, 0, 0, nheads, A))) return st;
     }
     const int np = batch - num_decodes;
     const int64_t tp = total_tokens - num_decodes;

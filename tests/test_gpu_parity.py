@@ -415,6 +415,76 @@ def test_carried_state_matters():
     assert sep_y > 50 * TOL["bf16"]
 
 
+def test_debug_mode_rejects_bad_step_sizes_and_decays(monkeypatch):
+    """With M2SSD_DEBUG=1 the host reads dt and A before any launch: a negative
+    or NaN step size, or a positive decay rate, is refused with M2_ERR_SHAPE
+    and no state changes (prefill, scan alone, decode); the packed-row entries
+    take raw step sizes of any sign but still refuse a positive A; valid
+    inputs run and match the oracle."""
+    monkeypatch.setenv("M2SSD_DEBUG", "1")
+    shape = LayerShape(4, 16, 16, 2)
+    H, P, N, G = shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    inp = small_shape_inputs(shape, [9, 5], seed=74, act="f32", init="random")
+    d = to_device(inp, "f32")
+    x, B, C = split_views(d["xbc"], shape)
+    cs0, ss0 = d["conv_state"].clone(), d["ssm_state"].clone()
+
+    def prefill(dt, A):
+        return m2.mamba2_prefill(x, B, C, d["z"], dt, A, d["D"], d["conv_w"], d["conv_b"], d["norm_w"],
+                                 d["conv_state"], d["ssm_state"], d["cu_seqlens"], 9, H, P, N, G, 16,
+                                 d["state_idx"], d["has_init"])
+
+    def refused(fn, *args):
+        with pytest.raises(m2.M2Error) as e:
+            fn(*args)
+        assert e.value.status == -2, e.value
+        torch.cuda.synchronize()
+        assert torch.equal(d["conv_state"], cs0) and torch.equal(d["ssm_state"], ss0)
+
+    neg, nan, posA = d["dt"].clone(), d["dt"].clone(), d["A"].clone()
+    neg[11, 2] = -1e-3
+    nan[3, 0] = float("nan")
+    posA[1] = 0.5
+    refused(prefill, neg, d["A"])
+    refused(prefill, nan, d["A"])
+    refused(prefill, d["dt"], posA)
+    u = tdev(R.prefill(inp, H, P, N, G, apply_norm=False)["u"])
+    ux, uB, uC = split_views(u, shape)
+    refused(lambda: m2.ssd_chunk_scan(ux, uB, uC, neg, d["A"], d["D"], d["ssm_state"], d["cu_seqlens"], 9,
+                                      H, P, N, G, 16, d["state_idx"], d["has_init"]))
+    refused(lambda: m2.mamba2_decode(x[:2], B[:2], C[:2], d["z"][:2], neg[10:12], d["A"], d["D"],
+                                     d["conv_w"], d["conv_b"], d["norm_w"], d["conv_state"],
+                                     d["ssm_state"], H, P, N, G, d["state_idx"], d["has_init"]))
+    # packed rows: any raw step-size sign is valid, a positive A is not
+    from workloads import inproj_inputs
+    pinp = inproj_inputs(shape, [9, 5], seed=75, act="f32", init="pool", n_slots=4)
+    raw0 = shape.d_inner + shape.conv_dim
+    assert (pinp["row"][:, raw0:raw0 + H] < 0).any()
+    pd = {k: tdev(pinp[k]) for k in ("row", "dt_bias", "A", "D", "conv_w", "conv_b", "norm_w",
+                                     "conv_state", "ssm_state")}
+    pidx, pinit = tdev(pinp["state_idx"], torch.int32), tdev(pinp["has_init"], torch.uint8)
+    pcu = tdev(pinp["cu_seqlens"], torch.int32)
+
+    def packed(A):
+        return m2.mamba2_prefill_inproj(pd["row"], pd["dt_bias"], A, pd["D"], pd["conv_w"], pd["conv_b"],
+                                        pd["norm_w"], pd["conv_state"], pd["ssm_state"], pcu, 9, H, P, N,
+                                        G, 16, pidx, pinit)
+    pcs0, pss0 = pd["conv_state"].clone(), pd["ssm_state"].clone()
+    with pytest.raises(m2.M2Error) as e:
+        packed(posA)
+    assert e.value.status == -2
+    torch.cuda.synchronize()
+    assert torch.equal(pd["conv_state"], pcs0) and torch.equal(pd["ssm_state"], pss0)
+    packed(pd["A"])
+    torch.cuda.synchronize()
+    # valid split-view inputs still run, and match the oracle
+    y = prefill(d["dt"], d["A"])
+    torch.cuda.synchronize()
+    ref = oracle_prefill(inp, shape)
+    assert rel_err(y, ref["y"], "y", 14 * shape.d_inner) <= TOL["f32"]
+    assert rel_err(d["ssm_state"], ref["ssm_state"], "ssm_state") <= TOL["f32"]
+
+
 def test_argument_errors_raise():
     shape = LayerShape(4, 16, 16, 2)
     inp = small_shape_inputs(shape, [8], seed=70, act="f32", init="zero")
