@@ -8,7 +8,9 @@ unnoticed.  The mutations are those a port of this method typically makes:
   3. the carry dropped (every call starts from a zero SSM state);
   4. the conv state shifted by one row;
   5. the gate order swapped;
-  6. the chunk treated as dense (the causal predicate dropped).
+  6. the chunk treated as dense (the causal predicate dropped);
+  7. (in-projection rows) the dt bias dropped, softplus confused with e^v or
+     with log(1 + e^-v), and the row read in the wrong order.
 
 Each mutant wraps or replaces one oracle function through monkeypatch; the
 pins are the functions of test_oracle_pins, called as they are.
@@ -132,3 +134,53 @@ def test_unmutated_pins_pass():
                  (PINS.test_norm_single_group_matches_torch_rms_norm, (True,)),
                  (PINS.test_golden_gated_norm, ()),
                  (PINS.test_recurrence_equals_chunk_form, (4, 2, 7))]) == 0
+
+
+# ------------------------------------------------------------------ in-projection rows
+#
+# Planted mistakes in oracle.inproj, each caught by the pins of
+# test_oracle_inproj_pins: the dt bias dropped, softplus confused with e^v or
+# with its mirror log(1 + e^-v), and the row read in the wrong order (xBC
+# before z, or the raw step size taken from the head of the row).
+
+import test_oracle_inproj_pins as IPINS
+from oracle import inproj as IP
+
+INPROJ_PINS = [(IPINS.test_softplus_closed_forms, ()),
+               (IPINS.test_step_size_inverts_and_biases_per_head, ()),
+               (IPINS.test_split_takes_head_middle_tail_of_the_row, ()),
+               (IPINS.test_packed_prefill_equals_prefill_of_the_pieces, (True,)),
+               (IPINS.test_mixed_batch_is_independent_sequences_with_decodes_first, ())]
+
+
+def test_inproj_mutation_bias_dropped(monkeypatch):
+    monkeypatch.setattr(IP, "step_size", lambda raw, bias: IP.softplus(np.asarray(raw, np.float64)))
+    assert _red(INPROJ_PINS) >= 2
+
+
+@pytest.mark.parametrize("wrong", ["exp", "mirror"])
+def test_inproj_mutation_softplus(monkeypatch, wrong):
+    real = IP.softplus
+    fn = (lambda v: np.exp(np.minimum(np.asarray(v, np.float64), 700.0))) if wrong == "exp" \
+        else (lambda v: real(-np.asarray(v, np.float64)))
+    monkeypatch.setattr(IP, "softplus", fn)
+    with np.errstate(over="ignore", invalid="ignore"):
+        assert _red(INPROJ_PINS) >= 2
+
+
+@pytest.mark.parametrize("order", ["xbc_first", "dt_at_head"])
+def test_inproj_mutation_row_order(monkeypatch, order):
+    def mutant(row, nheads, headdim, dstate, ngroups):
+        di = nheads * headdim
+        cd = di + 2 * ngroups * dstate
+        if row.shape[1] < di + cd + nheads:
+            raise ValueError("in-projection row narrower than z | xBC | dt")
+        if order == "xbc_first":
+            return row[:, cd:cd + di], row[:, :cd], row[:, di + cd:di + cd + nheads]
+        return row[:, nheads:nheads + di], row[:, nheads + di:nheads + di + cd], row[:, :nheads]
+    monkeypatch.setattr(IP, "split_inproj_row", mutant)
+    assert _red(INPROJ_PINS) >= 2
+
+
+def test_inproj_unmutated_pins_pass():
+    assert _red(INPROJ_PINS) == 0
