@@ -177,7 +177,12 @@ int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
  *   other bf16 shapes (one-pass path): every fp32 operand split into a (high,
  *     low) bf16 pair, three products per tile, fp32 accumulation; no workspace.
  *   fp32 inputs: computed in fp64 (fp64 matrix instructions, chunks evaluated
- *     64 rows at a time -- the same function of the inputs); no workspace.
+ *     64 rows at a time -- the same function of the inputs).  With fewer than
+ *     256 (sequence, head) pairs, long sequences are split into segments that
+ *     run in parallel from a zero state; a carry pass joins their end states
+ *     (the recurrence is linear in its state) and adds the carried-in state's
+ *     readout to the later segments' rows.  The workspace holds one fp64 state
+ *     and one fp64 log decay per (segment, sequence, head).
  * Cumulative sums and exponent differences are fp64 on every path.
  */
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
@@ -194,8 +199,10 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
  * shape runs on a path without workspace, or on bad arguments): on the
  * chunk-parallel path the state entering every chunk, (total_tokens/128 +
  * batch) * nheads * headdim * dstate * 4 bytes, then the order in which the
- * sequences' carries are dealt out (batch int32), each part rounded up to
- * 256 bytes.
+ * sequences' carries are dealt out (batch int32), then the buffers of long
+ * sequences split into segments; for fp32 inputs with items = batch * nheads
+ * below 256, ceil(256 / items) * items fp64 states of headdim * dstate and as
+ * many fp64 log decays; each part rounded up to 256 bytes.
  */
 size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads, int headdim,
                                      int dstate, int ngroups, int chunk_size, int act_dtype);
@@ -221,7 +228,7 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
  * activation dtype (0 on bad arguments).  The workspace holds the post-conv
  * activations of the batch (fp32 for bf16 inputs, fp64 for fp32 inputs; on the
  * chunk-parallel scan path blocked per head and per group), the fp32 pre-norm
- * output and, on the chunk-parallel scan path, the state entering every chunk.
+ * output and the scan's own workspace (ssd_chunk_scan_workspace_size()).
  */
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
                                      int nheads, int headdim, int dstate, int ngroups,

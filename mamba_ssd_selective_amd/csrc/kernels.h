@@ -70,6 +70,11 @@ struct ScanArgs {
     double* cum;                // per (chunk slot, head): log decay from its segment's start
     float* seg_end;             // [batch * nheads] local end states of last segments
     int out_split;              // chunk output: workgroups per (chunk, group), each a run of heads
+    // One-pass fp64 path, few long sequences split into segments of `seg` steps
+    // (seg_levels of them at most; lam holds each segment's total log decay):
+    // per (segment, sequence, head) the local end state, then the true one
+    // after the carry, P x N fp64 each.
+    double* seg_state;
 };
 
 struct NormArgs {
@@ -136,6 +141,13 @@ hipError_t launch_rebase(const int32_t* cu, int first, int count, int32_t rows, 
 
 // True when a scan kernel is compiled for this (headdim, dstate).
 bool scan_supported(int headdim, int dstate);
+// One-pass fp64 path (ssd_scan.hip): workspace bytes for splitting few long
+// sequences into segments (0 when the policy or the item count never splits),
+// and the split itself: sets a.seg, a.seg_levels, a.seg_state and a.lam from
+// the longest sequence, with ws (at least one_pass_seg_bytes) behind them; no
+// split without ws.
+size_t one_pass_seg_bytes(int batch, int nheads, int headdim, int dstate, int policy);
+void one_pass_plan(ScanArgs& a, int max_seqlen, void* ws);
 
 // Chunk-parallel scan (ssd_chunked.hip) for PolicyBf16x3 (x/B/C stored as bf16
 // or fp32), headdim 64, dstate 64 or 128, chunk 128, at most 256 heads per group.  The state pass writes the entry state of every chunk to

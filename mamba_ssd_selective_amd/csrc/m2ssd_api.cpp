@@ -248,6 +248,17 @@ size_t scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdi
     return m2::chunked_scan_states_bytes(total_tokens, batch, nheads, headdim, dstate);
 }
 
+// The scan's whole workspace: the chunk-parallel path's buffers, or the
+// one-pass fp64 path's segment buffers (0 for paths that need none).
+size_t scan_ws_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate, int ngroups,
+                     int chunk_size, int act_dtype) {
+    const size_t chunked = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups,
+                                             chunk_size, act_dtype);
+    if (chunked > 0) return chunked;
+    const int policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
+    return m2::one_pass_seg_bytes(batch, nheads, headdim, dstate, policy);
+}
+
 // Row-major conv output: segment s starts at its channel offset within each row.
 void set_rowmajor_out(m2::ConvArgs& a, void* out, int64_t ld_out, int elt) {
     int64_t c = 0;
@@ -330,7 +341,7 @@ size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads
     if (total_tokens < 0 || batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
         ngroups <= 0 || !valid_dtype(act_dtype))
         return 0;
-    return scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
+    return scan_ws_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
@@ -345,7 +356,8 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
                            headdim, dstate, ngroups, chunk_size, y, ld_y);
     if (st) return st;
     if (debug_enabled() && (st = debug_check_dt_A(dt, ld_dt, total_tokens, nheads, A))) return st;
-    const size_t need = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
+    const size_t chunked_need = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
+    const size_t need = scan_ws_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(M2_ERR_WORKSPACE, "scan: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (need > 0 && !aligned16(workspace)) return fail(M2_ERR_ALIGN, "scan: workspace must be 16-byte aligned");
@@ -358,9 +370,10 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     a.cu_seqlens = cu_seqlens; a.batch = batch; a.state_idx = state_idx; a.has_init = has_init;
     a.nheads = nheads; a.headdim = headdim; a.dstate = dstate; a.ngroups = ngroups;
     a.chunk = chunk_size; a.y = y; a.ld_y = ld_y;
-    a.states = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.states = chunked_need > 0 ? static_cast<float*>(workspace) : nullptr;
     a.order = a.states ? m2::chunked_scan_order(a.states, total_tokens, batch, nheads, headdim, dstate) : nullptr;
     if (a.states) m2::chunked_scan_plan(a, total_tokens, max_seqlen);
+    else m2::one_pass_plan(a, max_seqlen, need > 0 ? workspace : nullptr);
     if (batch == 1) a.order = nullptr;  // one sequence: no order to compute
     if ((st = launch_scan(a, total_tokens, static_cast<hipStream_t>(stream), nullptr))) return st;
     return ok();
@@ -397,7 +410,7 @@ size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_se
     // pre-norm output (fp32; used when y is not fp32) and the scan's entry states
     const int64_t ues = act_dtype == M2_BF16 ? 4 : 8;
     return (size_t)(round256(total_tokens * conv_dim * ues) + round256(total_tokens * di * 4)) +
-           scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
+           scan_ws_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
 }  // extern "C"
@@ -441,6 +454,10 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     float* ypre_ws = wsb ? reinterpret_cast<float*>(wsb + u_bytes) : nullptr;
     const bool chunked = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype) > 0;
     float* states_ws = (wsb && chunked) ? reinterpret_cast<float*>(wsb + u_bytes + ypre_bytes) : nullptr;
+    // one-pass path: its segment buffers (if any) take the same place
+    void* seg_ws = (wsb && !chunked &&
+                    scan_ws_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype) > 0)
+                       ? static_cast<void*>(wsb + u_bytes + ypre_bytes) : nullptr;
     if ((st = validate_conv(x, ld_x, B, ld_B, C, ld_C, d_x, d_b, act_dtype, conv_w, conv_b, 4,
                             conv_state, n_slots, cu_seqlens, batch, total_tokens, max_seqlen,
                             state_idx, u ? u : y, conv_dim, M2_F32)))
@@ -509,6 +526,7 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     sa.states = states_ws;
     sa.order = states_ws ? m2::chunked_scan_order(states_ws, total_tokens, batch, nheads, headdim, dstate) : nullptr;
     if (states_ws) m2::chunked_scan_plan(sa, total_tokens, max_seqlen);
+    else m2::one_pass_plan(sa, max_seqlen, seg_ws);
     if (batch == 1) sa.order = nullptr;  // one sequence: no order to compute
     if ((st = launch_scan(sa, total_tokens, s, tev ? tev[3] : nullptr))) return st;
     mark(4);

@@ -113,10 +113,19 @@ def test_scan_workspace_query():
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 1) == expect(1000, 3)
     assert lib.ssd_chunk_scan_workspace_size(4096 * 8, 8, 64, 64, 128, 8, 128, 1) == expect(4096 * 8, 8)
     assert lib.ssd_chunk_scan_workspace_size(1000, 100, 64, 64, 128, 8, 128, 1) == expect(1000, 100)
-    # paths without workspace: fp32 inputs, other chunk sizes, other shapes
-    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 0) == 0
+    # bf16 paths without workspace: other chunk sizes, other shapes
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 64, 1) == 0
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 8, 32, 64, 2, 128, 1) == 0
+    # fp32 inputs (the one-pass fp64 path): with fewer than 256 (sequence, head)
+    # items, room for ceil(256 / items) segments per item, an fp64 P x N state
+    # and an fp64 log decay each; none from 256 items on
+    def expect_f64(b, H, P, N):
+        items = b * H
+        nseg = -(-256 // items)
+        return r(nseg * items * P * N * 8) + r(nseg * items * 8)
+    assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 0) == expect_f64(3, 64, 64, 128)
+    assert lib.ssd_chunk_scan_workspace_size(11, 1, 4, 16, 16, 2, 16, 0) == expect_f64(1, 4, 16, 16)
+    assert lib.ssd_chunk_scan_workspace_size(1000, 4, 64, 64, 128, 8, 128, 0) == 0
     # the prefill workspace includes it, plus fp32 activations and the fp32 pre-norm output
     n = lib.mamba2_prefill_workspace_size(1000, 3, 1000, 64, 64, 128, 8, 128, 1)
     assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4 + (1000 // 128 + 3) * per_slot

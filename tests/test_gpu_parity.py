@@ -290,14 +290,18 @@ SEGMENT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
 @pytest.mark.parametrize("case", range(len(SEGMENT_CASES)))
-def test_prefill_long_sequences_split_into_segments(case):
+def test_prefill_long_sequences_split_into_segments(case, act):
+    """bf16: the chunk-parallel path's segments; f32: the fp64 one-pass path's
+    (segments of 64-row steps, the carry kernel and the readout fix of later
+    segments)."""
     shape, lens, init = SEGMENT_CASES[case]
-    inp = small_shape_inputs(shape, lens, seed=60 + case, act="bf16", init="pool",
+    inp = small_shape_inputs(shape, lens, seed=60 + case, act=act, init="pool",
                              n_slots=len(lens) + 3)
     inp["has_init"] = np.array(init, dtype=np.uint8)
     print(f" shape={shape} lens={lens} slots={inp['state_idx'].tolist()}")
-    check_all(inp, shape, "bf16")
+    check_all(inp, shape, act)
 
 
 def test_prefill_bf16_decay_stress_split_sequences():

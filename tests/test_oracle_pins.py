@@ -362,8 +362,9 @@ def test_segment_carry_identity(cuts):
     lambda_k = sum of dt*A over it, T_0 = E_0, T_k = exp(lambda_k) T_{k-1} + E_k
     is the true end state, and the true outputs of segment k add
     exp(sum of dt*A from the segment's start through t) * C_t . T_{k-1} to
-    the local ones.  This is the carry the state pass uses for long sequences
-    and the rank-level carry of a sequence split over devices."""
+    the local ones.  This is the carry both scan paths use for long sequences
+    (the bf16 state pass, and the fp64 one-pass path with its readout fix) and
+    the rank-level carry of a sequence split over devices."""
     rng = np.random.default_rng(81)
     L, H, P, N, G = 24, 4, 3, 5, 2
     x, B, C, dt, A, D, h0 = _rand_scan_inputs(rng, L, H, P, N, G)
