@@ -820,7 +820,18 @@ size_t mamba2_mixed_inproj_workspace_size(int64_t total_tokens, int batch, int m
                                                             headdim, dstate, ngroups, chunk_size,
                                                             act_dtype);
     if (pws == 0) return 0;
-    return (size_t)(round256((int64_t)(batch + 1) * 4) + round256((int64_t)batch * 4)) + pws;
+    // The prefill part is a sub-batch of batch - num_decodes sequences, and the
+    // fp64 path's segment buffers do not grow with the batch (a smaller batch
+    // can be split where a larger one is not): room for the largest of them.
+    size_t seg_any = 0;
+    if (act_dtype == M2_F32 && scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups,
+                                                 chunk_size, act_dtype) == 0) {
+        for (int b = 1; b <= batch && (int64_t)b * nheads < 256; ++b) {
+            const size_t v = m2::one_pass_seg_bytes(b, nheads, headdim, dstate, m2::kPolicyF64);
+            if (v > seg_any) seg_any = v;
+        }
+    }
+    return (size_t)(round256((int64_t)(batch + 1) * 4) + round256((int64_t)batch * 4)) + pws + seg_any;
 }
 
 int mamba2_mixed_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, const float* dt_bias,

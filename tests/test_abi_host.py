@@ -259,3 +259,18 @@ def test_mixed_inproj_rejects_bad_arguments(kw, code):
     lib = m2.load()
     assert _mixed(lib, **kw) == code
     assert lib.m2_last_error().decode() != ""
+
+
+def test_mixed_workspace_covers_every_prefill_part():
+    """The mixed entry hands its prefill part (batch - num_decodes sequences)
+    the rest of its workspace; for fp32 inputs the one-pass path's segment
+    buffers do not grow with the batch (a smaller batch can be split where a
+    larger one is not), so the mixed size must cover every sub-batch."""
+    lib = m2.load()
+    for (H, P, N, G) in ((64, 64, 128, 8), (4, 16, 16, 2), (24, 32, 64, 2)):
+        for batch in (1, 3, 5, 8, 40):
+            T = 64 * batch + 4000
+            mixed = lib.mamba2_mixed_inproj_workspace_size(T, batch, 4000, H, P, N, G, 128, 0)
+            for nd in range(batch):
+                part = lib.mamba2_prefill_inproj_workspace_size(T - nd, batch - nd, 4000, H, P, N, G, 128, 0)
+                assert mixed - 2 * ((4 * (batch + 1) + 255) // 256 * 256) >= part, (H, batch, nd)

@@ -118,6 +118,9 @@ MIXED_CASES = [
     (LayerShape(16, 64, 128, 2), [1, 1, 1, 1], 4, "bf16", 128, 4, [1, 1, 1, 0]),   # decode only
     (LayerShape(16, 64, 128, 2), [33, 1, 200], 0, "bf16", 128, 3, [1, 0, 1]),     # prefill only
     (NANO, [1] * 16 + [300, 129, 1], 16, "bf16", 128, 40, None),
+    # fp32: 20 sequences x 16 heads would not be split, but the prefill part's
+    # 2 x 16 are, so its segment buffers come from the mixed workspace
+    (LayerShape(16, 64, 128, 2), [1] * 18 + [1300, 700], 18, "f32", 128, 24, None),
 ]
 
 
