@@ -364,7 +364,9 @@ int mamba2_decode_inproj(const void* zxbcdt, int64_t ld_row, int act_dtype, cons
 /*
  * Bytes of device workspace mamba2_mixed_inproj needs (0 on bad arguments):
  * mamba2_prefill_inproj_workspace_size() for the whole batch plus the prefill
- * part's row offsets and slot map.
+ * part's row offsets and slot map, and for fp32 inputs room for the segment
+ * buffers of any smaller prefill part (a sub-batch can be split into segments
+ * where the whole batch would not be).
  */
 size_t mamba2_mixed_inproj_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
                                           int nheads, int headdim, int dstate, int ngroups,
