@@ -29,7 +29,9 @@
 //   6. y rows of the chunk are stored; after the last chunk the state is stored.
 // Matrix products use PolicyBf16x3 (bf16 inputs; fp32 values, 128-row chunks)
 // or PolicyF64 (fp32 inputs; fp64 values, chunks evaluated 64 rows at a time,
-// which is the same function of the inputs).
+// which is the same function of the inputs).  On the fp64 path, few long
+// sequences are split into segments walked by separate workgroups and joined
+// afterwards (see the segment kernels below).
 
 #include "device_common.h"
 #include "kernels.h"
