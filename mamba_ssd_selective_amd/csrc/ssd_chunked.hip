@@ -259,14 +259,16 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     constexpr int BG = QH / TB, XG = QH / TX;          // token groups
     constexpr int BC = N / CPL;                        // B channel groups
     static_assert(TB >= 2 && TX >= 2, "staging pieces");
-    __shared__ __align__(16) u16 BTh[N * RH];           // B^T [n][token of the half], high parts
-    __shared__ __align__(16) u16 BTl[SP ? N * RH : 8];  // low parts (fp32 inputs)
-    __shared__ __align__(16) u16 sXH[IPW][P * RH];      // (w x)^T [p][token] per item, high parts
-    __shared__ __align__(16) u16 sXL[IPW][P * RH];      // low parts
+    // Two items per workgroup (one per CU anyway) keep a tile set per half,
+    // so one barrier per half suffices; one item keeps one set (two
+    // workgroups then share a CU).
+    constexpr int NB = IPW == 2 ? 2 : 1;
+    __shared__ __align__(16) u16 sBTh[NB][N * RH];           // B^T [n][token of the half], high parts
+    __shared__ __align__(16) u16 sBTl[NB][SP ? N * RH : 8];  // low parts (fp32 inputs)
+    __shared__ __align__(16) u16 sXH[NB][IPW][P * RH];       // (w x)^T [p][token] per item, high parts
+    __shared__ __align__(16) u16 sXL[NB][IPW][P * RH];       // low parts
 
     const int sub = IPW > 1 ? (int)(threadIdx.x >> 8) : 0;   // item within the workgroup
-    u16* const XH = sXH[sub];
-    u16* const XL = sXL[sub];
     const int tid = threadIdx.x & (NT - 1);
     const int wave = tid >> 6, lane = tid & 63;
     const int gwave = (int)(threadIdx.x >> 6);                // wave within the workgroup
@@ -365,6 +367,10 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     // Rows past the sequence's end hold re-read (finite) rows and have weight 0
     // (dt is zeroed there), so their (w x) is 0 and they add nothing; no mask.
     auto stage = [&](HalfBuf<Tin, TB, TX>& b, int h, float w0, float w1) __attribute__((always_inline)) {
+        u16* const BTh = sBTh[h % NB];
+        u16* const BTl = sBTl[h % NB];
+        u16* const XH = sXH[h % NB][sub];
+        u16* const XL = sXL[h % NB][sub];
         // B^T: channel CPL b_cg + j, tokens TB b_tg ..
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -403,7 +409,11 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
 
     // h^T += B^T (w x) over the 16-row K blocks of a staged half (32x32x16: an
     // operand lane supplies row (or column) l % 32 and K slots 8 (l / 32) .. + 7)
-    auto multiply = [&](int nkb) __attribute__((always_inline)) {
+    auto multiply = [&](int nkb, int h) __attribute__((always_inline)) {
+        const u16* const BTh = sBTh[h % NB];
+        const u16* const BTl = sBTl[h % NB];
+        const u16* const XH = sXH[h % NB][sub];
+        const u16* const XL = sXL[h % NB][sub];
 #pragma unroll
         for (int k = 0; k < QH / 16; ++k) {
             if (k < nkb) {
@@ -469,24 +479,27 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         // first half.  The scheduling barriers keep each half's staging arithmetic
         // in its phase: hoisted above the barriers it would make the compiler wait
         // for that half's loads early and undo the prefetch distance.
+        // With one tile set, a barrier first waits for the previous half's
+        // products; with a set per half, the barrier after the previous half's
+        // staging already did (every wave multiplied this set before it).
         const int S0 = S < QH ? S : QH;
-        __syncthreads();  // the previous half's products are done with the LDS tiles
+        if (NB == 1) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         stage(buf0, 0, w0, w1);
         load_half(buf0, c + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        multiply((S0 + 15) >> 4);
+        multiply((S0 + 15) >> 4, 0);
 
         // second half
         const int S1 = S - QH;
-        __syncthreads();
+        if (NB == 1) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         stage(buf1, 1, w0, w1);
         load_half(buf1, c + 1, 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        multiply(S1 > 0 ? (S1 + 15) >> 4 : 0);
+        multiply(S1 > 0 ? (S1 + 15) >> 4 : 0, 1);
     }
 
     // The end state: the sequence's final state when this is its only segment;
