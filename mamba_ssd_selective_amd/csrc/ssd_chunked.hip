@@ -601,11 +601,13 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     constexpr int STAGE = (SP ? 4 : 2) * Q * HR;
     constexpr int HX = (SP ? 2 : 1) * P * RS;   // x^T planes of one head
     constexpr int HBUF = HX + 2 * P * NRS;      // + h_in planes: one head buffer
-    constexpr int SMEM = STAGE > 2 * HBUF ? STAGE : 2 * HBUF;
+    constexpr int SMEM = HBUF + STAGE > 2 * HBUF ? HBUF + STAGE : 2 * HBUF;
     constexpr int NXP = 16 * P / CPL;  // x pieces: 8 tokens x CPL columns
     constexpr int NHV = (P * N / 4) / NT;   // float4 of h_in per thread
     // Two head buffers: head j + 1 is staged into one while head j is multiplied
-    // out of the other.  The B / C slices of the G phase use the same memory.
+    // out of the other.  The B / C slices of the G phase lie past head buffer 0
+    // (over buffer 1), so the first head is staged while other waves still
+    // multiply the last slice.
     __shared__ __align__(16) u16 smem[SMEM];
     __shared__ __align__(16) float rowf[2][Q];      // dt_i e(gamma_r(i) - gamma_i)
     __shared__ __align__(16) float colf[2][Q * 8];  // [t][it]: e(gamma_t - gamma_r(it)), it below t's tile
@@ -613,10 +615,10 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     __shared__ __align__(16) float dts[2][Q];
     __shared__ __align__(16) float din[2][Q];       // e(gamma_t)
     __shared__ float sA[MAXHPG], sD[MAXHPG];        // A and D of the group's heads
-    u16* Bh = smem;
-    u16* Ch = smem + Q * HR;
-    u16* Bl = smem + 2 * Q * HR;
-    u16* Cl = smem + 3 * Q * HR;
+    u16* Bh = smem + HBUF;
+    u16* Ch = Bh + Q * HR;
+    u16* Bl = Bh + 2 * Q * HR;
+    u16* Cl = Bh + 3 * Q * HR;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, l16 = lane & 15;
@@ -952,8 +954,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         }
     };
 
-    __syncthreads();   // the G phase is done with the B / C slices
-    stage_head(0, j0);
+    stage_head(0, j0);   // (buffer 0: no G slice there)
     prefetch(j0 + 1 < j1 ? grp * hpg + j0 + 1 : grp * hpg + j0);
     __syncthreads();
     for (int j = j0; j < j1; ++j) {
