@@ -106,6 +106,11 @@ const char* m2_version(void);
 /*
  * mamba2_conv_rows -- causal depthwise conv1d (+ optional SiLU) over the xBC
  * stream of a packed varlen batch, advancing the conv state in place.
+ * (Page "perf(nemotron_h): prefill single-GPU prompts in multi-token chunks",
+ * section Implementation: the short-conv rows of a chunk read the conv state
+ * carried from earlier rows ahead of the chunk's own rows; page "Nemotron-H",
+ * section 3 for the SiLU after conv1d(xBC) and section 10 for the width - 1
+ * rows the conv state keeps per channel.)
  *
  * For sequence b of length L with padded stream xpad = [conv_state[slot] (width-1
  * rows, or zeros if has_init[b]==0) ; the L new rows]:
@@ -141,7 +146,11 @@ int mamba2_conv_rows(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
 /*
  * ssd_chunk_scan -- chunked selective scan (Mamba-2 SSD) of a packed varlen
  * batch, from post-conv x, B, C; writes the pre-norm output and advances the
- * SSM state in place.
+ * SSM state in place.  (Page "perf(nemotron_h): prefill single-GPU prompts in
+ * multi-token chunks", section Implementation: the SSD rows of a chunk with no
+ * sequential step, a_t = dt_t * A, the in-chunk cumulative sum, the chunk total
+ * read from its last element and every exponent clamped at 0; page
+ * "Nemotron-H", section 4.1 for the token recurrence the chunk form equals.)
  *
  * Per sequence, per head h (group g = h / (nheads/ngroups)), in chunks of
  * chunk_size rows counted from the sequence's first row, with
@@ -208,7 +217,11 @@ size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads
                                      int dstate, int ngroups, int chunk_size, int act_dtype);
 
 /*
- * gated_rmsnorm_group -- grouped RMSNorm with the SiLU(z) gate.
+ * gated_rmsnorm_group -- grouped RMSNorm with the SiLU(z) gate.  (Page
+ * "Nemotron-H", section 4.1: the scan output is normalised per group with the
+ * ssm_norm weight and multiplied by the SiLU(z) gate; page "NemotronH decodes
+ * on the single-step recurrent kernels", PR description, names the op
+ * RmsNormGatedGroup(n_groups).)
  *
  * Per token t and group j (channels j*d_inner/ngroups .. (j+1)*d_inner/ngroups-1):
  *   norm_before_gate != 0:  out = y / sqrt(mean_j(y^2) + eps) * w * silu(z)
@@ -237,7 +250,12 @@ size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_se
 /*
  * mamba2_prefill -- the whole mixer core of one layer for a packed varlen batch:
  * conv (+SiLU) over [conv_state ; rows] of x | B | C, the chunked scan with
- * carried ssm_state, the D skip and the grouped gated RMSNorm with z.
+ * carried ssm_state, the D skip and the grouped gated RMSNorm with z.  (Page
+ * "Nemotron-H", section 3: the Mamba-2 layer's conv1d -> SiLU -> SSM -> gated
+ * norm sequence, and section 4.1 for each step; page "perf(nemotron_h): prefill
+ * single-GPU prompts in multi-token chunks", section Implementation: a layer's
+ * conv rows and SSD rows run in one prefill pass over the chunked prompt, the
+ * states committed after it.)
  * Arguments mean what they mean for the three calls above; additionally
  *   z [T, nheads*headdim] (ld_z) of act_dtype;
  *   conv_w [conv_dim, 4], conv_b [conv_dim] or NULL, norm_w [nheads*headdim];

@@ -325,8 +325,10 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     const int64_t cbase = s0 / Q + seq;   // entry-state slot of the sequence's first chunk
     // this workgroup's chunks: all of them, or segment seg_k's (a later segment
     // starts from zero; its first entry slot belongs to the segment before)
+    // (the last level runs to the sequence's end, so a sequence longer than the
+    // max_seqlen the plan was made for still gets every chunk)
     const int cfirst = seg_k * a.seg;
-    const int cend = a.seg > 0 ? (cfirst + a.seg < nch ? cfirst + a.seg : nch) : nch;
+    const int cend = a.seg > 0 && seg_k < a.seg_levels - 1 ? (cfirst + a.seg < nch ? cfirst + a.seg : nch) : nch;
     const Tin* Xg = static_cast<const Tin*>(a.x);
     const Tin* Bg = static_cast<const Tin*>(a.B);
 
@@ -545,7 +547,8 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(ScanArgs a) {
     const int64_t L = a.cu_seqlens[seq + 1] - s0;
     if (L <= 0) return;
     const int nch = (int)((L + Q - 1) / Q);
-    const int nseg = (nch + a.seg - 1) / a.seg;
+    int nseg = (nch + a.seg - 1) / a.seg;
+    if (nseg > a.seg_levels) nseg = a.seg_levels;   // the last level takes the rest
     if (nseg <= 1) return;
     const int64_t cbase = s0 / Q + seq;
     auto entry = [&](int c) {
@@ -657,8 +660,10 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     // In a split sequence, a chunk after the first of a later segment holds a
     // local entry state: the true one adds e(log decay since the segment's start)
     // times the segment's true entry state (its first chunk's slot).
-    const bool fix = a.seg > 0 && c >= a.seg && c % a.seg != 0;
-    const int64_t cslot0 = cslot - (fix ? c % a.seg : 0);
+    // (the last segment takes every chunk from its start on)
+    const int kseg = a.seg > 0 ? min((int)(c / a.seg), a.seg_levels - 1) : 0;
+    const bool fix = kseg >= 1 && c != (int64_t)kseg * a.seg;
+    const int64_t cslot0 = cslot - (fix ? c - (int64_t)kseg * a.seg : 0);
     float4 hs[NHV];
     float fcum = 0.f;
     float dr0 = 0.f, dr1 = 0.f;

@@ -9,7 +9,8 @@ unnoticed.  The mutations are those a port of this method typically makes:
   4. the conv state shifted by one row;
   5. the gate order swapped;
   6. the chunk treated as dense (the causal predicate dropped);
-  7. (in-projection rows) the dt bias dropped, softplus confused with e^v or
+  7. B and C read from each other's channel runs of the conv output;
+  8. (in-projection rows) the dt bias dropped, softplus confused with e^v or
      with log(1 + e^-v), and the row read in the wrong order.
 
 Each mutant wraps or replaces one oracle function through monkeypatch; the
@@ -125,9 +126,25 @@ def test_mutation_dense_chunk(monkeypatch, chunk):
     assert _red([(PINS.test_recurrence_equals_chunk_form, (4, 2, chunk))]) == 1
 
 
+def test_mutation_B_and_C_swapped(monkeypatch):
+    """The conv output's B and C channel runs read the other way round."""
+    def mutant(u, nheads, headdim, ngroups, dstate):
+        L = u.shape[0]
+        di, gn = nheads * headdim, ngroups * dstate
+        x = u[:, :di].reshape(L, nheads, headdim)
+        C = u[:, di:di + gn].reshape(L, ngroups, dstate)
+        B = u[:, di + gn:di + 2 * gn].reshape(L, ngroups, dstate)
+        return x, B, C
+    monkeypatch.setattr(R, "split_xbc", mutant)
+    assert _red([(PINS.test_split_xbc_takes_x_then_B_then_C, ()),
+                 (PINS.test_one_token_roles_of_B_and_C, ())]) == 2
+
+
 def test_unmutated_pins_pass():
     """The same pins, unmutated, are green (so a red above is the mutation's)."""
     assert _red([(PINS.test_group_map_is_contiguous_heads, ()),
+                 (PINS.test_split_xbc_takes_x_then_B_then_C, ()),
+                 (PINS.test_one_token_roles_of_B_and_C, ()),
                  (PINS.test_decay_stress_small_shape_finite_and_chunk_form_agrees, ()),
                  (PINS.test_split_7_plus_4_equals_11_equals_11_single_steps, ()),
                  (PINS.test_conv_matches_numpy_convolve, (4,)),

@@ -197,6 +197,65 @@ def test_positive_exponent_is_detected():
         Ch.chunk_scan_seq(x, B, C, dt, np.abs(A), D, h0, 4)
 
 
+# ---------------------------------------------------------------- the x | B | C split of the conv output
+#
+# Page "feat(#1311 A2-D1): NemotronH decodes on the single-step recurrent
+# kernels ...", PR description: the conv output is split as QkvSplit(x | B | C);
+# page "Nemotron-H", section 4.1: xBC is the joint (x, B, C) stream, B enters
+# the state update and C the read-out.
+
+def test_split_xbc_takes_x_then_B_then_C():
+    """Channel c of a conv-output row carries the value c: the split must give
+    x = channels [0, H*P), B = [H*P, H*P + G*N), C = [H*P + G*N, H*P + 2*G*N),
+    with x[t, h, p] = u[t, h*P + p] and B[t, g, n] = u[t, H*P + g*N + n]."""
+    H, P, G, N, L = 4, 3, 2, 5, 3
+    di, gn = H * P, G * N
+    u = np.arange(L)[:, None] * 1000.0 + np.arange(di + 2 * gn)[None, :]
+    x, B, C = R.split_xbc(u, H, P, G, N)
+    assert x.shape == (L, H, P) and B.shape == (L, G, N) and C.shape == (L, G, N)
+    for t in range(L):
+        for h in range(H):
+            for p in range(P):
+                assert x[t, h, p] == 1000.0 * t + h * P + p
+        for g in range(G):
+            for n in range(N):
+                assert B[t, g, n] == 1000.0 * t + di + g * N + n
+                assert C[t, g, n] == 1000.0 * t + di + gn + g * N + n
+
+
+def test_one_token_roles_of_B_and_C():
+    """One token through the whole prefill driver, identity conv tap (u =
+    silu(xBC)) and a carried state h0: the new state is e^{dt A} h0 + dt x (outer)
+    B with B = silu of the middle channel run, and the pre-norm output is
+    C . h + D x with C = silu of the last run.  B and C hold different values,
+    so reading them the other way round changes both."""
+    H, P, N, G = 2, 3, 4, 1
+    di, gn = H * P, G * N
+    cd = di + 2 * gn
+    row = np.concatenate([np.linspace(-1.0, 1.0, di), np.arange(1, N + 1) * 0.5,
+                          -np.arange(1, N + 1) * 0.25])[None, :]
+    w = np.zeros((cd, 4))
+    w[:, 3] = 1.0
+    rng = np.random.default_rng(91)
+    h0 = rng.standard_normal((1, H, P, N))
+    dt = np.array([[0.3, 0.7]])
+    A = np.array([-1.5, -0.5])
+    D = np.array([0.25, -2.0])
+    inp = dict(xbc=row, conv_w=w, conv_b=np.zeros(cd), conv_state=np.zeros((1, 3, cd)),
+               ssm_state=h0, dt=dt, A=A, D=D, z=np.zeros((1, di)), norm_w=np.ones(di),
+               cu_seqlens=np.array([0, 1]), state_idx=np.array([0]), has_init=np.array([1]))
+    out = R.prefill(inp, H, P, N, G, apply_norm=False)
+    sx = row[0, :di] / (1.0 + np.exp(-row[0, :di]))
+    sb = row[0, di:di + gn] / (1.0 + np.exp(-row[0, di:di + gn]))
+    sc = row[0, di + gn:] / (1.0 + np.exp(-row[0, di + gn:]))
+    for h in range(H):
+        xh = sx[h * P:(h + 1) * P]
+        want_h = math.exp(dt[0, h] * A[h]) * h0[0, h] + dt[0, h] * np.outer(xh, sb)
+        np.testing.assert_allclose(out["ssm_state"][0, h], want_h, rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(out["y"][0, h * P:(h + 1) * P], want_h @ sc + D[h] * xh,
+                                   rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- conv and norm vs library routines
 
 def test_conv_identity_tap_is_silu():
