@@ -278,6 +278,34 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * mamba2_prefill_noalloc -- mamba2_prefill for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and bitwise the same results.  Its scratch is a fixed device array
+ * inside the library, mamba2_prefill_noalloc_scratch_bytes() bytes (64 MiB),
+ * one copy per GPU the library runs on, held until the process ends; its
+ * device address is looked up on the first call on each device.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Sizes whose mamba2_prefill_workspace_size() exceeds the scratch are
+ *   refused with M2_ERR_WORKSPACE before any launch, with no side effects.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last
+ *   call's contents (nothing in it needs to start at zero): calls that overlap
+ *   on one GPU -- on different streams, or from different threads -- race and
+ *   must be serialized by the caller.
+ */
+size_t mamba2_prefill_noalloc_scratch_bytes(void);
+int mamba2_prefill_noalloc(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
+                           const void* C, int64_t ld_C, const void* z, int64_t ld_z, int act_dtype,
+                           const float* dt, int64_t ld_dt, const float* A, const float* D,
+                           const float* conv_w, const float* conv_b, const float* norm_w,
+                           float eps, int norm_before_gate,
+                           float* conv_state, float* ssm_state, int n_slots,
+                           const int32_t* cu_seqlens, int batch, int64_t total_tokens,
+                           int max_seqlen, const int32_t* state_idx, const uint8_t* has_init,
+                           int nheads, int headdim, int dstate, int ngroups, int chunk_size,
+                           void* y, int64_t ld_y, int y_dtype, void* stream);
+
+/*
  * mamba2_decode -- one new token for each of `batch` sequences, at their cache
  * slots: the conv update, the selective state update with its readout and the
  * grouped gated RMSNorm, in one fused kernel (for a small batch with an fp32

@@ -6,6 +6,7 @@ with ``python -m mamba_ssd_selective_amd.build``.
 """
 from ._lib import (M2_BF16, M2_F32, M2Error, cu_seqlens_of, gated_rmsnorm_group, get_counters,
                    load, mamba2_conv_rows, mamba2_decode, mamba2_prefill, mamba2_prefill_workspace_size,
+                   mamba2_prefill_noalloc, mamba2_prefill_noalloc_scratch_bytes,
                    mamba2_prefill_inproj, mamba2_prefill_inproj_workspace_size,
                    mamba2_decode_inproj, mamba2_mixed_inproj, mamba2_mixed_inproj_workspace_size,
                    reset_counters, ssd_chunk_scan, ssd_chunk_scan_workspace_size, timing_enable,
@@ -13,7 +14,8 @@ from ._lib import (M2_BF16, M2_F32, M2Error, cu_seqlens_of, gated_rmsnorm_group,
 
 __all__ = ["M2_BF16", "M2_F32", "M2Error", "cu_seqlens_of", "gated_rmsnorm_group",
            "get_counters", "load", "mamba2_conv_rows", "mamba2_decode", "mamba2_prefill",
-           "mamba2_prefill_workspace_size", "mamba2_prefill_inproj",
+           "mamba2_prefill_workspace_size", "mamba2_prefill_noalloc",
+           "mamba2_prefill_noalloc_scratch_bytes", "mamba2_prefill_inproj",
            "mamba2_prefill_inproj_workspace_size", "mamba2_decode_inproj", "mamba2_mixed_inproj",
            "mamba2_mixed_inproj_workspace_size", "reset_counters", "ssd_chunk_scan",
            "ssd_chunk_scan_workspace_size", "timing_enable",

@@ -66,6 +66,10 @@ _SIGS = {
     "mamba2_prefill": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
                             _F, _I, _P, _P, _I, _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I,
                             _P, _L, _I, _P, ctypes.c_size_t, _P]),
+    "mamba2_prefill_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "mamba2_prefill_noalloc": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
+                                    _F, _I, _P, _P, _I, _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I,
+                                    _P, _L, _I, _P]),
     "mamba2_decode": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
                            _F, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _L, _I, _P]),
     "mamba2_prefill_inproj_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I, _I]),
@@ -310,6 +314,44 @@ def mamba2_prefill(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm
         _ptr(conv_state), _ptr(ssm_state), conv_state.size(0), _ptr(cu_seqlens), batch, T,
         int(max_seqlen), _ptr(state_idx), _ptr(has_init), nheads, headdim, dstate, ngroups,
         chunk_size, _ptr(y), _rows(y, "y"), _dtype_code(y), _ptr(workspace), ws_bytes, _stream())
+    _check(st)
+    return y
+
+
+def mamba2_prefill_noalloc_scratch_bytes() -> int:
+    """Size of the library's fixed device scratch used by mamba2_prefill_noalloc."""
+    return int(load().mamba2_prefill_noalloc_scratch_bytes())
+
+
+def mamba2_prefill_noalloc(x, B, C, z, dt, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state,
+                           cu_seqlens, max_seqlen, nheads, headdim, dstate, ngroups, chunk_size=128,
+                           state_idx=None, has_init=None, eps=1e-5, norm_before_gate=True, y=None,
+                           y_dtype=torch.float32):
+    """mamba2_prefill with the library's own fixed device scratch instead of a
+    workspace (no device allocation in the library; y is allocated here only
+    when not given)."""
+    lib = load()
+    T = x.size(0)
+    batch = cu_seqlens.numel() - 1
+    if y is None:
+        y = torch.empty((T, nheads * headdim), dtype=y_dtype, device=x.device)
+    for t, n in ((A, "A"), (D, "D"), (conv_w, "conv_w"), (conv_b, "conv_b"), (norm_w, "norm_w"),
+                 (conv_state, "conv_state"), (ssm_state, "ssm_state")):
+        _vec(t, n, torch.float32)
+    _vec(cu_seqlens, "cu_seqlens", torch.int32)
+    _vec(state_idx, "state_idx", torch.int32)
+    _vec(has_init, "has_init", torch.uint8)
+    if dt.dtype != torch.float32:
+        raise ValueError("dt must be float32")
+    if not (x.dtype == B.dtype == C.dtype == z.dtype):
+        raise ValueError("x, B, C and z must share one dtype")
+    st = lib.mamba2_prefill_noalloc(
+        _ptr(x), _rows(x, "x"), _ptr(B), _rows(B, "B"), _ptr(C), _rows(C, "C"),
+        _ptr(z), _rows(z, "z"), _dtype_code(x), _ptr(dt), _rows(dt, "dt"), _ptr(A), _ptr(D),
+        _ptr(conv_w), _ptr(conv_b), _ptr(norm_w), float(eps), int(bool(norm_before_gate)),
+        _ptr(conv_state), _ptr(ssm_state), conv_state.size(0), _ptr(cu_seqlens), batch, T,
+        int(max_seqlen), _ptr(state_idx), _ptr(has_init), nheads, headdim, dstate, ngroups,
+        chunk_size, _ptr(y), _rows(y, "y"), _dtype_code(y), _stream())
     _check(st)
     return y
 

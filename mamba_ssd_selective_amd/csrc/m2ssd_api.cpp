@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -735,6 +736,81 @@ int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
         if ((st = run(false)) || (st = debug_check_dt_A(dt, ld_dt, total_tokens, nheads, A))) return st;
     }
     st = run(true);
+    return st ? st : ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of mamba2_prefill_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses
+// its name as an address (on the host it is a stand-in symbol); the device
+// address of each GPU's copy is looked up once per device and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // by device ordinal; nullptr until looked up
+
+// The current device's copy of `scratch`, or nullptr (with the error set).
+void* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        fail(M2_ERR_HIP, "prefill_noalloc: hipGetDevice failed");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(M2_ERR_HIP, "prefill_noalloc: hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba2_prefill_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int mamba2_prefill_noalloc(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
+                           int64_t ld_C, const void* z, int64_t ld_z, int act_dtype, const float* dt,
+                           int64_t ld_dt, const float* A, const float* D, const float* conv_w,
+                           const float* conv_b, const float* norm_w, float eps, int norm_before_gate,
+                           float* conv_state, float* ssm_state, int n_slots, const int32_t* cu_seqlens,
+                           int batch, int64_t total_tokens, int max_seqlen, const int32_t* state_idx,
+                           const uint8_t* has_init, int nheads, int headdim, int dstate, int ngroups,
+                           int chunk_size, void* y, int64_t ld_y, int y_dtype, void* stream) {
+    const size_t need = mamba2_prefill_workspace_size(total_tokens, batch, max_seqlen, nheads, headdim,
+                                                      dstate, ngroups, chunk_size, act_dtype);
+    if (need > kNoAllocScratchBytes)
+        return fail(M2_ERR_WORKSPACE,
+                    "prefill_noalloc: these sizes need %zu bytes of scratch, above the library's %zu",
+                    need, kNoAllocScratchBytes);
+    // every argument check runs before the device scratch is looked up
+    auto run = [&](bool launch, void* ws) {
+        return prefill_run(x, ld_x, B, ld_B, C, ld_C, z, ld_z, act_dtype, dt, ld_dt, A, D, conv_w, conv_b,
+                           norm_w, eps, norm_before_gate, conv_state, ssm_state, n_slots, cu_seqlens,
+                           batch, total_tokens, max_seqlen, state_idx, has_init, nheads, headdim,
+                           dstate, ngroups, chunk_size, y, ld_y, y_dtype, ws,
+                           ws ? kNoAllocScratchBytes : 0, stream, launch);
+    };
+    int st;
+    // The argument checks run first, also on a machine without a GPU: a dry run
+    // (no launch, nothing dereferenced) with a host stand-in for the workspace.
+    alignas(256) static unsigned char dry_ws[256];
+    if ((st = run(false, need > 0 ? dry_ws : nullptr))) return st;
+    if (debug_enabled() && (st = debug_check_dt_A(dt, ld_dt, total_tokens, nheads, A))) return st;
+    void* ws = nullptr;
+    if (need > 0 && !(ws = scratch_on_current_device())) return M2_ERR_HIP;
+    st = run(true, ws);
     return st ? st : ok();
 }
 
