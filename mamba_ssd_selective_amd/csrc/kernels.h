@@ -70,6 +70,18 @@ struct ScanArgs {
     double* cum;                // per (chunk slot, head): log decay from its segment's start
     float* seg_end;             // [batch * nheads] local end states of last segments
     int out_split;              // chunk output: workgroups per (chunk, group), each a run of heads
+    // Chunk-parallel path, raw_conv set: x, B, C are the raw (pre-conv) bf16
+    // xBC rows and both scan kernels compute the conv (width 4) + SiLU
+    // themselves, reading the 3 rows before a sequence's first row from
+    // conv_state (zeros when has_init is 0).  conv_w [conv_dim, 4], conv_b
+    // [conv_dim] or null; x channel (h, p) is xBC channel h*headdim + p, B
+    // channel (g, n) is d_inner + g*dstate + n, C channel (g, n) is
+    // d_inner + ngroups*dstate + g*dstate + n.  conv_state is only read.
+    int raw_conv;
+    const float* conv_w;
+    const float* conv_b;
+    const float* conv_state;
+    int conv_dim;
     // One-pass fp64 path, few long sequences split into segments of `seg` steps
     // (seg_levels of them at most; lam holds each segment's total log decay):
     // per (segment, sequence, head) the local end state, then the true one
@@ -158,6 +170,9 @@ void one_pass_plan(ScanArgs& a, int max_seqlen, void* ws);
 // The workspace holds the entry states (256-byte rounded) and then the int32
 // order of the sequences, longest first, that the state pass deals work in.
 bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, int dstate, int chunk);
+// True when the chunk-parallel kernels also take raw bf16 xBC rows (raw_conv):
+// dstate 64, or dstate 128 with an even number of heads per group.
+bool chunked_raw_supported(int nheads, int ngroups, int headdim, int dstate, int chunk);
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate);
 int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
                             int dstate);

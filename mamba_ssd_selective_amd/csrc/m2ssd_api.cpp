@@ -33,13 +33,19 @@ struct Counters {
 
 // Event recorder for m2_timing_*: set k holds kEv events around the kernel
 // stages of call k (conv, conv state, scan state pass, scan output, norm).
+// Interval k (events k -> k + 1, in stream order) of a call is stage
+// stage[call][k]: 0 conv, 1 conv state, 2 scan state pass, 3 scan output, 4 norm.
 constexpr int kEv = 6;
 struct Timing {
     std::vector<hipEvent_t> ev;
+    std::vector<int> stage;
     int max_calls = 0;
     int used = 0;
-    hipEvent_t* next() {  // event set for the next prefill call, or null when off / full
+    // event set for the next prefill call (its intervals in stream order are the
+    // stages `order`), or null when off / full
+    hipEvent_t* next(const int (&order)[kEv - 1]) {
         if (used >= max_calls) return nullptr;
+        for (int k = 0; k < kEv - 1; ++k) stage[(size_t)(kEv - 1) * used + k] = order[k];
         return &ev[kEv * used++];
     }
 } g_timing;
@@ -272,6 +278,18 @@ void set_rowmajor_out(m2::ConvArgs& a, void* out, int64_t ld_out, int elt) {
     }
 }
 
+// The prefill's scan convolves the raw bf16 rows itself (no post-conv
+// activations in the workspace) wherever the chunk-parallel kernels take raw
+// rows; M2SSD_PREFILL_CHAIN=1 (read at every call) runs the four-kernel chain
+// with the post-conv activations in the workspace instead.
+bool prefill_raw(int act_dtype, int nheads, int headdim, int dstate, int ngroups, int chunk_size) {
+    if (act_dtype != M2_BF16) return false;
+    if (nheads <= 0 || ngroups <= 0 || nheads % ngroups) return false;
+    if (!m2::chunked_raw_supported(nheads, ngroups, headdim, dstate, chunk_size)) return false;
+    const char* e = std::getenv("M2SSD_PREFILL_CHAIN");
+    return !(e && e[0] == '1');
+}
+
 }  // namespace
 
 extern "C" {
@@ -407,10 +425,12 @@ size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_se
         return 0;
     const int64_t conv_dim = (int64_t)nheads * headdim + 2 * (int64_t)ngroups * dstate;
     const int64_t di = (int64_t)nheads * headdim;
-    // post-conv activations (fp32 for bf16 inputs, fp64 for fp32 inputs), the
-    // pre-norm output (fp32; used when y is not fp32) and the scan's entry states
+    // post-conv activations (fp32 for bf16 inputs, fp64 for fp32 inputs; none
+    // when the scan convolves the raw rows itself), the pre-norm output (fp32;
+    // used when y is not fp32) and the scan's entry states
     const int64_t ues = act_dtype == M2_BF16 ? 4 : 8;
-    return (size_t)(round256(total_tokens * conv_dim * ues) + round256(total_tokens * di * 4)) +
+    const bool raw = prefill_raw(act_dtype, nheads, headdim, dstate, ngroups, chunk_size);
+    return (size_t)((raw ? 0 : round256(total_tokens * conv_dim * ues)) + round256(total_tokens * di * 4)) +
            scan_ws_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
@@ -448,10 +468,11 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     // rounding alone, where the largest outputs are tens of times the RMS.
     const int u_dtype = act_dtype == M2_BF16 ? m2::kF32 : m2::kF64;
     const int ues = u_dtype == m2::kF64 ? 8 : 4;
-    const int64_t u_bytes = round256((int64_t)total_tokens * conv_dim * ues);
+    const bool raw = prefill_raw(act_dtype, nheads, headdim, dstate, ngroups, chunk_size);
+    const int64_t u_bytes = raw ? 0 : round256((int64_t)total_tokens * conv_dim * ues);
     const int64_t ypre_bytes = round256((int64_t)total_tokens * d_x * 4);
     char* wsb = static_cast<char*>(workspace);
-    void* u = wsb;
+    void* u = raw ? nullptr : wsb;
     float* ypre_ws = wsb ? reinterpret_cast<float*>(wsb + u_bytes) : nullptr;
     const bool chunked = scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype) > 0;
     float* states_ws = (wsb && chunked) ? reinterpret_cast<float*>(wsb + u_bytes + ypre_bytes) : nullptr;
@@ -466,15 +487,23 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     if ((total_tokens > 0 && !dt) || !A || !ssm_state) return fail(M2_ERR_NULL, "prefill: dt, A and ssm_state are required");
     if (ld_dt < nheads) return fail(M2_ERR_STRIDE, "prefill: ld_dt < nheads");
     if (!aligned16(ssm_state)) return fail(M2_ERR_ALIGN, "prefill: ssm_state must be 16-byte aligned");
-    if ((st = validate_norm(static_cast<const float*>(u ? u : y), d_x, z, ld_z, act_dtype, norm_w,
-                            ngroups, total_tokens, d_x, y, ld_y, y_dtype)))
+    // (the norm's input: the pre-norm output, in y itself when y is fp32)
+    const bool pre_in_y = y_dtype == M2_F32 || !ypre_ws;
+    if ((st = validate_norm(pre_in_y ? static_cast<const float*>(y) : ypre_ws, pre_in_y ? ld_y : d_x, z, ld_z,
+                            act_dtype, norm_w, ngroups, total_tokens, d_x, y, ld_y,
+                            pre_in_y ? M2_F32 : y_dtype)))
         return st;
     if (y_dtype == M2_F32 && (ld_y * 4) % 16) return fail(M2_ERR_ALIGN, "prefill: ld_y must be a multiple of 16 bytes");
     if (!aligned16(y)) return fail(M2_ERR_ALIGN, "prefill: y must be 16-byte aligned");
     if (!launch) return M2_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipEvent_t* tev = g_timing.next();
+    // stages in stream order: the chain runs conv, conv state, state pass, chunk
+    // output, norm; with raw rows the scan comes first and the conv state after it
+    // (both scan kernels read the old conv state)
+    static const int kChainOrder[kEv - 1] = {0, 1, 2, 3, 4};
+    static const int kRawOrder[kEv - 1] = {2, 3, 1, 4, 0};
+    hipEvent_t* tev = g_timing.next(raw ? kRawOrder : kChainOrder);
     auto mark = [&](int k) { if (tev) (void)hipEventRecord(tev[k], s); };
     mark(0);
     m2::ConvArgs ca{};
@@ -492,7 +521,14 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     const int64_t T = total_tokens;
     char* ub = static_cast<char*>(u);
     m2::ScanArgs sa{};
-    if (chunked) {
+    if (raw) {
+        set_rowmajor_out(ca, nullptr, conv_dim, ues);   // (no conv output: only the state advance runs)
+        sa.x = x; sa.ld_x = ld_x; sa.hs_x = headdim;
+        sa.B = B; sa.ld_B = ld_B; sa.gs_B = dstate;
+        sa.C = C; sa.ld_C = ld_C; sa.gs_C = dstate;
+        sa.raw_conv = 1; sa.conv_w = conv_w; sa.conv_b = conv_b; sa.conv_state = conv_state;
+        sa.conv_dim = conv_dim;
+    } else if (chunked) {
         const int64_t off[3] = {0, (int64_t)d_x * T * ues, (int64_t)(d_x + d_b) * T * ues};
         const int bw[3] = {headdim, dstate, dstate};
         for (int k = 0; k < 3; ++k) {
@@ -507,18 +543,20 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
         sa.B = ub + (int64_t)d_x * ues; sa.ld_B = conv_dim; sa.gs_B = dstate;
         sa.C = ub + (int64_t)(d_x + d_b) * ues; sa.ld_C = conv_dim; sa.gs_C = dstate;
     }
-    if (total_tokens > 0) {
-        if ((st = hip_status(m2::launch_conv_rows(ca, s), "prefill conv launch"))) return st;
-        g_counters.conv++;
+    if (!raw) {
+        if (total_tokens > 0) {
+            if ((st = hip_status(m2::launch_conv_rows(ca, s), "prefill conv launch"))) return st;
+            g_counters.conv++;
+        }
+        mark(1);
+        if ((st = hip_status(m2::launch_conv_state_update(ca, s), "prefill conv state launch"))) return st;
+        g_counters.conv_state++;
+        mark(2);
     }
-    mark(1);
-    if ((st = hip_status(m2::launch_conv_state_update(ca, s), "prefill conv state launch"))) return st;
-    g_counters.conv_state++;
-    mark(2);
 
     float* ypre = (y_dtype == M2_F32) ? static_cast<float*>(y) : ypre_ws;
     const int64_t ld_pre = (y_dtype == M2_F32) ? ld_y : d_x;
-    sa.act_dtype = u_dtype;
+    sa.act_dtype = raw ? m2::kBF16 : u_dtype;
     sa.policy = act_dtype == M2_BF16 ? m2::kPolicyBf16x3 : m2::kPolicyF64;
     sa.dt = dt; sa.ld_dt = ld_dt; sa.A = A; sa.D = D; sa.ssm_state = ssm_state;
     sa.cu_seqlens = cu_seqlens; sa.batch = batch; sa.state_idx = state_idx; sa.has_init = has_init;
@@ -529,8 +567,15 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     if (states_ws) m2::chunked_scan_plan(sa, total_tokens, max_seqlen);
     else m2::one_pass_plan(sa, max_seqlen, seg_ws);
     if (batch == 1) sa.order = nullptr;  // one sequence: no order to compute
-    if ((st = launch_scan(sa, total_tokens, s, tev ? tev[3] : nullptr))) return st;
-    mark(4);
+    if ((st = launch_scan(sa, total_tokens, s, tev ? tev[raw ? 1 : 3] : nullptr))) return st;
+    if (raw) {
+        mark(2);
+        if ((st = hip_status(m2::launch_conv_state_update(ca, s), "prefill conv state launch"))) return st;
+        g_counters.conv_state++;
+        mark(3);
+    } else {
+        mark(4);
+    }
 
     if (total_tokens > 0) {
         m2::NormArgs na{};
@@ -541,7 +586,12 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
         if ((st = hip_status(m2::launch_gated_norm(na, s), "prefill norm launch"))) return st;
         g_counters.norm++;
     }
-    mark(5);
+    if (raw) {
+        mark(4);
+        mark(5);
+    } else {
+        mark(5);
+    }
     g_counters.prefill++;
     return ok();
 }
@@ -1010,6 +1060,7 @@ int m2_timing_enable(int max_calls) {
     g_timing.max_calls = 0;
     if (max_calls == 0) return ok();
     g_timing.ev.resize((size_t)kEv * max_calls);
+    g_timing.stage.assign((size_t)(kEv - 1) * max_calls, 0);
     for (auto& e : g_timing.ev) {
         const hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -1033,7 +1084,7 @@ int m2_timing_read(m2_kernel_times* out) {
         for (int k = 0; k < kEv - 1; ++k) {
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, e[k], e[k + 1]) != hipSuccess) ms = 0.f;
-            *dst[k] += ms;
+            *dst[g_timing.stage[(size_t)(kEv - 1) * c + k]] += ms;
         }
     }
     out->calls = (uint64_t)g_timing.used;

@@ -156,6 +156,153 @@ struct In {
     }
 };
 
+// Raw input: the pre-conv bf16 xBC rows.  A kernel reading them convolves on
+// the fly (width 4, bias, SiLU in fp32, the same operations in the same order as
+// the conv kernel, so the post-conv values are those the conv kernel writes)
+// and takes every post-conv value as an fp32 (hi, lo) operand.
+struct RawBf16 {};
+template <>
+struct In<RawBf16> {
+    static constexpr bool kSplit = true;
+    static constexpr int CPL = 8;
+};
+template <typename Tin>
+constexpr bool is_raw() { return std::is_same<Tin, RawBf16>::value; }
+
+// A raw piece: RR consecutive rows of 8 channels, read as the RR + 3 raw rows
+// that start 3 rows earlier (the conv's halo).
+constexpr int RR = 4;
+constexpr int RW = RR + 3;
+
+__device__ __forceinline__ float bf16_lane(const uint4& v, int k) {
+    const uint32_t w = word_of(v, k >> 1);
+    return __builtin_bit_cast(float, (k & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Conv-weight tables in LDS hold channel 8 cg + k of each 64-channel block at
+// slot 8 k + cg: the 8 channel groups of a wave then read 8 consecutive
+// entries for one k (in channel order the same reads were 128 bytes apart and
+// fell into 2 of the 64 banks).  Bias tables stay in channel order, read as
+// two 16-byte runs per channel group.
+__device__ __forceinline__ int wsw(int e) { return (e & ~63) | ((e & 7) << 3) | ((e >> 3) & 7); }
+
+// The conv biases of channel group base .. base + 7 from LDS (the weights are
+// read one channel at a time where they are used: held for all 8 channels at
+// once they made the chunk output spill).
+struct ConvW {
+    const float4* wt;
+    int base;
+    float b[8];
+    __device__ __forceinline__ float4 w(int k) const { return wt[wsw(base + k)]; }
+};
+__device__ __forceinline__ ConvW read_convw(const float4* wt, const float* bt, int base) {
+    ConvW c;
+    c.wt = wt;
+    c.base = base;
+    const float4 b0 = *reinterpret_cast<const float4*>(bt + base);
+    const float4 b1 = *reinterpret_cast<const float4*>(bt + base + 4);
+    c.b[0] = b0.x; c.b[1] = b0.y; c.b[2] = b0.z; c.b[3] = b0.w;
+    c.b[4] = b1.x; c.b[5] = b1.y; c.b[6] = b1.z; c.b[7] = b1.w;
+    return c;
+}
+
+// Raw rows row0 - 3 .. row0 + RR - 1 of a chunk, rows clamped into the
+// sequence [lo, hi] (chunk-relative: lo = -(chunk's first row in the
+// sequence), hi = lo + L - 1); the conv of a piece that starts the sequence
+// takes its first 3 rows from the conv state instead (conv_piece_start).  col
+// points at the piece's first channel in the chunk's first row; row offsets
+// are 32-bit (a chunk's rows lie within 2^31 elements of its first row).
+//
+// Lanes 8m .. 8m + 7 hold consecutive row groups of one channel group, so the
+// 3 halo rows of a piece are rows 1..3 of the previous lane's piece (raw_halo,
+// a row shift between lanes); only lanes 8m (own_halo) read theirs.
+__device__ __forceinline__ void load_raw_piece(const uint16_t* col, int ld, int row0, int lo, int hi,
+                                               bool own_halo, uint4 (&r)[RW]) {
+    // The row offsets are recomputed at every call: kept across a loop instead
+    // (they do not change from head to head) they made the chunk output spill.
+    asm volatile("" : "+v"(ld));
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        int rr = row0 - 3 + j;
+        rr = rr < lo ? lo : rr > hi ? hi : rr;
+        if (j >= 3 || own_halo) r[j] = *reinterpret_cast<const uint4*>(col + rr * ld);
+    }
+}
+
+// Rows 0..2 of every piece whose lane did not read them, from lane - 1 (DPP
+// row_shr:1; the lanes 8m keep what they read).
+__device__ __forceinline__ int dpp_prev(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false); }
+__device__ __forceinline__ void raw_halo(uint4 (&r)[RW], int lane) {
+    const bool own = (lane & 7) == 0;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const uint4 v = r[4 + j];
+        const uint4 u = uint4{(uint32_t)dpp_prev((int)v.x), (uint32_t)dpp_prev((int)v.y),
+                              (uint32_t)dpp_prev((int)v.z), (uint32_t)dpp_prev((int)v.w)};
+        if (!own) r[j] = u;
+    }
+}
+
+// The 3 rows before a sequence's first row for the 8 channels at conv-state
+// column ch: the slot's carried state (oldest first) or zeros.
+__device__ __forceinline__ void load_halo(const float* conv_state, int conv_dim, int slot, bool init, int ch,
+                                          float (&hv)[3][8]) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        float4 v0 = float4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (init) {
+            const float* p = conv_state + ((int64_t)slot * 3 + j) * conv_dim + ch;
+            v0 = *reinterpret_cast<const float4*>(p);
+            v1 = *reinterpret_cast<const float4*>(p + 4);
+        }
+        hv[j][0] = v0.x; hv[j][1] = v0.y; hv[j][2] = v0.z; hv[j][3] = v0.w;
+        hv[j][4] = v1.x; hv[j][5] = v1.y; hv[j][6] = v1.z; hv[j][7] = v1.w;
+    }
+}
+
+// SiLU(b + w0 v[t] + w1 v[t+1] + w2 v[t+2] + w3 v[t+3]) for the RR rows t of
+// channel k of a piece; with `start` the first 3 window rows are hv[.][k].
+__device__ __forceinline__ void conv_piece(const uint4 (&r)[RW], int k, bool start, const float (&hv)[3][8],
+                                           float4 w, float b, float (&u)[RR]) {
+    float v[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) v[j] = bf16_lane(r[j], k);
+    if (start) {
+        v[0] = hv[0][k];
+        v[1] = hv[1][k];
+        v[2] = hv[2][k];
+    }
+#pragma unroll
+    for (int t = 0; t < RR; ++t) {
+        float acc = b;
+        acc = fmaf(w.x, v[t], acc);
+        acc = fmaf(w.y, v[t + 1], acc);
+        acc = fmaf(w.z, v[t + 2], acc);
+        acc = fmaf(w.w, v[t + 3], acc);
+        u[t] = silu(acc);
+    }
+}
+
+// conv_piece for a piece that starts its sequence, reading channel k's 3 carried
+// rows from the conv state (zeros when init is 0) as it goes.
+__device__ __forceinline__ void conv_piece_start(const uint4 (&r)[RW], int k, const float* conv_state, int conv_dim,
+                                                 int slot, bool init, int ch, float4 w, float b, float (&u)[RR]) {
+    float v[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) v[j] = bf16_lane(r[j], k);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) v[j] = init ? conv_state[((int64_t)slot * 3 + j) * conv_dim + ch + k] : 0.f;
+#pragma unroll
+    for (int t = 0; t < RR; ++t) {
+        float acc = b;
+        acc = fmaf(w.x, v[t], acc);
+        acc = fmaf(w.y, v[t + 1], acc);
+        acc = fmaf(w.z, v[t + 2], acc);
+        acc = fmaf(w.w, v[t + 3], acc);
+        u[t] = silu(acc);
+    }
+}
+
 // acc += a b over (hi, lo) operands: the lo x lo term (~2^-18 relative) is dropped,
 // and a lo part that is known to be zero (SA / SB false) is skipped.
 template <bool SA, bool SB>
@@ -225,6 +372,10 @@ struct HalfBuf {
     uint4 br[TB];      // B piece: TB tokens x CPL channels
     uint4 xr[TX];      // x piece: TX tokens x CPL columns
 };
+// Raw input: one piece per thread, of x or of B (see the state pass).
+struct RawBuf {
+    uint4 r[RW];
+};
 
 template <int K, typename Tin>
 __device__ __forceinline__ void load_rows_clamped(const Tin* base, int64_t ld, int valid, uint4 (&r)[K]) {
@@ -247,18 +398,29 @@ __device__ __forceinline__ void store_tokens(u16* dst, const uint32_t (&w)[(TB +
 // loads, the largest part of the per-CU load instructions (the vector memory
 // units of a CU were busy 80-90% of the kernel).  Both items share their
 // sequence, so they have the same chunk count and take every barrier together.
+//
+// Raw input (pre-conv bf16 rows, N = 64 * IPW): each thread convolves one piece
+// of RR rows x 8 channels per half.  Threads 0-127 of an item take its head's x
+// (8 channel groups x 16 row groups), threads 128-255 its share of B (8 channel
+// groups x 16 row groups: all of B for N = 64, half of it per item for N = 128);
+// the conv weights of the workgroup's channels are staged in LDS once.
 template <int N, int IPW, typename Tin>
 __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_kernel(ScanArgs a) {
+    constexpr bool RAW = is_raw<Tin>();
     constexpr bool SP = In<Tin>::kSplit;
     constexpr int CPL = In<Tin>::CPL;
     constexpr int NT = 256;                            // threads per item
     constexpr int NTB = NT * IPW;                      // threads that stage B
     constexpr int TPW = N / 64;                        // 32x32 state tiles per wave
-    constexpr int TB = QH * N / (CPL * NTB);           // tokens per B piece (one piece per thread)
-    constexpr int TX = QH * P / (CPL * NT);            // tokens per x piece
+    constexpr int TB = RAW ? 2 : QH * N / (CPL * NTB); // tokens per B piece (one piece per thread)
+    constexpr int TX = RAW ? 2 : QH * P / (CPL * NT);  // tokens per x piece
     constexpr int BG = QH / TB, XG = QH / TX;          // token groups
     constexpr int BC = N / CPL;                        // B channel groups
     static_assert(TB >= 2 && TX >= 2, "staging pieces");
+    static_assert(!RAW || N == 64 * IPW, "raw pieces: 8 B channel groups per item");
+    constexpr int NCW = RAW ? IPW * P + N : 1;         // conv channels of the workgroup (raw input)
+    __shared__ float4 sCW[NCW];                        // their conv weights (slots wsw)
+    __shared__ __align__(16) float sCB[NCW];           // and biases (channel order)
     // Two items per workgroup (one per CU anyway) keep a tile set per half,
     // so one barrier per half suffices; one item keeps one set (two
     // workgroups then share a CU).
@@ -321,6 +483,24 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         return;
     }
 
+    // raw input: this thread's piece (x of the item's head, or a share of B),
+    // and the conv weights of the workgroup's channels into LDS
+    const bool rx = tid < 128;                                   // wave-uniform
+    const int r_rg = (lane & 7) + 8 * (wave & 1);                // row group: rows 4 r_rg .. + 3 of a half
+    const int r_cg = (rx ? 0 : (IPW == 2 ? 8 * sub : 0)) + (lane >> 3);  // channel group of x or of B
+    const int d_inner = a.nheads * P;
+    const int r_ch = rx ? head * P + 8 * r_cg : d_inner + grp * N + 8 * r_cg;   // first xBC channel
+    const int r_lch = rx ? sub * P + 8 * r_cg : IPW * P + 8 * r_cg;             // its weights in LDS
+    if constexpr (RAW) {
+        const int head0 = head - sub;
+        for (int e = (int)threadIdx.x; e < NCW; e += NT * IPW) {
+            const int ch = e < IPW * P ? (head0 + e / P) * P + e % P : d_inner + grp * N + (e - IPW * P);
+            sCW[wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
+            sCB[e] = a.conv_b ? a.conv_b[ch] : 0.f;
+        }
+        __syncthreads();
+    }
+
     const int nch = (int)((L + Q - 1) / Q);
     const int64_t cbase = s0 / Q + seq;   // entry-state slot of the sequence's first chunk
     // this workgroup's chunks: all of them, or segment seg_k's (a later segment
@@ -342,20 +522,30 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     const int b_cg = B88 ? (lane >> 3) + 8 * (gwave % (BC / 8)) : (int)threadIdx.x / BG;
     const int x_tg = SP ? (lane & 7) + 8 * (wave & 1) : tid % XG;
     const int x_cg = SP ? (lane >> 3) + 8 * (wave >> 1) : tid / XG;
-    static_assert(!SP || (XG == 16 && P / CPL == 16), "fp32 x piece mapping");
+    static_assert(RAW || !SP || (XG == 16 && P / CPL == 16), "fp32 x piece mapping");
 
     // Loads of half h (0, 1) of chunk c, clamped to the last chunk so the call is
     // unconditional; rows beyond the chunk re-read its last row (zeroed later).
-    auto load_half = [&](HalfBuf<Tin, TB, TX>& b, int c, int h) __attribute__((always_inline)) {
+    using Buf = typename std::conditional<RAW, RawBuf, HalfBuf<Tin, TB, TX>>::type;
+    auto load_half = [&](Buf& b, int c, int h) __attribute__((always_inline)) {
         c = c < cend ? c : cend - 1;
+        if constexpr (RAW) {
+            const int64_t ld = rx ? a.ld_x : a.ld_B;
+            const uint16_t* col = rx ? static_cast<const uint16_t*>(a.x) + head * a.hs_x + 8 * r_cg
+                                     : static_cast<const uint16_t*>(a.B) + grp * a.gs_B + 8 * r_cg;
+            load_raw_piece(col + (s0 + (int64_t)c * Q) * ld, (int)ld, h * QH + 4 * r_rg, -c * Q,
+                           (int)(L - 1 - (int64_t)c * Q), (lane & 7) == 0, b.r);
+            return;
+        } else {
         const int64_t left = L - (int64_t)c * Q - h * QH;     // rows of the sequence from this half on
         const int S = (int)(left < QH ? left : QH);
         // an empty half (the chunk ends in its first half) reads the chunk's first row
         const int64_t r0 = s0 + (int64_t)c * Q + (S > 0 ? h * QH : 0);
         const int rb = TB * b_tg < S ? TB * b_tg : 0;
         load_rows_clamped<TB>(Bg + (r0 + rb) * a.ld_B + grp * a.gs_B + b_cg * CPL, a.ld_B, S - rb, b.br);
-        const int rx = TX * x_tg < S ? TX * x_tg : 0;
-        load_rows_clamped<TX>(Xg + (r0 + rx) * a.ld_x + head * a.hs_x + x_cg * CPL, a.ld_x, S - rx, b.xr);
+        const int rxo = TX * x_tg < S ? TX * x_tg : 0;
+        load_rows_clamped<TX>(Xg + (r0 + rxo) * a.ld_x + head * a.hs_x + x_cg * CPL, a.ld_x, S - rxo, b.xr);
+        }
     };
     auto load_dt = [&](int c, float& d0, float& d1) __attribute__((always_inline)) {
         c = c < cend ? c : cend - 1;
@@ -368,11 +558,45 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     // Stage half h of chunk c from b with weights w0/w1 (rows 2 lane, 2 lane + 1).
     // Rows past the sequence's end hold re-read (finite) rows and have weight 0
     // (dt is zeroed there), so their (w x) is 0 and they add nothing; no mask.
-    auto stage = [&](HalfBuf<Tin, TB, TX>& b, int h, float w0, float w1) __attribute__((always_inline)) {
+    auto stage = [&](Buf& b, int c, int h, float w0, float w1) __attribute__((always_inline)) {
         u16* const BTh = sBTh[h % NB];
         u16* const BTl = sBTl[h % NB];
         u16* const XH = sXH[h % NB][sub];
         u16* const XL = sXL[h % NB][sub];
+        if constexpr (RAW) {
+            // conv + SiLU of the piece; x rows are then weighted by w
+            const int row0 = QH * h + 4 * r_rg;               // first row of the piece in the chunk
+            const bool start = c == 0 && row0 == 0;           // the piece starts the sequence
+            raw_halo(b.r, lane);
+            float hv[3][8];
+            if (start) load_halo(a.conv_state, a.conv_dim, slot, init, r_ch, hv);
+            float wx[RR];
+#pragma unroll
+            for (int t = 0; t < RR; ++t) {
+                const int row = row0 + t;
+                const float wa = __shfl(w0, row >> 1, 64), wb = __shfl(w1, row >> 1, 64);
+                wx[t] = (row & 1) ? wb : wa;
+            }
+            const ConvW cw = read_convw(sCW, sCB, r_lch);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float u[RR];
+                conv_piece(b.r, k, start, hv, cw.w(k), cw.b[k], u);
+                uint32_t wh[RR / 2], wl[RR / 2];
+                if (rx) {
+#pragma unroll
+                    for (int m = 0; m < RR / 2; ++m) split2(u[2 * m] * wx[2 * m], u[2 * m + 1] * wx[2 * m + 1], wh[m], wl[m]);
+                    store_tokens<RR>(XH + (8 * r_cg + k) * RH + 4 * r_rg, wh);
+                    store_tokens<RR>(XL + (8 * r_cg + k) * RH + 4 * r_rg, wl);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < RR / 2; ++m) split2(u[2 * m], u[2 * m + 1], wh[m], wl[m]);
+                    store_tokens<RR>(BTh + (8 * r_cg + k) * RH + 4 * r_rg, wh);
+                    store_tokens<RR>(BTl + (8 * r_cg + k) * RH + 4 * r_rg, wl);
+                }
+            }
+            return;
+        } else {
         // B^T: channel CPL b_cg + j, tokens TB b_tg ..
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -407,6 +631,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
             store_tokens<TX>(XH + (x_cg * CPL + j) * RH + TX * x_tg, wh);
             store_tokens<TX>(XL + (x_cg * CPL + j) * RH + TX * x_tg, wl);
         }
+        }
     };
 
     // h^T += B^T (w x) over the 16-row K blocks of a staged half (32x32x16: an
@@ -440,7 +665,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     // (dt, first half, second half): the compiler's wait counts at the loop head
     // take the later position of each register over both ways in, so a different
     // order here would make every chunk wait for both halves at once.
-    HalfBuf<Tin, TB, TX> buf0, buf1;
+    Buf buf0, buf1;
     float d0, d1;
     load_dt(cfirst, d0, d1);
     __builtin_amdgcn_sched_barrier(0);
@@ -487,7 +712,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         const int S0 = S < QH ? S : QH;
         if (NB == 1) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        stage(buf0, 0, w0, w1);
+        stage(buf0, c, 0, w0, w1);
         load_half(buf0, c + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -497,7 +722,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         const int S1 = S - QH;
         if (NB == 1) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        stage(buf1, 1, w0, w1);
+        stage(buf1, c, 1, w0, w1);
         load_half(buf1, c + 1, 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -592,8 +817,15 @@ __global__ __launch_bounds__(256) void segment_carry_kernel(ScanArgs a) {
 // e(gamma_t - gamma_r), r the last row of i's tile (both exponents <= 0, so
 // neither factor overflows); diagonal tiles take the exponential per element.
 
+//
+// Raw input (pre-conv bf16 rows): the G phase convolves B and C in pieces of
+// RR rows x 8 channels (threads 0-255 B, 256-511 C, one piece per 64-n slice),
+// with their conv weights staged over head buffer 0; each head's x is
+// convolved by threads 0-255 in the same pieces, with the head's conv weights
+// staged into LDS one head ahead by threads 256 .. 256 + 5P/4 - 1.
 template <int N, typename Tin>
 __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
+    constexpr bool RAW = is_raw<Tin>();
     constexpr bool SP = In<Tin>::kSplit;
     constexpr int CPL = In<Tin>::CPL;
     constexpr int NT = 512;
@@ -618,6 +850,9 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     __shared__ __align__(16) float dts[2][Q];
     __shared__ __align__(16) float din[2][Q];       // e(gamma_t)
     __shared__ float sA[MAXHPG], sD[MAXHPG];        // A and D of the group's heads
+    __shared__ float4 sXW[2][RAW ? P : 1];          // raw input: conv weights of a head's x, per head buffer
+    __shared__ __align__(16) float sXB[2][RAW ? P : 1];   // and biases (channel order)
+    static_assert(!RAW || 2 * N * 5 * 4 <= 2 * HBUF, "G-phase conv weights fit over head buffer 0");
     u16* Bh = smem + HBUF;
     u16* Ch = Bh + Q * HR;
     u16* Bl = Bh + 2 * Q * HR;
@@ -652,6 +887,14 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     const Tin* Xg = static_cast<const Tin*>(a.x);
     const Tin* Bg = static_cast<const Tin*>(a.B);
     const Tin* Cg = static_cast<const Tin*>(a.C);
+    // raw input: the conv state's slot of this sequence (for the chunk's first rows)
+    const int slot = a.state_idx ? a.state_idx[seq] : seq;
+    const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
+    const int d_inner = a.nheads * P;
+    // raw input: this thread's x piece (threads 0-255): 8 channels x RR rows
+    const int x_cg = lane >> 3, x_rg = (lane & 7) + 8 * (wave & 3);
+    // (threads 256 .. hold the conv weights of the workgroup's next head in xraw[0])
+    uint4 xraw[RAW ? RW : 1];
 
     // per-head staging registers: x piece (8 tokens x CPL columns), h_in, dt
     const int tg = tid % 16;
@@ -673,7 +916,19 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     // run per column and read back with one 16-byte LDS read.
     const int xrow0 = 32 * (tg >> 2) + 4 * (tg & 3);
     auto prefetch = [&](int head) {
-        if (tid < NXP) {
+        if constexpr (RAW) {
+            if (tid < 256) {
+                load_raw_piece(static_cast<const uint16_t*>(a.x) + r0 * a.ld_x + head * a.hs_x + 8 * x_cg,
+                               (int)a.ld_x, 4 * x_rg, (int)(-c * Q), (int)(L - 1 - c * Q), (lane & 7) == 0, xraw);
+            } else if (tid < 256 + P + P / 4) {
+                // conv weights of the workgroup's next head (or this one again at the end)
+                const int hn = head + 1 < grp * hpg + j1 ? head + 1 : head;
+                const int e = tid - 256;
+                xraw[0] = uint4{0u, 0u, 0u, 0u};
+                if (e < P) xraw[0] = *reinterpret_cast<const uint4*>(a.conv_w + ((int64_t)hn * P + e) * 4);
+                else if (a.conv_b) xraw[0] = *reinterpret_cast<const uint4*>(a.conv_b + hn * P + 4 * (e - P));
+            }
+        } else if (tid < NXP) {
             const Tin* xb = Xg + r0 * a.ld_x + head * a.hs_x + (tid / 16) * CPL;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -684,7 +939,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
         for (int k = 0; k < NHV; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + NT * k));
-        if (fix) {
+        if (fix && !RAW) {
             const float* hf = a.states + (cslot0 * a.nheads + head) * (int64_t)(P * N);
 #pragma unroll
             for (int k = 0; k < NHV; ++k) hs[k] = *reinterpret_cast<const float4*>(hf + 4 * (tid + NT * k));
@@ -717,8 +972,35 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     // slices cost one memory round trip per piece.  Rows past the chunk's end
     // only reach G entries that the causal mask or a zero dt leaves unused.
     constexpr int PPR = 64 / CPL;            // pieces per 64-n row slice
-    constexpr int GIT = Q * PPR / NT;        // pieces per thread per slice
+    constexpr int GIT = RAW ? 1 : Q * PPR / NT;   // pieces per thread per slice
     uint4 gbv[NPASS][GIT], gcv[NPASS][GIT];
+    // raw input: one piece per slice, of B (threads 0-255) or C (256-511)
+    const bool gB = tid < 256;
+    const int g_cg = lane >> 3, g_rg = (lane & 7) + 8 * (wave & 3);
+    uint4 graw[RAW ? NPASS : 1][RAW ? RW : 1];
+    float4* gW = reinterpret_cast<float4*>(smem);          // G-phase conv weights, over head buffer 0:
+    float* gBias = reinterpret_cast<float*>(smem + 16 * N);  // [B channels ; C channels]
+    if constexpr (RAW) {
+        const int64_t gld = gB ? a.ld_B : a.ld_C;
+        const uint16_t* gcol = gB ? static_cast<const uint16_t*>(a.B) + r0 * a.ld_B + grp * a.gs_B
+                                  : static_cast<const uint16_t*>(a.C) + r0 * a.ld_C + grp * a.gs_C;
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps)
+            load_raw_piece(gcol + 64 * ps + 8 * g_cg, (int)gld, 4 * g_rg, (int)(-c * Q), (int)(L - 1 - c * Q),
+                           (lane & 7) == 0, graw[ps]);
+        for (int e = tid; e < 2 * N; e += NT) {
+            const int ch = d_inner + (e < N ? grp * N + e : G * N + grp * N + (e - N));
+            gW[wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
+            gBias[e] = a.conv_b ? a.conv_b[ch] : 0.f;
+        }
+        // the first head's x conv weights
+        for (int e = tid; e < P; e += NT) {
+            const int ch = (grp * hpg + j0) * P + e;
+            sXW[0][wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
+            sXB[0][e] = a.conv_b ? a.conv_b[ch] : 0.f;
+        }
+        __syncthreads();
+    } else {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps)
 #pragma unroll
@@ -730,9 +1012,47 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             gbv[ps][k] = *reinterpret_cast<const uint4*>(Bg + row * a.ld_B + grp * a.gs_B + col);
             gcv[ps][k] = *reinterpret_cast<const uint4*>(Cg + row * a.ld_C + grp * a.gs_C + col);
         }
+    }
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
         if (ps > 0) __syncthreads();   // the previous slice's products are done
+        if constexpr (RAW) {
+            // conv + SiLU of this thread's piece of the slice, rows 4 g_rg .. + 3
+            raw_halo(graw[ps], lane);
+            const int row0 = 4 * g_rg;
+            const bool start = c == 0 && row0 == 0;
+            const int wi = (gB ? 0 : N) + 64 * ps + 8 * g_cg;
+            const int ch0 = d_inner + (gB ? 0 : G * N) + grp * N + 64 * ps + 8 * g_cg;
+            u16* const dh = gB ? Bh : Ch;
+            u16* const dl = gB ? Bl : Cl;
+            const ConvW cw = read_convw(gW, gBias, wi);
+            // one output row (8 channels) at a time; window row j of output row tt
+            // is raw row tt + j, or for a piece that starts the sequence and
+            // tt + j < 3, carried row tt + j of the conv state
+#pragma unroll
+            for (int tt = 0; tt < RR; ++tt) {
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 w4 = cw.w(k);
+                    const float wk[4] = {w4.x, w4.y, w4.z, w4.w};
+                    float acc = cw.b[k];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float xv = bf16_lane(graw[ps][tt + j], k);
+                        if (tt + j < 3 && start)
+                            xv = init ? a.conv_state[((int64_t)slot * 3 + tt + j) * a.conv_dim + ch0 + k] : 0.f;
+                        acc = fmaf(wk[j], xv, acc);
+                    }
+                    v[k] = silu(acc);
+                }
+                uint4 h4, l4;
+                split8(v, h4, l4);
+                const int off = (row0 + tt) * HR + 8 * g_cg;
+                *reinterpret_cast<uint4*>(dh + off) = h4;
+                *reinterpret_cast<uint4*>(dl + off) = l4;
+            }
+        } else {
 #pragma unroll
         for (int k = 0; k < GIT; ++k) {
             const int e = tid + NT * k;
@@ -754,6 +1074,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
                 *reinterpret_cast<uint4*>(Bh + off) = vb;
                 *reinterpret_cast<uint4*>(Ch + off) = vc;
             }
+        }
         }
         __syncthreads();
 #pragma unroll
@@ -799,6 +1120,62 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
             }
         }
 
+        if constexpr (RAW) {
+            // the next head's conv weights into the other buffer (read one phase later)
+            if (tid >= 256 && tid < 256 + P) {
+                sXW[bf ^ 1][wsw(tid - 256)] = __builtin_bit_cast(float4, xraw[0]);
+            } else if (tid >= 256 + P && tid < 256 + P + P / 4) {
+                *reinterpret_cast<float4*>(&sXB[bf ^ 1][4 * (tid - 256 - P)]) = __builtin_bit_cast(float4, xraw[0]);
+            }
+            // a later segment's local entry state: its true part is added here (the
+            // loads wait in place; only split sequences take this path)
+            if (fix) {
+                const int head = grp * hpg + j;
+                const float* hf = a.states + (cslot0 * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+                for (int k = 0; k < NHV; ++k) hs[k] = *reinterpret_cast<const float4*>(hf + 4 * (tid + NT * k));
+                fcum = expc(a.cum[(int64_t)cslot * a.nheads + head]);
+            }
+            // conv + SiLU of the x piece: rows 4 x_rg .. + 3 of the chunk, placed at
+            // their positions in the K-slot order of the x^T planes (row i sits at
+            // 8 (4 (i / 32) + (i / 4) % 4) + 4 ((i / 16) % 2) + i % 4)
+            if (tid < 256) {
+                raw_halo(xraw, lane);
+                const int head = grp * hpg + j;
+                const int row0 = 4 * x_rg;
+                const bool start = c == 0 && row0 == 0;
+                const int pos = 8 * (4 * (row0 >> 5) + ((row0 >> 2) & 3)) + 4 * ((row0 >> 4) & 1);
+                auto put = [&](int k, float (&u)[RR]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int tt = 0; tt < RR; ++tt)
+                        if (row0 + tt >= S) u[tt] = 0.f;
+                    uint32_t hb[2], lb[2];
+                    split2(u[0], u[1], hb[0], lb[0]);
+                    split2(u[2], u[3], hb[1], lb[1]);
+                    const int off = (8 * x_cg + k) * RS + pos;
+                    *reinterpret_cast<uint2*>(Xh + off) = uint2{hb[0], hb[1]};
+                    *reinterpret_cast<uint2*>(Xl + off) = uint2{lb[0], lb[1]};
+                };
+                const ConvW cw = read_convw(sXW[bf], sXB[bf], 8 * x_cg);
+                if (start) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        float u[RR];
+                        conv_piece_start(xraw, k, a.conv_state, a.conv_dim, slot, init, head * P + 8 * x_cg,
+                                         cw.w(k), cw.b[k], u);
+                        put(k, u);
+                    }
+                } else {
+                    const float hv[3][8] = {};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        float u[RR];
+                        conv_piece(xraw, k, false, hv, cw.w(k), cw.b[k], u);
+                        put(k, u);
+                    }
+                }
+            }
+        } else
         // x^T planes: column (tid / 16) * CPL + jj, positions 8 tg .. +7 (the rows above)
         if (tid < NXP) {
 #pragma unroll
@@ -982,8 +1359,13 @@ hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((ssd_state_pass_kernel<N, 1, Tin>), dim3(a.nheads * a.batch * levels), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    if constexpr (is_raw<Tin>() && N == 128) {
+        return hipErrorInvalidValue;   // raw pieces at dstate 128 need two heads per workgroup
+    } else {
+        hipLaunchKernelGGL((ssd_state_pass_kernel<N, 1, Tin>), dim3(a.nheads * a.batch * levels), dim3(256), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
 }
 
 template <int N>
@@ -1006,6 +1388,11 @@ hipError_t launch_out(const ScanArgs& a, int64_t total_tokens, hipStream_t strea
 bool chunked_scan_supported(int policy, int nheads, int ngroups, int headdim, int dstate, int chunk) {
     return policy == kPolicyBf16x3 && headdim == P && (dstate == 64 || dstate == 128) && chunk == Q &&
            ngroups > 0 && nheads % ngroups == 0 && nheads / ngroups <= MAXHPG;
+}
+
+bool chunked_raw_supported(int nheads, int ngroups, int headdim, int dstate, int chunk) {
+    if (!chunked_scan_supported(kPolicyBf16x3, nheads, ngroups, headdim, dstate, chunk)) return false;
+    return dstate == 64 || (dstate == 128 && (nheads / ngroups) % 2 == 0);
 }
 
 static size_t r256(size_t v) { return (v + 255) / 256 * 256; }
@@ -1082,13 +1469,25 @@ hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream) {
     }
     const bool f = a.act_dtype == kF32;
     hipError_t e = hipErrorInvalidValue;
-    if (a.dstate == 128) e = f ? launch_pass<128, float>(a, stream) : launch_pass<128, u16>(a, stream);
-    if (a.dstate == 64) e = f ? launch_pass<64, float>(a, stream) : launch_pass<64, u16>(a, stream);
+    if (a.raw_conv) {
+        // (launch_pass picks two heads per workgroup for dstate 128, which the
+        // raw pieces need; chunked_raw_supported admits only those shapes)
+        if (a.dstate == 128) e = launch_pass<128, RawBf16>(a, stream);
+        if (a.dstate == 64) e = launch_pass<64, RawBf16>(a, stream);
+    } else {
+        if (a.dstate == 128) e = f ? launch_pass<128, float>(a, stream) : launch_pass<128, u16>(a, stream);
+        if (a.dstate == 64) e = f ? launch_pass<64, float>(a, stream) : launch_pass<64, u16>(a, stream);
+    }
     if (e != hipSuccess || a.seg == 0) return e;
     return a.dstate == 128 ? launch_carry<128>(a, stream) : launch_carry<64>(a, stream);
 }
 
 hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream) {
+    if (a.raw_conv) {
+        if (a.dstate == 128) return launch_out<128, RawBf16>(a, total_tokens, stream);
+        if (a.dstate == 64) return launch_out<64, RawBf16>(a, total_tokens, stream);
+        return hipErrorInvalidValue;
+    }
     const bool f = a.act_dtype == kF32;
     if (a.dstate == 128) return f ? launch_out<128, float>(a, total_tokens, stream) : launch_out<128, u16>(a, total_tokens, stream);
     if (a.dstate == 64) return f ? launch_out<64, float>(a, total_tokens, stream) : launch_out<64, u16>(a, total_tokens, stream);

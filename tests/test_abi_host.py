@@ -88,10 +88,22 @@ def test_conv_and_norm_reject_bad_arguments():
     assert lib.gated_rmsnorm_group(16, 64, 32, 64, 0, 64, 1e-5, 2, 1, 4, 64, 16, 128, 0, None) == -5
 
 
-def test_workspace_query_and_prefill_workspace_error():
+def test_workspace_query_and_prefill_workspace_error(monkeypatch):
     lib = m2.load()
+    r = lambda v: (v + 255) // 256 * 256
+    scan = lib.ssd_chunk_scan_workspace_size(1000, 1, 64, 64, 128, 8, 128, 1)
+    # bf16 rows at a shape whose scan convolves the raw rows itself: the pre-norm
+    # output and the scan's own buffers, no post-conv activations
     n = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128, 1)
-    assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4
+    assert scan > 0 and n == r(1000 * 4096 * 4) + scan
+    # the four-kernel chain keeps the fp32 post-conv activations as well
+    monkeypatch.setenv("M2SSD_PREFILL_CHAIN", "1")
+    n_chain = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128, 1)
+    assert n_chain == r(1000 * 6144 * 4) + r(1000 * 4096 * 4) + scan
+    monkeypatch.delenv("M2SSD_PREFILL_CHAIN")
+    # an odd number of heads per group at dstate 128 takes the chain
+    n_odd = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 56, 64, 128, 8, 128, 1)
+    assert n_odd >= 1000 * (3584 + 2048) * 4 + 1000 * 3584 * 4
     n32 = lib.mamba2_prefill_workspace_size(1000, 1, 1000, 64, 64, 128, 8, 128, 0)
     assert n32 >= 1000 * (4096 + 2048) * 8 + 1000 * 4096 * 4
     assert lib.mamba2_prefill_workspace_size(-1, 1, 1, 64, 64, 128, 8, 128, 1) == 0
@@ -126,9 +138,10 @@ def test_scan_workspace_query():
     assert lib.ssd_chunk_scan_workspace_size(1000, 3, 64, 64, 128, 8, 128, 0) == expect_f64(3, 64, 64, 128)
     assert lib.ssd_chunk_scan_workspace_size(11, 1, 4, 16, 16, 2, 16, 0) == expect_f64(1, 4, 16, 16)
     assert lib.ssd_chunk_scan_workspace_size(1000, 4, 64, 64, 128, 8, 128, 0) == 0
-    # the prefill workspace includes it, plus fp32 activations and the fp32 pre-norm output
+    # the prefill workspace includes it, plus the fp32 pre-norm output (the scan
+    # convolves the raw bf16 rows itself at this shape)
     n = lib.mamba2_prefill_workspace_size(1000, 3, 1000, 64, 64, 128, 8, 128, 1)
-    assert n >= 1000 * (4096 + 2048) * 4 + 1000 * 4096 * 4 + (1000 // 128 + 3) * per_slot
+    assert n == r(1000 * 4096 * 4) + expect(1000, 3)
 
 
 def _decode(lib, **kw):

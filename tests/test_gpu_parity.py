@@ -3,9 +3,10 @@
 Metric: max|gpu - oracle| / RMS(oracle) per tensor (y, final conv_state, final
 ssm_state), with the element count asserted.  Bars: 1e-4 for fp32 inputs,
 2e-2 for bf16 inputs.  Small shapes span several 16-row tiles, several chunks
-and ragged tails; the full-size workloads are checked on sampled (sequence,
-group) pairs the oracle computes in seconds -- groups are independent
-through the whole mixer core, so a one-group slice is an exact sub-problem.
+and ragged tails; the full-size workloads are checked on every (sequence,
+group) pair, each an exact sub-problem the oracle computes in seconds
+(groups are independent through the whole mixer core), in a pool of host
+processes.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 
 import mamba_ssd_selective_amd as m2
 from oracle import recurrence as R
-from workloads import LayerShape, Workload, WORKLOADS, make_inputs, round_bf16, small_shape_inputs
+from workloads import LayerShape, Workload, WORKLOADS, make_inputs, round_bf16, seqlens_of, small_shape_inputs
 from parity_util import TOL, group_channels, rel_err, slice_group, split_views, tdev, to_device
 
 pytestmark = pytest.mark.gpu
@@ -243,14 +244,6 @@ def test_prefill_nano_137_tokens():
     check_all(inp, w.shape, "bf16", w.chunk_size)
 
 
-def _sampled(w, seed, pairs, act):
-    inp = make_inputs(w, seed)
-    s = w.shape
-    y, cs, ss = gpu_prefill(inp, s, act, w.chunk_size)
-    assert torch.isfinite(y).all() and torch.isfinite(ss).all() and torch.isfinite(cs).all()
-    _check_pairs(inp, s, y, cs, ss, pairs, act)
-
-
 def _check_pairs(inp, s, y, cs, ss, pairs, act):
     """Each (sequence, group) pair of the device results against the oracle run
     on that sequence's rows and that group alone."""
@@ -339,19 +332,55 @@ def test_prefill_many_heads_per_group():
     check_all(inp, shape, "bf16")
 
 
-def test_prefill_decay_stress_full_size():
-    w = WORKLOADS[3]
-    _sampled(w, 3, [(0, 0), (0, 7), (1, 3), (1, 4)], "f32")
+def _all_pairs(w, seed, act, tmp_path):
+    """The full-size workload on the GPU (the launch configuration the bench
+    times), then every (sequence, group) pair against the fp64 oracle, element by
+    element, in a pool of host processes (tests/oracle_pool.py)."""
+    import oracle_pool
+    inp = make_inputs(w, seed)
+    s = w.shape
+    y, cs, ss = gpu_prefill(inp, s, act, w.chunk_size)
+    assert torch.isfinite(y).all() and torch.isfinite(ss).all() and torch.isfinite(cs).all()
+    np.save(tmp_path / "y.npy", y.cpu().numpy())
+    np.save(tmp_path / "ssm_state.npy", ss.cpu().numpy())
+    np.save(tmp_path / "conv_state.npy", cs.cpu().numpy())
+    T = int(inp["cu_seqlens"][-1])
+    del inp, y, cs, ss
+    res = oracle_pool.all_pairs(w, seed, str(tmp_path))
+    tol = TOL[act]
+    assert len(res) == len(seqlens_of(w, seed)) * s.ngroups
+    assert sum(r["y"]["n"] for r in res) == T * s.d_inner
+    worst = {}
+    for r in res:
+        for name in ("y", "ssm_state", "conv_state"):
+            m = r[name]
+            assert m["finite"], f"non-finite {name} at sequence {r['seq']} group {r['group']}"
+            rel = m["err"] / m["rms"] if m["rms"] > 0 else m["err"]
+            if rel > worst.get(name, (-1.0,))[0]:
+                worst[name] = (rel, r["seq"], r["group"], r["len"])
+            assert rel <= tol, f"{name} sequence {r['seq']} group {r['group']}: {rel:.3e} > {tol}"
+    for name, (rel, b, g, L) in worst.items():
+        print(f"  {name}: worst max|err|/rms {rel:.3e} at sequence {b} (len {L}) group {g}; "
+              f"{len(res)} pairs", flush=True)
 
 
-def test_prefill_nano_8x4096_full_size_sampled():
-    w = WORKLOADS[2]
-    _sampled(w, 2, [(0, 0), (3, 5), (7, 7)], "bf16")
+def test_prefill_decay_stress_full_size_all_pairs(tmp_path):
+    _all_pairs(WORKLOADS[3], 3, "f32", tmp_path)
 
 
-def test_prefill_h8b_varlen_full_size_sampled():
-    w = WORKLOADS[4]
-    _sampled(w, 4, [(0, 0), (2, 3), (12, 7)], "bf16")
+def test_prefill_decay_stress_full_size_nonzero_initial_states(tmp_path):
+    """The decay-stress configuration from carried (nonzero) conv and SSM states."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS[3], name="decay_stress_2x2048_f32_carried", init="random")
+    _all_pairs(w, 33, "f32", tmp_path)
+
+
+def test_prefill_nano_8x4096_full_size_all_pairs(tmp_path):
+    _all_pairs(WORKLOADS[2], 2, "bf16", tmp_path)
+
+
+def test_prefill_h8b_varlen_full_size_all_pairs(tmp_path):
+    _all_pairs(WORKLOADS[4], 4, "bf16", tmp_path)
 
 
 def test_prefill_offsets_past_4_gib():

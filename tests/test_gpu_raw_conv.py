@@ -1,0 +1,64 @@
+"""The prefill's scan kernels convolving the raw bf16 rows themselves, against
+the four-kernel chain (conv kernel, fp32 post-conv activations in the
+workspace, selected with M2SSD_PREFILL_CHAIN=1).  Both compute the conv with
+the same operations in the same order and feed the same (hi, lo) products, so
+the conv state must be bitwise equal, and y and the SSM state agree to the
+rounding of the split products (the compiler may fuse the dt weighting of x
+into the low part of the split differently in the two kernels; where that
+moves a value across a bf16 rounding boundary its (hi, lo) pair changes and
+the product with it, at ~1e-5 of the values -- measured: both paths are as far
+from the oracle as from each other; the check allows 1e-3 of the RMS); each is
+also checked against the fp64 oracle at the bf16 bar.  Cases: sequences shorter than the conv's 3-row
+halo (their first rows read the carried conv state), ragged chunk tails,
+empty sequences, dstate 64 (one head per state-pass workgroup), long
+sequences split into segments, the 137-token prompt (chunk output split over
+heads), both gate orders, a fresh slot next to carried ones."""
+import numpy as np
+import pytest
+import torch
+
+import mamba_ssd_selective_amd as m2
+from oracle import recurrence as R
+from workloads import LayerShape, small_shape_inputs
+from parity_util import TOL, rel_err
+from test_gpu_parity import gpu_prefill
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (shape, lengths, init, norm_before_gate)
+    (LayerShape(16, 64, 128, 2), [300, 1, 2, 3, 129, 0, 257], "random", True),
+    (LayerShape(16, 64, 128, 2), [300, 1, 2, 3, 129, 0, 257], "random", False),
+    (LayerShape(8, 64, 64, 4), [513, 3, 0, 128], "pool", True),
+    (LayerShape(16, 64, 128, 2), [2000, 700, 1, 0], "pool", True),
+    (LayerShape(64, 64, 128, 8), [137], "zero", True),
+    (LayerShape(32, 64, 128, 2), [4096], "random", True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_raw_conv_scan_equals_chain_and_oracle(case, monkeypatch):
+    m2.load()
+    shape, lens, init, nbg = CASES[case]
+    inp = small_shape_inputs(shape, lens, seed=200 + case, act="bf16", init=init,
+                             n_slots=len(lens) + 2)
+    if init == "pool":
+        inp["has_init"] = np.array([(b + 1) % 3 != 0 for b in range(len(lens))], dtype=np.uint8)
+    print(f" shape={shape} lens={lens} init={init} nbg={nbg}", flush=True)
+    m2.reset_counters()
+    y, cs, ss = gpu_prefill(inp, shape, "bf16", nbg=nbg)
+    c = m2.get_counters()
+    assert c["conv_launches"] == 0 and c["scan_chunked_launches"] == 1 and c["conv_state_launches"] == 1
+    monkeypatch.setenv("M2SSD_PREFILL_CHAIN", "1")
+    y2, cs2, ss2 = gpu_prefill(inp, shape, "bf16", nbg=nbg)
+    assert m2.get_counters()["conv_launches"] == 1
+    monkeypatch.delenv("M2SSD_PREFILL_CHAIN")
+    assert torch.equal(cs, cs2)
+    assert rel_err(ss, ss2.double().cpu().numpy(), "ssm_state raw vs chain") <= 1e-3
+    assert rel_err(y, y2.double().cpu().numpy(), "y raw vs chain") <= 1e-3
+    ref = R.prefill(inp, shape.nheads, shape.headdim, shape.dstate, shape.ngroups,
+                    norm_before_gate=nbg)
+    tol = TOL["bf16"]
+    assert rel_err(y, ref["y"], "y", sum(lens) * shape.d_inner) <= tol
+    assert rel_err(cs, ref["conv_state"], "conv_state") == 0.0
+    assert rel_err(ss, ref["ssm_state"], "ssm_state") <= tol
