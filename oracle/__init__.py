@@ -10,8 +10,11 @@ code with the HIP library (mamba_ssd_selective_amd) and never imports it.
                  the materialised quadratic form, used to pin the recurrence.
   inproj      -- the packed in-projection row (z | xBC | dt), the step size
                  softplus(dt + bias), and mixed decode + prefill batches.
+  precision   -- the definitions run with one narrower rounding inserted (the
+                 conv output, the per-chunk entry state, a bf16 product), to
+                 measure the error budget behind the library's fp32 choices.
 
 Every function is pinned by a CPU test (tests/test_oracle_pins.py) against a
 closed form, an invariant, a library routine or a hand-derived fixture.
 """
-from . import recurrence, chunked, inproj  # noqa: F401
+from . import recurrence, chunked, inproj, precision  # noqa: F401

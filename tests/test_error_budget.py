@@ -1,0 +1,112 @@
+"""Error budget of the library's storage and product precision (CPU only).
+
+Each check runs the fp64 definitions with one narrower rounding inserted
+(oracle/precision.py) and measures max|err|/RMS against the unrounded result,
+the metric and the 2e-2 bar of the GPU parity checks for bf16 inputs:
+
+  * post-conv activations stored in bf16 alone break the bar, in fp16 alone
+    they land within 2x of it (the state over it), in fp32 they cost nothing:
+    the conv output stays fp32 (or never leaves the chip);
+  * the state entering each chunk stored in bf16 alone reaches the bar, in
+    fp16 it keeps a 4x margin (and fp16's range, 65504, is below the ~2e4-RMS
+    states of the 1e6 decay stress): it stays fp32;
+  * one bf16 matrix product on single bf16 operands carries ~1e-2 of its RMS,
+    on (hi, lo) pairs ~3e-5: fp32 operands enter as pairs.
+
+The precision model itself is pinned first: its roundings match torch's
+bfloat16 / float16 conversions, and with no rounding its chunk form equals
+the token recurrence.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import precision as PR
+from oracle import recurrence as R
+from workloads import NANO, LayerShape, slice_group, small_shape_inputs
+
+BAR = 2e-2
+
+
+def test_roundings_match_torch():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.uniform(-6, 4, 5000),
+                        [0.0, -0.0, 1.0, 65504.0, 1e-8]]).astype(np.float32)
+    tb = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    th = torch.from_numpy(v).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(PR.round_bf16(v), tb)
+    np.testing.assert_array_equal(PR.round_fp16(v), th)
+    np.testing.assert_array_equal(PR.round_fp32(v.astype(np.float64)), v.astype(np.float64))
+
+
+def test_chunk_form_without_rounding_is_the_recurrence():
+    rng = np.random.default_rng(6)
+    L, H, P, N, G = 300, 4, 8, 16, 2
+    x, B, C = rng.standard_normal((L, H, P)), rng.standard_normal((L, G, N)), rng.standard_normal((L, G, N))
+    dt = np.log1p(np.exp(rng.standard_normal((L, H)) - 1.0))
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), H))
+    D = rng.standard_normal(H)
+    h0 = 0.3 * rng.standard_normal((H, P, N))
+    y = PR.entry_state_rounded(x, B, C, dt, A, D, h0, 128, "fp64")
+    ref, _ = R.ssd_recurrence_seq(x, B, C, dt, A, D, h0)
+    assert PR.rel_max(y, ref) < 1e-12
+
+
+def test_split_products_exact_for_bf16_inputs():
+    rng = np.random.default_rng(7)
+    a = PR.round_bf16(rng.standard_normal((32, 64)))
+    b = PR.round_bf16(rng.standard_normal((64, 16)))
+    assert PR.split_product_error(a, b, split=False) == 0.0
+    assert PR.split_product_error(a, b, split=True) == 0.0
+
+
+def test_post_conv_activation_storage():
+    """16 heads x headdim 64, dstate 128, 2 groups; 700 + 300 bf16 rows from
+    carried states."""
+    shape = LayerShape(16, 64, 128, 2)
+    inp = small_shape_inputs(shape, [700, 300], seed=3, act="bf16", init="random")
+    dims = (shape.nheads, shape.headdim, shape.dstate, shape.ngroups)
+    y0, h0 = PR.conv_output_rounded(inp, *dims, "fp64", "fp64")
+    err = {}
+    for name, fx, fbc in (("fp32", "fp32", "fp32"), ("bf16", "bf16", "bf16"), ("fp16", "fp16", "fp16"),
+                          ("x fp16", "fp16", "fp64"), ("B,C fp16", "fp64", "fp16")):
+        y, h = PR.conv_output_rounded(inp, *dims, fx, fbc)
+        err[name] = (PR.rel_max(y, y0), PR.rel_max(h, h0))
+        print(f"  conv output stored {name}: y {err[name][0]:.2e}, state {err[name][1]:.2e}", flush=True)
+    assert max(err["fp32"]) < 2e-5                      # the stored format: ~1000x inside the bar
+    assert min(err["bf16"]) > 2 * BAR                   # bf16 alone breaks the bar (measured 0.09 / 0.125)
+    assert BAR / 2 < err["fp16"][0] < BAR < err["fp16"][1] < 2 * BAR   # fp16: y 1.2e-2, state 2.2e-2
+    assert BAR / 3 < max(err["x fp16"]) < BAR           # x alone in fp16: 1.1e-2 / 1.2e-2, a 1.7x margin
+    assert BAR / 4 < max(err["B,C fp16"]) < BAR         # B, C alone in fp16: 5.8e-3 / 1.1e-2
+
+
+def test_entry_state_storage():
+    """One group (8 heads) of the 8 x 4096 workload's shape, 2048 tokens from
+    a carried state, chunks of 128: the state entering each chunk rounded for
+    that chunk's read-out, y compared after the gated norm."""
+    inp = small_shape_inputs(NANO, [2048], seed=2, act="bf16", init="random")
+    sub, sh = slice_group(inp, NANO, 3)
+    u, _ = R.conv_rows_seq(sub["xbc"], sub["conv_w"], sub["conv_b"], sub["conv_state"][0])
+    x, B, C = R.split_xbc(u, sh.nheads, sh.headdim, 1, sh.dstate)
+    args = (x, B, C, sub["dt"], sub["A"], sub["D"], sub["ssm_state"][0], 128)
+    norm = lambda y: R.gated_rmsnorm_group(y.reshape(len(x), -1), sub["z"], sub["norm_w"], 1e-5, 1)
+    y0 = norm(PR.entry_state_rounded(*args, "fp64"))
+    err = {f: PR.rel_max(norm(PR.entry_state_rounded(*args, f)), y0) for f in ("fp32", "fp16", "bf16")}
+    print("  entry states stored " + ", ".join(f"{k}: y {v:.2e}" for k, v in err.items()), flush=True)
+    assert err["fp32"] < 1e-5
+    assert BAR / 10 < err["fp16"] < BAR / 3             # measured 4.6e-3
+    assert BAR / 2 < err["bf16"]                        # measured 1.9e-2: at the bar
+
+
+@pytest.mark.parametrize("k", [32, 128])
+def test_split_bf16_products(k):
+    """An (M x K) by (K x N) product of N(0, 1) fp32 values, K = 32 (one
+    16x16x32 instruction) and 128 (a chunk)."""
+    rng = np.random.default_rng(8 + k)
+    a, b = rng.standard_normal((128, k)), rng.standard_normal((k, 64))
+    single = PR.split_product_error(a, b, split=False)
+    split = PR.split_product_error(a, b, split=True)
+    print(f"  K={k}: single bf16 {single:.2e}, (hi, lo) pairs {split:.2e}", flush=True)
+    assert single > 2e-3                                # ~2^-8 relative per operand
+    assert split < 1e-4                                 # ~2^-16: the dropped lo.lo and the lo roundings
+    assert single / split > 100
