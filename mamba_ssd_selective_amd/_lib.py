@@ -13,7 +13,9 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libm2ssd.so")
+# M2SSD_LIB names another build of the same library (the ABI tests load the
+# host-sanitized one this way); by default the in-tree libm2ssd.so.
+LIB_PATH = os.environ.get("M2SSD_LIB") or os.path.join(_PKG, "libm2ssd.so")
 
 M2_F32 = 0
 M2_BF16 = 1

@@ -68,6 +68,50 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI
+# layer, for the CPU tests of its argument checks: only m2ssd_api.cpp is
+# rebuilt, its host code instrumented (each -fsanitize= applies to the host
+# compilation only; the device code and the kernel objects are unchanged).
+# Load it with the clang ASan runtime preloaded (asan_runtime()).
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "san", "libm2ssd_san.so")
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime in the ROCm LLVM tree."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    for cand in sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                              "libclang_rt.asan-x86_64.so")), reverse=True):
+        return cand
+    raise RuntimeError("clang ASan runtime not found under the ROCm LLVM tree")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Link libm2ssd_san.so: the kernel objects of build() plus m2ssd_api.cpp with
+    host ASan/UBSan.  Returns its path."""
+    os.makedirs(os.path.join(BUILD, "san"), exist_ok=True)
+    kernels = [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "m2ssd_api.cpp"]
+    if not all(os.path.exists(o) for o in kernels):
+        build(verbose)
+    obj = os.path.join(BUILD, "san", "m2ssd_api.o")
+    cmd = [_hipcc(), "-xhip", "-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+           "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *SAN_FLAGS,
+           "-c", os.path.join(CSRC, "m2ssd_api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libasan",
+           "-o", SAN_LIB, *kernels, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"  linked {SAN_LIB}", flush=True)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
