@@ -10,9 +10,14 @@ step, so every step does identical work.
 
 Prints one JSON line on stdout (progress goes to stderr):
   value        tokens/s of the whole step (sum of sequence lengths / step time)
-  roofline     the dominant kernel's algorithmic bytes per launch over its
-               average launch time (HIP events recorded by the library on the
-               launch stream during the timed steps), against 8 TB/s HBM
+  roofline     step_frac: the step's method bytes (read x|B|C, z, dt and the
+               states; write y and the states) over the step time, against
+               8 TB/s HBM; frac: the dominant kernel's method bytes per launch
+               (kernel_bytes) over its average launch time (HIP events the
+               library records on the launch stream during the timed steps);
+               design_extra_bytes: what that kernel moves beyond its method
+               bytes because of this design's decomposition; traffic: the
+               counter-measured HBM bytes of that kernel (profiles/)
   cpu_baseline the fp64 oracle on a bounded sample of the same input, on the
                host cores, in a process pool over (sequence, group) slices
 
@@ -99,39 +104,56 @@ def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=1536):
 
 # ---------------------------------------------------------------- algorithmic work per kernel
 
-def kernel_bytes(w, T, nseq):
-    """Algorithmic HBM bytes of one launch of each kernel of the prefill chain (bf16 inputs).
+def kernel_bytes(w, T, nseq, raw=True):
+    """Method bytes of one launch of each prefill kernel: the layer's own inputs and
+    outputs a kernel reads or writes, each counted once at its storage width (bf16
+    x|B|C and z, fp32 dt, y and states), plus the stage boundaries the separate
+    kernels keep: the pre-norm output y_pre (fp32, written by the scan, read by
+    the norm) and, on the four-kernel chain, the conv's fp32 output (written by
+    the conv, read by the scan kernels).  Each kernel counts every input it needs
+    for its own function.  The state entering every chunk (written by the state
+    pass, read by the chunk output: the staged carry this design chose) is not
+    a method byte: design_extra_bytes() counts it.
 
-    conv         read x|B|C, write the post-conv activations (fp32)
-    conv_state   read the old and write the new conv state of each sequence
-    scan_pass    read post-conv x, B and dt; write the state entering every
-                 chunk; read the initial and write the final SSM state
-    scan_out     read post-conv x, B, C, dt and the entry state of every chunk;
-                 write y before the norm (fp32)
-    norm         read y (fp32) and z, write the output (fp32)
+    raw (the default prefill at bf16: the scan kernels convolve the raw rows)
+      conv_state   read the old and write the new conv state of each sequence
+      scan_pass    read raw x, B and dt; read the initial, write the final SSM state
+      scan_out     read raw x, B, C and dt; write y_pre
+      norm         read y_pre and z, write y
+    chain (M2SSD_PREFILL_CHAIN=1, fp32 inputs)
+      conv         read x|B|C, write the post-conv activations (fp32; fp64 for fp32 inputs)
+      scan_pass    read post-conv x, B and dt; states as above (fp32 inputs: the
+                   one-pass scan, which also reads C and writes y_pre)
+      scan_out     read post-conv x, B, C and dt; write y_pre
+      norm         as above
     """
     s = w.shape
     act = 2 if w.act == "bf16" else 4
-    di, cd, gn = s.d_inner, s.conv_dim, s.ngroups * s.dstate
-    state = s.nheads * s.headdim * s.dstate * 4
+    di, cd, gn, H = s.d_inner, s.conv_dim, s.ngroups * s.dstate, s.nheads
+    states = nseq * 2 * s.nheads * s.headdim * s.dstate * 4
+    conv_state = nseq * 2 * 3 * cd * 4
+    norm = T * (di * 4 + di * act + di * 4)
     if w.act != "bf16":
-        # fp32 inputs: post-conv activations in fp64 and the one-pass scan, which
-        # reads x, B, C and dt and writes y with the state held on chip
-        return {
-            "conv": T * (cd * 4 + cd * 8),
-            "conv_state": nseq * 2 * 3 * cd * 4,
-            "scan_pass": T * (cd * 8 + s.nheads * 4 + di * 4) + nseq * 2 * state,
-            "scan_out": 0,
-            "norm": T * (di * 4 + di * act + di * 4),
-        }
-    slots = T // w.chunk_size + nseq
-    return {
-        "conv": T * (cd * act + cd * 4),
-        "conv_state": nseq * 2 * 3 * cd * 4,
-        "scan_pass": T * (di * 4 + gn * 4 + s.nheads * 4) + slots * state + nseq * 2 * state,
-        "scan_out": T * (di * 4 + 2 * gn * 4 + s.nheads * 4 + di * 4) + slots * state,
-        "norm": T * (di * 4 + di * act + di * 4),
-    }
+        return {"conv": T * (cd * 4 + cd * 8), "conv_state": conv_state,
+                "scan_pass": T * (cd * 8 + H * 4 + di * 4) + states, "scan_out": 0, "norm": norm}
+    if raw:
+        return {"conv": 0, "conv_state": conv_state,
+                "scan_pass": T * ((di + gn) * act + H * 4) + states,
+                "scan_out": T * (cd * act + H * 4 + di * 4), "norm": norm}
+    return {"conv": T * (cd * act + cd * 4), "conv_state": conv_state,
+            "scan_pass": T * ((di + gn) * 4 + H * 4) + states,
+            "scan_out": T * (cd * 4 + H * 4 + di * 4), "norm": norm}
+
+
+def design_extra_bytes(w, T, nseq):
+    """Bytes a kernel moves beyond its method bytes because of this design's
+    decomposition: the fp32 state entering every chunk slot, written by the state
+    pass and read by the chunk output (the staged carry)."""
+    s = w.shape
+    if w.act != "bf16":
+        return {}
+    entry = (T // w.chunk_size + nseq) * s.nheads * s.headdim * s.dstate * 4
+    return {"scan_pass": entry, "scan_out": entry}
 
 
 # The device sources each measured kernel set is built from: a traffic record holds
@@ -306,6 +328,7 @@ def main():
     log(f"warmup {args.warmup} steps done")
 
     m2.timing_enable(args.steps)
+    m2.reset_counters()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -334,23 +357,28 @@ def main():
         log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
         del src, dst
 
-    kb = kernel_bytes(w, T, nseq)
+    raw = m2.get_counters()["conv_launches"] == 0   # the scan kernels convolved the raw rows
+    kb = kernel_bytes(w, T, nseq, raw)
+    extra = design_extra_bytes(w, T, nseq)
     dom = max(kms, key=kms.get)
+    step_b = fused_bytes(w, T, nseq)
+    step_frac = round(step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if w.act == "bf16":
         achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, dom)}
+        roof = {"step_frac": step_frac, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(w.name, dom), "design_extra_bytes": extra.get(dom, 0)}
     else:
         # fp32 inputs: the one-pass scan on fp64 matrix instructions dominates,
         # against the fp64 peak (algorithmic flops over its time)
         achieved = scan_flops(w, T) / (kms["scan_pass"] * 1e-3) / 1e12
-        roof = {"bound": "fp64", "achieved": round(achieved, 2), "peak": FP64_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP64_PEAK_TFLOPS, 4), "traffic": None}
+        roof = {"step_frac": step_frac, "bound": "fp64", "achieved": round(achieved, 2),
+                "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP64_PEAK_TFLOPS, 4),
+                "traffic": None}
         dom = "scan_pass"
-    roof.update({"kernel": dom,
+    roof.update({"kernel": dom, "path": "raw rows convolved in the scan" if raw else "four-kernel chain",
             "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
-            "step_bytes": fused_bytes(w, T, nseq),
-            "step_frac": round(fused_bytes(w, T, nseq) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_bytes": step_b,
             "scan_tflops_alg": round(scan_flops(w, T) / ((kms["scan_pass"] + kms["scan_out"]) * 1e-3) / 1e12, 2),
             "mfma": mfma_line(w, lens, kms),
             "kernel_ms_all": {k: round(v, 4) for k, v in kms.items()}})
@@ -494,6 +522,7 @@ def run_other_mode(args):
     chain = mode != "decode"
     if chain:
         m2.timing_enable(args.steps)
+    m2.reset_counters()
     # one event pair per step on the launch stream: for decode that brackets the one kernel
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -527,7 +556,7 @@ def run_other_mode(args):
         kms = {k: kt[k + "_ms"] / max(1, kt["calls"]) for k in stages}
         from workloads import Workload
         wl = Workload("x", s, tuple(lens[nd:]), "bf16", "pool")
-        kb = kernel_bytes(wl, T - nd, nseq - nd)
+        kb = kernel_bytes(wl, T - nd, nseq - nd, raw=m2.get_counters()["conv_launches"] == 0)
         if mode == "mixed":
             # the decode rows run on a second stream beside the prefill chain, so
             # the chain's kernel times overlap them: the whole step is the unit
