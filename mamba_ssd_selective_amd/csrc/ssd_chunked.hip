@@ -77,21 +77,41 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
 }
 
 
+// A double moved between lanes by one DPP control (applied to both halves);
+// lanes with no source lane (or outside the row mask) get 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Inclusive prefix sum of a = dt * A over the 128 rows of a chunk on one wave:
-// lane l holds rows 2l and 2l+1 (dt already 0 beyond the chunk's rows).
-__device__ __forceinline__ void gamma_scan(float d0, float d1, float Ah, int lane, double& g0, double& g1) {
+// lane l holds rows 2l and 2l+1 (dt already 0 beyond the chunk's rows).  The
+// lane moves are DPP: row shifts give the scan within each row of 16 lanes,
+// the two row broadcasts carry it across rows, a wave shift makes it exclusive.
+__device__ __forceinline__ void gamma_scan(float d0, float d1, float Ah, double& g0, double& g1) {
     const double a0 = (double)d0 * (double)Ah;
     const double a1 = (double)d1 * (double)Ah;
     double v = a0 + a1;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const double t = __shfl_up(v, s, 64);
-        if (lane >= s) v += t;
-    }
-    double run = __shfl_up(v, 1, 64);
-    if (lane == 0) run = 0.0;
+    v += dpp_f64<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_f64<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_f64<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_f64<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_f64<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    const double run = dpp_f64<0x138, 0xf>(v);   // wave_shr:1
     g0 = run + a0;
     g1 = g0 + a1;
+}
+
+// The value of v in lane l (l uniform), as a uniform double.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ float expc(double v) { return __expf(static_cast<float>(fmin(v, 0.0))); }
@@ -429,6 +449,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
     __shared__ __align__(16) u16 sBTl[NB][SP ? N * RH : 8];  // low parts (fp32 inputs)
     __shared__ __align__(16) u16 sXH[NB][IPW][P * RH];       // (w x)^T [p][token] per item, high parts
     __shared__ __align__(16) u16 sXL[NB][IPW][P * RH];       // low parts
+    __shared__ __align__(16) float sW[4 * IPW][Q];           // per wave: the chunk's weights w_i
 
     const int sub = IPW > 1 ? (int)(threadIdx.x >> 8) : 0;   // item within the workgroup
     const int tid = threadIdx.x & (NT - 1);
@@ -555,10 +576,10 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         d1 = a.dt[(r0 + (2 * lane + 1 < S ? 2 * lane + 1 : S - 1)) * a.ld_dt + head];
     };
 
-    // Stage half h of chunk c from b with weights w0/w1 (rows 2 lane, 2 lane + 1).
+    // Stage half h of chunk c from b, with the weights of this wave's table.
     // Rows past the sequence's end hold re-read (finite) rows and have weight 0
     // (dt is zeroed there), so their (w x) is 0 and they add nothing; no mask.
-    auto stage = [&](Buf& b, int c, int h, float w0, float w1) __attribute__((always_inline)) {
+    auto stage = [&](Buf& b, int c, int h) __attribute__((always_inline)) {
         u16* const BTh = sBTh[h % NB];
         u16* const BTl = sBTl[h % NB];
         u16* const XH = sXH[h % NB][sub];
@@ -570,13 +591,8 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
             raw_halo(b.r, lane);
             float hv[3][8];
             if (start) load_halo(a.conv_state, a.conv_dim, slot, init, r_ch, hv);
-            float wx[RR];
-#pragma unroll
-            for (int t = 0; t < RR; ++t) {
-                const int row = row0 + t;
-                const float wa = __shfl(w0, row >> 1, 64), wb = __shfl(w1, row >> 1, 64);
-                wx[t] = (row & 1) ? wb : wa;
-            }
+            const float4 w4 = *reinterpret_cast<const float4*>(&sW[gwave][row0]);
+            const float wx[RR] = {w4.x, w4.y, w4.z, w4.w};
             const ConvW cw = read_convw(sCW, sCB, r_lch);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -616,11 +632,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         // (w x)^T: weights of rows 64 h + TX x_tg + k, held by lane (64 h + TX x_tg + k) / 2
         float wx[TX];
 #pragma unroll
-        for (int k = 0; k < TX; ++k) {
-            const int row = QH * h + TX * x_tg + k;
-            const float wa = __shfl(w0, row >> 1, 64), wb = __shfl(w1, row >> 1, 64);
-            wx[k] = (row & 1) ? wb : wa;
-        }
+        for (int k = 0; k < TX; ++k) wx[k] = sW[gwave][QH * h + TX * x_tg + k];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             uint32_t wh[TX / 2], wl[TX / 2];
@@ -680,10 +692,13 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         if (2 * lane + 1 >= S) d1 = 0.f;
         // gamma over the chunk (every wave), weights w_i = dt_i e(gamma_S - gamma_i)
         double g0, g1;
-        gamma_scan(d0, d1, Ah, lane, g0, g1);
-        const double gS = __shfl(((S - 1) & 1) ? g1 : g0, (S - 1) >> 1, 64);
+        gamma_scan(d0, d1, Ah, g0, g1);
+        const double gS = ((S - 1) & 1) ? readlane_f64(g1, (S - 1) >> 1) : readlane_f64(g0, (S - 1) >> 1);
         const float w0 = d0 * expc(gS - g0);
         const float w1 = d1 * expc(gS - g1);
+        // this wave's table of the weights (read back by the same wave's lanes:
+        // its LDS operations complete in order)
+        *reinterpret_cast<float2*>(&sW[gwave][2 * lane]) = float2{w0, w1};
         const float decay = expc(gS);
         // entry state of this chunk, then h <- e(gamma_S) h (the stores go out first,
         // so they are the oldest memory operations whenever a later load is awaited)
@@ -712,7 +727,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         const int S0 = S < QH ? S : QH;
         if (NB == 1) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        stage(buf0, c, 0, w0, w1);
+        stage(buf0, c, 0);
         load_half(buf0, c + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -722,7 +737,7 @@ __global__ __launch_bounds__(256 * IPW, IPW == 1 ? 2 : 1) void ssd_state_pass_ke
         const int S1 = S - QH;
         if (NB == 1) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        stage(buf1, c, 1, w0, w1);
+        stage(buf1, c, 1);
         load_half(buf1, c + 1, 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -1106,17 +1121,21 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
         double ga0 = 0.0, ga1 = 0.0;
         float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
         if (wave == 0) {
-            gamma_scan(dr0, dr1, sA[j], lane, ga0, ga1);
+            gamma_scan(dr0, dr1, sA[j], ga0, ga1);
             // rows 2 lane, 2 lane + 1 lie in tile lane / 8, whose last row 16 (lane / 8) + 15
             // is held (as ga1) by lane 8 (lane / 8) + 7
-            const double gr = __shfl(ga1, 8 * (lane >> 3) + 7, 64);
+            double gri[8];
+#pragma unroll
+            for (int it = 0; it < 8; ++it) gri[it] = readlane_f64(ga1, 8 * it + 7);
+            double gr = gri[0];
+#pragma unroll
+            for (int it = 1; it < 8; ++it) gr = (lane >> 3) == it ? gri[it] : gr;
             rf0 = dr0 * expc(gr - ga0);
             rf1 = dr1 * expc(gr - ga1);
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
-                const double gri = __shfl(ga1, 8 * it + 7, 64);
-                cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri) : 0.f;
-                cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri) : 0.f;
+                cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri[it]) : 0.f;
+                cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri[it]) : 0.f;
             }
         }
 
@@ -1349,6 +1368,14 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
     }
 }
 
+
+// x^T plane layout of the raw chunk output: the 32-row block kb of plane row p
+// sits at block kb ^ ((p / 16) % 4).  A consumer's operand read (16 plane rows
+// of one 16-row group, one block) moves as a whole; a producer's store (8 plane
+// rows 8 apart, one block) then spreads over 4 bank windows instead of 2.
+__device__ __forceinline__ int xsw(int kb, int p) { return kb ^ ((p >> 4) & 3); }
+
+
 // ------------------------------------------------------------------ chunk output, raw rows
 //
 // The chunk output for raw bf16 rows, with the waves split by role.  Waves 0-3
@@ -1534,17 +1561,21 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
             double ga0 = 0.0, ga1 = 0.0;
             float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
             if (wave == 0) {
-                gamma_scan(dr0, dr1, sA[j], lane, ga0, ga1);
+                gamma_scan(dr0, dr1, sA[j], ga0, ga1);
                 // rows 2 lane, 2 lane + 1 lie in tile lane / 8, whose last row 16 (lane / 8) + 15
                 // is held (as ga1) by lane 8 (lane / 8) + 7
-                const double gr = __shfl(ga1, 8 * (lane >> 3) + 7, 64);
+                double gri[8];
+#pragma unroll
+                for (int it = 0; it < 8; ++it) gri[it] = readlane_f64(ga1, 8 * it + 7);
+                double gr = gri[0];
+#pragma unroll
+                for (int it = 1; it < 8; ++it) gr = (lane >> 3) == it ? gri[it] : gr;
                 rf0 = dr0 * expc(gr - ga0);
                 rf1 = dr1 * expc(gr - ga1);
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
-                    const double gri = __shfl(ga1, 8 * it + 7, 64);
-                    cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri) : 0.f;
-                    cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri) : 0.f;
+                    cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri[it]) : 0.f;
+                    cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri[it]) : 0.f;
                 }
             }
             // the next head's conv weights into the other buffer (read one phase later)
@@ -1555,30 +1586,37 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
             }
             // conv + SiLU of the x piece: rows 4 x_rg .. + 3 of the chunk, placed at
             // their positions in the K-slot order of the x^T planes (row i sits at
-            // 8 (4 (i / 32) + (i / 4) % 4) + 4 ((i / 16) % 2) + i % 4)
+            // 8 (4 (i / 32) + (i / 4) % 4) + 4 ((i / 16) % 2) + i % 4), the 32-row
+            // block i / 32 swizzled by plane row (xsw)
             {
                 raw_halo(xraw, lane);
                 const int row0 = 4 * x_rg;
                 const bool start = c == 0 && row0 == 0;
-                const int pos = 8 * (4 * (row0 >> 5) + ((row0 >> 2) & 3)) + 4 * ((row0 >> 4) & 1);
+                const int pos = 8 * ((row0 >> 2) & 3) + 4 * ((row0 >> 4) & 1);
                 auto put = [&](int k, float (&u)[RR]) __attribute__((always_inline)) {
+                    if (S < Q) {
 #pragma unroll
-                    for (int tt = 0; tt < RR; ++tt)
-                        if (row0 + tt >= S) u[tt] = 0.f;
+                        for (int tt = 0; tt < RR; ++tt)
+                            if (row0 + tt >= S) u[tt] = 0.f;
+                    }
                     uint32_t hb[2], lb[2];
                     split2(u[0], u[1], hb[0], lb[0]);
                     split2(u[2], u[3], hb[1], lb[1]);
-                    const int off = (8 * x_cg + k) * RS + pos;
+                    const int off = (8 * x_cg + k) * RS + 32 * xsw(row0 >> 5, 8 * x_cg + k) + pos;
                     *reinterpret_cast<uint2*>(Xh + off) = uint2{hb[0], hb[1]};
                     *reinterpret_cast<uint2*>(Xl + off) = uint2{lb[0], lb[1]};
                 };
+                // (the producers have the registers to hold all 8 channels' weights)
                 const ConvW cw = read_convw(sXW[bf], sXB[bf], 8 * x_cg);
+                float4 wv[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) wv[k] = cw.w(k);
                 if (start) {
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         float u[RR];
                         conv_piece_start(xraw, k, a.conv_state, a.conv_dim, slot, init, head * P + 8 * x_cg,
-                                         cw.w(k), cw.b[k], u);
+                                         wv[k], cw.b[k], u);
                         put(k, u);
                     }
                 } else {
@@ -1586,7 +1624,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         float u[RR];
-                        conv_piece(xraw, k, false, hv, cw.w(k), cw.b[k], u);
+                        conv_piece(xraw, k, false, hv, wv[k], cw.b[k], u);
                         put(k, u);
                     }
                 }
@@ -1655,8 +1693,11 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
         auto consumer = [&](auto TAc) __attribute__((always_inline)) {
             constexpr int TA = decltype(TAc)::value;
             constexpr int TB = 7 - TA;
-            const int tA = 16 * TA + l16, tB = 16 * TB + l16;   // this lane's output rows
-            const bool actA = 16 * TA < S, actB = 16 * TB < S;
+            // this lane's output rows.  Tiles past a short chunk's end are
+            // multiplied all the same (their rows are finite: B and C rows are
+            // clamped into the sequence, x rows and dt are 0 there) and not
+            // stored: the products stay free of branches.
+            const int tA = 16 * TA + l16, tB = 16 * TB + l16;
             // C operands of the two tiles (column t, K = n), kept for every head
             bf16x8_t chA[NKB], clA[NKB], chB[NKB], clB[NKB];
             // G^T[i, t] = B_i . C_t for the i tiles it <= T of each tile
@@ -1684,13 +1725,11 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                         clB[k] = as_bf16x8(lds128(Cl + tB * HR + 32 * k2 + 8 * q));
 #pragma unroll
                         for (int it = 0; it <= TB; ++it) {
-                            if (16 * it < S) {
-                                const int row = (16 * it + l16) * HR + 32 * k2 + 8 * q;
-                                const bf16x8_t bh = as_bf16x8(lds128(Bh + row));
-                                const bf16x8_t bl = as_bf16x8(lds128(Bl + row));
-                                if (actB) mma2<true, true>(gtB[it], bh, bl, chB[k], clB[k]);
-                                if (it <= TA && actA) mma2<true, true>(gtA[it], bh, bl, chA[k], clA[k]);
-                            }
+                            const int row = (16 * it + l16) * HR + 32 * k2 + 8 * q;
+                            const bf16x8_t bh = as_bf16x8(lds128(Bh + row));
+                            const bf16x8_t bl = as_bf16x8(lds128(Bl + row));
+                            mma2<true, true>(gtB[it], bh, bl, chB[k], clB[k]);
+                            if (it <= TA) mma2<true, true>(gtA[it], bh, bl, chA[k], clA[k]);
                         }
                     }
                 }
@@ -1722,8 +1761,8 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                     for (int pt = 0; pt < 4; ++pt) {
                         const bf16x8_t ah = as_bf16x8(lds128(HH + (16 * pt + l16) * NRS + 32 * k + 8 * q));
                         const bf16x8_t al = as_bf16x8(lds128(HL + (16 * pt + l16) * NRS + 32 * k + 8 * q));
-                        if (actA) mma2<true, true>(yA[pt], ah, al, chA[k], clA[k]);
-                        if (actB) mma2<true, true>(yB[pt], ah, al, chB[k], clB[k]);
+                        mma2<true, true>(yA[pt], ah, al, chA[k], clA[k]);
+                        mma2<true, true>(yB[pt], ah, al, chB[k], clB[k]);
                     }
                 }
                 {
@@ -1765,16 +1804,20 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                             m[4 * h2 + 2] = gT[it][2] * rf.z * cv;
                             m[4 * h2 + 3] = gT[it][3] * rf.w * cv;
                         } else if (it == TT) {
+                            // the diagonal tile, branch-free: for i > t the clamped
+                            // exponent gives a finite factor that the select drops
                             const double gt = gamb[t];
+                            const float4 d4 = *reinterpret_cast<const float4*>(dtsb + i0);
+                            const double2 ga = *reinterpret_cast<const double2*>(gamb + i0);
+                            const double2 gb = *reinterpret_cast<const double2*>(gamb + i0 + 2);
+                            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+                            const double gv[4] = {ga.x, ga.y, gb.x, gb.y};
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const int i = i0 + r;
-                                float v = 0.f;
-                                if (i <= t) {
-                                    v = gT[it][r] * dtsb[i] * expc(gt - gamb[i]);
-                                    if (i == t) v += Dh;
-                                }
-                                m[4 * h2 + r] = v;
+                                float v = gT[it][r] * dv[r] * expc(gt - gv[r]);
+                                v = (i == t) ? v + Dh : v;
+                                m[4 * h2 + r] = (i <= t) ? v : 0.f;
                             }
                         } else {
 #pragma unroll
@@ -1793,11 +1836,11 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                     if (kb <= TA / 2) mslots(std::integral_constant<int, TA>{}, kb, gtA, cfA, tA, mhA, mlA);
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) {
-                        const int xo = (16 * pt + l16) * RS + 32 * kb + 8 * q;
+                        const int xo = (16 * pt + l16) * RS + 32 * xsw(kb, 16 * pt) + 8 * q;
                         const bf16x8_t xh = as_bf16x8(lds128(Xh + xo));
                         const bf16x8_t xl = as_bf16x8(lds128(Xl + xo));
-                        if (actB) mma2<true, true>(yB[pt], xh, xl, mhB, mlB);
-                        if (kb <= TA / 2 && actA) mma2<true, true>(yA[pt], xh, xl, mhA, mlA);
+                        mma2<true, true>(yB[pt], xh, xl, mhB, mlB);
+                        if (kb <= TA / 2) mma2<true, true>(yA[pt], xh, xl, mhA, mlA);
                     }
                 }
                 // store y rows tA, tB of the chunk: lane has y[t][16 pt + 4q .. +3]
