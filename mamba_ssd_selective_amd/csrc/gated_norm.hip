@@ -12,6 +12,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "norm_row.h"
 
 namespace m2 {
 namespace {
@@ -69,21 +70,8 @@ __global__ __launch_bounds__(BLOCK) void gated_norm_kernel(NormArgs a) {
 
 // Vector form for group widths that are multiples of 8 with 16-byte aligned
 // rows: lane l handles 8-channel blocks l, l + 64, ... of its (token, group),
-// each one 32-byte fp32 load of y and one 16- or 32-byte load of z.
-template <typename T> __device__ __forceinline__ void load8v(const T* p, float (&v)[8]) { load8(p, v); }
-
-__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
-    *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
-}
-__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        w[k] = (uint32_t)f32_to_bf16_bits(v[2 * k]) | ((uint32_t)f32_to_bf16_bits(v[2 * k + 1]) << 16);
-    *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
-}
-
+// each one 32-byte fp32 load of y and one 16- or 32-byte load of z
+// (norm_row.h, shared with the chunk output's fused norm).
 constexpr int MAXB = 4;   // 8-channel blocks per lane: group width up to 2048
 
 template <typename Tz, typename Tout>
@@ -96,47 +84,13 @@ __global__ __launch_bounds__(BLOCK) void gated_norm_vec_kernel(NormArgs a) {
     const int j = (int)(item % a.ngroups);
     const int cbase = j * gs;
     const int nb = gs / 8;
-    const float* yr = a.y + t * a.ld_y + cbase;
-    const Tz* zr = static_cast<const Tz*>(a.z) + t * a.ld_z + cbase;
-
-    float v[MAXB][8], gate[MAXB][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < MAXB; ++k) {
-        const int b = lane + 64 * k;
-        if (b < nb) {
-            float yv[8], zv[8];
-            load8v(yr + 8 * b, yv);
-            load8v(zr + 8 * b, zv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float g = silu(zv[e]);
-                const float u = a.norm_before_gate ? yv[e] : yv[e] * g;
-                v[k][e] = u;
-                gate[k][e] = g;
-                ss = fmaf(u, u, ss);
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    const float rstd = __builtin_amdgcn_rsqf(ss / (float)gs + a.eps);
-
-    Tout* orow = static_cast<Tout*>(a.out) + t * a.ld_out + cbase;
-#pragma unroll
-    for (int k = 0; k < MAXB; ++k) {
-        const int b = lane + 64 * k;
-        if (b < nb) {
-            float wv[8], o[8];
-            load8(a.norm_w + cbase + 8 * b, wv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o[e] = v[k][e] * rstd * wv[e];
-                if (a.norm_before_gate) o[e] *= gate[k][e];
-            }
-            store8(orow + 8 * b, o);
-        }
-    }
+    NormRow<MAXB, Tz> r;
+    NormW<MAXB> W;
+    norm_row_load_y(r, a.y + t * a.ld_y + cbase, nb, lane);
+    norm_row_load_z(r, static_cast<const Tz*>(a.z) + t * a.ld_z + cbase, nb, lane);
+    norm_w_load(W, a.norm_w + cbase, nb, lane);
+    norm_row_store(r, W, static_cast<Tout*>(a.out) + t * a.ld_out + cbase, gs, nb, a.eps, a.norm_before_gate != 0,
+                   lane);
 }
 
 }  // namespace

@@ -82,6 +82,18 @@ struct ScanArgs {
     const float* conv_b;
     const float* conv_state;
     int conv_dim;
+    // Raw chunk output, fuse_norm set (out_split 1): after its heads, each
+    // workgroup applies the grouped gated RMSNorm (norm group = its SSM group)
+    // to its chunk's rows of y, with z (bf16, rows of ld_z), norm_w, eps and
+    // the gate order, writing norm_out (out_dtype; rows of ld_out, may be y
+    // itself for fp32).  The group width (heads per group x headdim) is at
+    // most 2048 and every row 16-byte aligned.
+    int fuse_norm;
+    const void* z; int64_t ld_z;
+    const float* norm_w;
+    float eps;
+    int norm_before_gate;
+    void* norm_out; int64_t ld_out; int out_dtype;
     // One-pass fp64 path, few long sequences split into segments of `seg` steps
     // (seg_levels of them at most; lam holds each segment's total log decay):
     // per (segment, sequence, head) the local end state, then the true one

@@ -567,6 +567,19 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     if (states_ws) m2::chunked_scan_plan(sa, total_tokens, max_seqlen);
     else m2::one_pass_plan(sa, max_seqlen, seg_ws);
     if (batch == 1) sa.order = nullptr;  // one sequence: no order to compute
+    // The raw chunk output applies the norm itself when each of its workgroups
+    // holds a whole norm group (out_split 1) and every row is 16-byte aligned.
+    {
+        const int gs = d_x / ngroups;
+        const int oes = y_dtype == M2_BF16 ? 2 : 4;
+        const bool al = aligned16(ypre) && aligned16(z) && aligned16(y) && aligned16(norm_w) &&
+                        (ld_pre * 4) % 16 == 0 && (ld_z * 2) % 16 == 0 && (ld_y * oes) % 16 == 0;
+        if (raw && sa.out_split <= 1 && gs % 8 == 0 && gs <= 2048 && al && total_tokens > 0) {
+            sa.fuse_norm = 1;
+            sa.z = z; sa.ld_z = ld_z; sa.norm_w = norm_w; sa.eps = eps; sa.norm_before_gate = norm_before_gate;
+            sa.norm_out = y; sa.ld_out = ld_y; sa.out_dtype = y_dtype;
+        }
+    }
     if ((st = launch_scan(sa, total_tokens, s, tev ? tev[raw ? 1 : 3] : nullptr))) return st;
     if (raw) {
         mark(2);
@@ -577,7 +590,7 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
         mark(4);
     }
 
-    if (total_tokens > 0) {
+    if (total_tokens > 0 && !sa.fuse_norm) {
         m2::NormArgs na{};
         na.y = ypre; na.ld_y = ld_pre; na.z = z; na.ld_z = ld_z; na.z_dtype = act_dtype;
         na.norm_w = norm_w; na.eps = eps; na.ngroups = ngroups; na.norm_before_gate = norm_before_gate;

@@ -51,6 +51,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "norm_row.h"
 
 namespace m2 {
 namespace {
@@ -1376,6 +1377,44 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_kernel(ScanArgs a) {
 __device__ __forceinline__ int xsw(int kb, int p) { return kb ^ ((p >> 4) & 3); }
 
 
+// The fused norm of a chunk's rows i0, i0 + 8, ... (one wave per row, NR rows'
+// loads in flight at once, NBL 8-channel blocks per lane): see norm_row.h.  The
+// first rows' z and the weights are loaded before the barrier that makes y
+// visible (they do not depend on it), y after it.
+template <typename Tout, int NBL, int NR>
+__device__ __forceinline__ void chunk_norm_rows(const ScanArgs& a, int64_t r0, int S, int cbase, int gs, int i0,
+                                                int lane) {
+    const int nb = gs / 8;
+    const uint16_t* zb = static_cast<const uint16_t*>(a.z);
+    Tout* ob = static_cast<Tout*>(a.norm_out);
+    NormRow<NBL, uint16_t> r[NR];
+    NormW<NBL> W;
+    auto load_z = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int row = i + 8 * k < S ? i + 8 * k : (i < S ? i : 0);
+            norm_row_load_z(r[k], zb + (r0 + row) * a.ld_z + cbase, nb, lane);
+        }
+    };
+    load_z(i0);
+    norm_w_load(W, a.norm_w + cbase, nb, lane);
+    __syncthreads();   // every wave's y stores are visible
+    for (int i = i0; i < S; i += 8 * NR) {
+        if (i != i0) load_z(i);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int row = i + 8 * k < S ? i + 8 * k : i;
+            norm_row_load_y(r[k], a.y + (r0 + row) * a.ld_y + cbase, nb, lane);
+        }
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            if (i + 8 * k < S)
+                norm_row_store(r[k], W, ob + (r0 + i + 8 * k) * a.ld_out + cbase, gs, nb, a.eps,
+                               a.norm_before_gate != 0, lane);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ chunk output, raw rows
 //
 // The chunk output for raw bf16 rows, with the waves split by role.  Waves 0-3
@@ -1866,6 +1905,302 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
             default: consumer(std::integral_constant<int, 3>{}); break;
         }
     }
+
+    if (a.fuse_norm) {
+        // The grouped gated RMSNorm of this chunk's rows over this group's
+        // channels, wave w the rows w, w + 8, ..., read back while they are
+        // still in cache.  (The norm's barrier sits inside chunk_norm_rows.)
+        const int gs = hpg * P;
+        const int nbl = (gs / 8 + 63) / 64;
+        if (a.out_dtype == kBF16) {
+            if (nbl == 1) chunk_norm_rows<uint16_t, 1, 8>(a, r0, S, grp * gs, gs, wave, lane);
+            else if (nbl == 2) chunk_norm_rows<uint16_t, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
+            else chunk_norm_rows<uint16_t, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
+        } else {
+            if (nbl == 1) chunk_norm_rows<float, 1, 8>(a, r0, S, grp * gs, gs, wave, lane);
+            else if (nbl == 2) chunk_norm_rows<float, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
+            else chunk_norm_rows<float, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ state pass, raw rows
+//
+// The state pass for raw bf16 rows at dstate 128, two heads of one group per
+// workgroup, with the waves split by role like the raw chunk output.  The walk
+// goes in units of half a chunk (64 rows).  Waves 0-3 (producers) convolve and
+// stage the next unit: each thread one x piece (waves 0-1 the first head's x,
+// waves 2-3 the second's; 4 rows x 8 channels, times the rows' weights w_i) and
+// one B piece (16 row groups x 16 channel groups over the 4 waves), and at a
+// chunk's first unit the gamma scan of its head, the weights and the decay.
+// Waves 4-7 (consumers) hold h^T of both heads in matrix-core accumulators,
+// consumer w the n tile w of each head (both p tiles), so the B operand it
+// reads serves four tiles; they store the entry state and scale by the decay
+// at a chunk's start, and multiply the current unit.  A producer and a
+// consumer share each SIMD, so the conv's vector work runs beside the
+// products.
+template <int N>
+__global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
+    static_assert(N == 128, "two heads of 64 B channels each");
+    constexpr int IPW = 2;
+    constexpr int NCW = IPW * P + N;                   // conv channels of the workgroup
+    __shared__ float4 sCW[NCW];                        // their conv weights (slots wsw)
+    __shared__ __align__(16) float sCB[NCW];           // and biases (channel order)
+    __shared__ __align__(16) u16 sBTh[2][N * RH];      // per unit buffer: B^T [n][row of the half], high parts
+    __shared__ __align__(16) u16 sBTl[2][N * RH];      // low parts
+    __shared__ __align__(16) u16 sXH[2][IPW][P * RH];  // (w x)^T [p][row] per head, high parts
+    __shared__ __align__(16) u16 sXL[2][IPW][P * RH];  // low parts
+    __shared__ __align__(16) float sW[4][Q];           // per producer wave: its head's weights w_i of the chunk
+    __shared__ float sDecay[IPW];                      // e(gamma_S) of the chunk being started, per head
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int l32 = lane & 31, g32 = lane >> 5;
+    // grid: one level of batch * nheads / 2 workgroups per segment index
+    const int level = a.nheads * a.batch / IPW;
+    const int seg_k = (int)blockIdx.x / level;
+    int seq, head0;
+    state_item((int)blockIdx.x % level, a, IPW, 0, seq, head0);
+    const int hpg = a.nheads / a.ngroups;
+    const int grp = head0 / hpg;
+    const int64_t s0 = a.cu_seqlens[seq];
+    const int64_t L = a.cu_seqlens[seq + 1] - s0;
+    // segment seg_k of this sequence has no chunk
+    if (seg_k > 0 && (int64_t)seg_k * a.seg * Q >= L) return;
+    const int slot = a.state_idx ? a.state_idx[seq] : seq;
+    const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
+    if (L <= 0) {
+        // Empty sequence: a fresh slot is still reset, a carried one is untouched.
+        if (!init) {
+            for (int e = tid; e < IPW * P * N / 4; e += 512) {
+                float* st = a.ssm_state + ((int64_t)slot * a.nheads + head0 + e / (P * N / 4)) * (int64_t)(P * N);
+                *reinterpret_cast<float4*>(st + 4 * (e % (P * N / 4))) = float4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        return;
+    }
+    const int d_inner = a.nheads * P;
+    for (int e = tid; e < NCW; e += 512) {
+        const int ch = e < IPW * P ? (head0 + e / P) * P + e % P : d_inner + grp * N + (e - IPW * P);
+        sCW[wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
+        sCB[e] = a.conv_b ? a.conv_b[ch] : 0.f;
+    }
+
+    const int nch = (int)((L + Q - 1) / Q);
+    const int64_t cbase = s0 / Q + seq;   // entry-state slot of the sequence's first chunk
+    // this workgroup's chunks: all of them, or segment seg_k's (a later segment
+    // starts from zero; its first entry slot belongs to the segment before)
+    // (the last level runs to the sequence's end)
+    const int cfirst = seg_k * a.seg;
+    const int cend = a.seg > 0 && seg_k < a.seg_levels - 1 ? (cfirst + a.seg < nch ? cfirst + a.seg : nch) : nch;
+
+    if (wave < 4) {
+        // ---------------------------------------------------------- producers
+        const int hp = wave >> 1;              // the head of this wave's x pieces
+        const int head = head0 + hp;
+        const float Ah = a.A[head];
+        const int rg = (lane & 7) + 8 * (wave & 1);   // row group: rows 4 rg .. + 3 of a half
+        const int xcg = lane >> 3;                    // x channel group (8 channels)
+        const int bcg = (lane >> 3) + 8 * hp;         // B channel group (of 16)
+        const uint16_t* xcol = static_cast<const uint16_t*>(a.x) + head * a.hs_x + 8 * xcg;
+        const uint16_t* bcol = static_cast<const uint16_t*>(a.B) + grp * a.gs_B + 8 * bcg;
+        const int xch = head * P + 8 * xcg, bch = d_inner + grp * N + 8 * bcg;   // first xBC channels
+        const int xlw = hp * P + 8 * xcg, blw = IPW * P + 8 * bcg;               // their weights in LDS
+        RawBuf bx0, bx1, bb0, bb1;   // the pieces of each half, refilled a chunk ahead
+        float d0, d1;                // dt of the next chunk to start (rows 2 lane, 2 lane + 1)
+        double lrun = 0.0;           // log decay from the segment's start
+        auto load_half = [&](RawBuf& bx, RawBuf& bb, int c, int h) __attribute__((always_inline)) {
+            c = c < cend ? c : cend - 1;
+            const int lo = (int)(-(int64_t)c * Q), hi = (int)(L - 1 - (int64_t)c * Q);
+            load_raw_piece(xcol + (s0 + (int64_t)c * Q) * a.ld_x, (int)a.ld_x, h * QH + 4 * rg, lo, hi,
+                           (lane & 7) == 0, bx.r);
+            load_raw_piece(bcol + (s0 + (int64_t)c * Q) * a.ld_B, (int)a.ld_B, h * QH + 4 * rg, lo, hi,
+                           (lane & 7) == 0, bb.r);
+        };
+        auto load_dt = [&](int c) __attribute__((always_inline)) {
+            c = c < cend ? c : cend - 1;
+            const int64_t r0 = s0 + (int64_t)c * Q;
+            const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
+            d0 = a.dt[(r0 + (2 * lane < S ? 2 * lane : S - 1)) * a.ld_dt + head];
+            d1 = a.dt[(r0 + (2 * lane + 1 < S ? 2 * lane + 1 : S - 1)) * a.ld_dt + head];
+        };
+        // conv + SiLU of one piece of half h of chunk c; x rows are then weighted
+        auto conv_store = [&](RawBuf& b, int c, int h, bool isx) __attribute__((always_inline)) {
+            const int row0 = QH * h + 4 * rg;             // first row of the piece in the chunk
+            const bool start = c == 0 && row0 == 0;       // the piece starts the sequence
+            raw_halo(b.r, lane);
+            float hv[3][8];
+            if (start) load_halo(a.conv_state, a.conv_dim, slot, init, isx ? xch : bch, hv);
+            float wx[RR] = {1.f, 1.f, 1.f, 1.f};
+            if (isx) {
+                const float4 w4 = *reinterpret_cast<const float4*>(&sW[wave][row0]);
+                wx[0] = w4.x; wx[1] = w4.y; wx[2] = w4.z; wx[3] = w4.w;
+            }
+            const ConvW cw = read_convw(sCW, sCB, isx ? xlw : blw);
+            u16* const dh = isx ? sXH[h][hp] : sBTh[h];
+            u16* const dl = isx ? sXL[h][hp] : sBTl[h];
+            const int cg = isx ? xcg : bcg;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float u[RR];
+                conv_piece(b.r, k, start, hv, cw.w(k), cw.b[k], u);
+                uint32_t wh[RR / 2], wl[RR / 2];
+#pragma unroll
+                for (int m = 0; m < RR / 2; ++m)
+                    split2(u[2 * m] * wx[2 * m], u[2 * m + 1] * wx[2 * m + 1], wh[m], wl[m]);
+                store_tokens<RR>(dh + (8 * cg + k) * RH + 4 * rg, wh);
+                store_tokens<RR>(dl + (8 * cg + k) * RH + 4 * rg, wl);
+            }
+        };
+        // a chunk's start: gamma of this wave's head, the weights w_i = dt_i
+        // e(gamma_S - gamma_i) into this wave's table, the decay for the consumers
+        auto start_chunk = [&](int c) __attribute__((always_inline)) {
+            const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
+            if (2 * lane >= S) d0 = 0.f;
+            if (2 * lane + 1 >= S) d1 = 0.f;
+            double g0, g1;
+            gamma_scan(d0, d1, Ah, g0, g1);
+            const double gS = ((S - 1) & 1) ? readlane_f64(g1, (S - 1) >> 1) : readlane_f64(g0, (S - 1) >> 1);
+            // (read back by this wave's own lanes: its LDS operations complete in order)
+            *reinterpret_cast<float2*>(&sW[wave][2 * lane]) = float2{d0 * expc(gS - g0), d1 * expc(gS - g1)};
+            if ((wave & 1) == 0 && lane == 0) {
+                sDecay[hp] = expc(gS);
+                if (seg_k > 0 && c > cfirst) a.cum[(cbase + c) * a.nheads + head] = lrun;
+            }
+            lrun += gS;
+            load_dt(c + 1);
+        };
+
+        load_dt(cfirst);
+        __builtin_amdgcn_sched_barrier(0);
+        load_half(bx0, bb0, cfirst, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_half(bx1, bb1, cfirst, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();   // conv weights
+        start_chunk(cfirst);
+        conv_store(bx0, cfirst, 0, true);
+        conv_store(bb0, cfirst, 0, false);
+        load_half(bx0, bb0, cfirst + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();   // unit (cfirst, 0) staged
+        for (int c = cfirst; c < cend; ++c) {
+            conv_store(bx1, c, 1, true);
+            conv_store(bb1, c, 1, false);
+            load_half(bx1, bb1, c + 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();   // unit (c, 0) multiplied, (c, 1) staged
+            if (c + 1 < cend) {
+                start_chunk(c + 1);
+                conv_store(bx0, c + 1, 0, true);
+                conv_store(bb0, c + 1, 0, false);
+                load_half(bx0, bb0, c + 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();   // unit (c, 1) multiplied, (c + 1, 0) staged
+        }
+        if (!(cend == nch && seg_k == 0) && seg_k > 0 && (wave & 1) == 0 && lane == 0)
+            a.lam[(cbase + cfirst) * a.nheads + head] = lrun;
+    } else {
+        // ---------------------------------------------------------- consumers
+        const int cw = wave - 4;   // n tile of both heads' states
+        // acc[hh][pt]: head hh, p tile pt; lane l has p = 32 pt + l % 32 and, in
+        // registers 4m .. 4m + 3, n = 32 cw + 8m + 4 (l / 32) + 0..3
+        f32x16_t acc[IPW][2];
+        auto soff = [&](int pt, int m) { return (32 * pt + l32) * N + 32 * cw + 8 * m + 4 * g32; };
+        // entry states in accumulator order: float4 ((tile * 4 + m) * 64 + lane), tile = 2 cw + pt
+        auto eoff = [&](int pt, int m) { return 4 * (((2 * cw + pt) * 4 + m) * 64 + lane); };
+#pragma unroll
+        for (int hh = 0; hh < IPW; ++hh) {
+            const float* st = a.ssm_state + ((int64_t)slot * a.nheads + head0 + hh) * (int64_t)(P * N);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    float4 v = float4{0.f, 0.f, 0.f, 0.f};
+                    if (init && seg_k == 0) v = *reinterpret_cast<const float4*>(st + soff(pt, m));
+                    acc[hh][pt][4 * m + 0] = v.x; acc[hh][pt][4 * m + 1] = v.y;
+                    acc[hh][pt][4 * m + 2] = v.z; acc[hh][pt][4 * m + 3] = v.w;
+                }
+        }
+        // h^T += B^T (w x) over the 16-row K blocks of a staged half
+        auto multiply = [&](int nkb, int h) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < QH / 16; ++k) {
+                if (k < nkb) {
+                    const int bo = (32 * cw + l32) * RH + 16 * k + 8 * g32;
+                    const bf16x8_t bh = as_bf16x8(lds128(sBTh[h] + bo));
+                    const bf16x8_t bl = as_bf16x8(lds128(sBTl[h] + bo));
+#pragma unroll
+                    for (int hh = 0; hh < IPW; ++hh)
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt) {
+                            const int xo = (32 * pt + l32) * RH + 16 * k + 8 * g32;
+                            const bf16x8_t xh = as_bf16x8(lds128(sXH[h][hh] + xo));
+                            const bf16x8_t xl = as_bf16x8(lds128(sXL[h][hh] + xo));
+                            mma32<true, true>(acc[hh][pt], bh, bl, xh, xl);
+                        }
+                }
+            }
+        };
+        __syncthreads();   // conv weights
+        __syncthreads();   // unit (cfirst, 0) staged
+        for (int c = cfirst; c < cend; ++c) {
+            const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
+            // entry state of this chunk, then h <- e(gamma_S) h
+            const bool store = seg_k == 0 || c > cfirst;
+#pragma unroll
+            for (int hh = 0; hh < IPW; ++hh) {
+                float* he = a.states + ((cbase + c) * a.nheads + head0 + hh) * (int64_t)(P * N);
+                const float decay = sDecay[hh];
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    if (store) {
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            *reinterpret_cast<float4*>(he + eoff(pt, m)) =
+                                float4{acc[hh][pt][4 * m], acc[hh][pt][4 * m + 1], acc[hh][pt][4 * m + 2],
+                                       acc[hh][pt][4 * m + 3]};
+                    }
+                    acc[hh][pt] *= decay;
+                }
+            }
+            const int S0 = S < QH ? S : QH;
+            multiply((S0 + 15) >> 4, 0);
+            __syncthreads();
+            const int S1 = S - QH;
+            multiply(S1 > 0 ? (S1 + 15) >> 4 : 0, 1);
+            __syncthreads();
+        }
+        // The end state: the sequence's final state when this is its only segment;
+        // otherwise a local end state, left in the next segment's first entry slot
+        // (for segment 0 that is already the true entry state there) or, for the
+        // last segment, in seg_end, for the carry kernel to complete.
+#pragma unroll
+        for (int hh = 0; hh < IPW; ++hh) {
+            const int head = head0 + hh;
+            if (cend == nch && seg_k == 0) {
+                float* st = a.ssm_state + ((int64_t)slot * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        *reinterpret_cast<float4*>(st + soff(pt, m)) =
+                            float4{acc[hh][pt][4 * m], acc[hh][pt][4 * m + 1], acc[hh][pt][4 * m + 2],
+                                   acc[hh][pt][4 * m + 3]};
+            } else {
+                float* he = cend < nch ? a.states + ((cbase + cend) * a.nheads + head) * (int64_t)(P * N)
+                                       : a.seg_end + ((int64_t)seq * a.nheads + head) * (int64_t)(P * N);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        *reinterpret_cast<float4*>(he + eoff(pt, m)) =
+                            float4{acc[hh][pt][4 * m], acc[hh][pt][4 * m + 1], acc[hh][pt][4 * m + 2],
+                                   acc[hh][pt][4 * m + 3]};
+            }
+        }
+    }
 }
 
 template <int N, typename Tin>
@@ -1873,8 +2208,12 @@ hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
     const unsigned levels = a.seg > 0 ? (unsigned)a.seg_levels : 1u;
     if constexpr (N == 128) {
         if ((a.nheads / a.ngroups) % 2 == 0) {
-            hipLaunchKernelGGL((ssd_state_pass_kernel<N, 2, Tin>), dim3(a.nheads * a.batch / 2 * levels), dim3(512),
-                               0, stream, a);
+            if constexpr (is_raw<Tin>())
+                hipLaunchKernelGGL(ssd_state_pass_raw_kernel<N>, dim3(a.nheads * a.batch / 2 * levels), dim3(512),
+                                   0, stream, a);
+            else
+                hipLaunchKernelGGL((ssd_state_pass_kernel<N, 2, Tin>), dim3(a.nheads * a.batch / 2 * levels),
+                                   dim3(512), 0, stream, a);
             return hipGetLastError();
         }
     }
