@@ -1927,18 +1927,19 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
 // ------------------------------------------------------------------ state pass, raw rows
 //
 // The state pass for raw bf16 rows at dstate 128, two heads of one group per
-// workgroup, with the waves split by role like the raw chunk output.  The walk
-// goes in units of half a chunk (64 rows).  Waves 0-3 (producers) convolve and
-// stage the next unit: each thread one x piece (waves 0-1 the first head's x,
-// waves 2-3 the second's; 4 rows x 8 channels, times the rows' weights w_i) and
-// one B piece (16 row groups x 16 channel groups over the 4 waves), and at a
-// chunk's first unit the gamma scan of its head, the weights and the decay.
-// Waves 4-7 (consumers) hold h^T of both heads in matrix-core accumulators,
-// consumer w the n tile w of each head (both p tiles), so the B operand it
-// reads serves four tiles; they store the entry state and scale by the decay
-// at a chunk's start, and multiply the current unit.  A producer and a
-// consumer share each SIMD, so the conv's vector work runs beside the
-// products.
+// workgroup, with the waves split by role.  The walk goes in units of half a
+// chunk (64 rows).  Waves 0-3 (producers) convolve the next unit's x: waves 0-1
+// the first head's, 2-3 the second's, each thread a piece of 4 rows x 8
+// channels, weighted by the rows' w_i; at a chunk's first unit they also run
+// the gamma scan of their head, the weights and the decay.  Waves 4-7
+// (consumers) hold h^T of both heads in matrix-core accumulators, consumer w
+// the n tile w of each head (both p tiles), so each B operand read serves four
+// tiles; they convolve the next unit's B (16 row groups x 16 channel groups
+// over their 256 threads) in the same stretch of code as the current unit's
+// products, so the conv's vector work fills the gaps between matrix
+// instructions, and at a chunk's start they store the entry state and scale
+// by the decay.  Every SIMD then holds one producer and one consumer, both
+// convolving.
 template <int N>
 __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
     static_assert(N == 128, "two heads of 64 B channels each");
@@ -1994,63 +1995,58 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
     const int cfirst = seg_k * a.seg;
     const int cend = a.seg > 0 && seg_k < a.seg_levels - 1 ? (cfirst + a.seg < nch ? cfirst + a.seg : nch) : nch;
 
+    // One raw piece (4 rows x 8 channels, rows 4 rg .. of half h) of chunk c,
+    // refilled a chunk ahead; and its conv + SiLU into the unit's LDS planes,
+    // times the rows' weights when wt is given (x) or not (B).
+    const int rg = (lane & 7) + 8 * (wave & 1);   // row group of both roles' pieces
+    auto load_piece = [&](RawBuf& b, const uint16_t* col, int64_t ld, int c, int h) __attribute__((always_inline)) {
+        c = c < cend ? c : cend - 1;
+        load_raw_piece(col + (s0 + (int64_t)c * Q) * ld, (int)ld, h * QH + 4 * rg, (int)(-(int64_t)c * Q),
+                       (int)(L - 1 - (int64_t)c * Q), (lane & 7) == 0, b.r);
+    };
+    auto conv_store = [&](RawBuf& b, int c, int h, int ch, int lw, const float* wt, u16* dh, u16* dl, int cg)
+        __attribute__((always_inline)) {
+        const int row0 = QH * h + 4 * rg;             // first row of the piece in the chunk
+        const bool start = c == 0 && row0 == 0;       // the piece starts the sequence
+        raw_halo(b.r, lane);
+        float hv[3][8];
+        if (start) load_halo(a.conv_state, a.conv_dim, slot, init, ch, hv);
+        float wx[RR] = {1.f, 1.f, 1.f, 1.f};
+        if (wt) {
+            const float4 w4 = *reinterpret_cast<const float4*>(wt + row0);
+            wx[0] = w4.x; wx[1] = w4.y; wx[2] = w4.z; wx[3] = w4.w;
+        }
+        const ConvW cw = read_convw(sCW, sCB, lw);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float u[RR];
+            conv_piece(b.r, k, start, hv, cw.w(k), cw.b[k], u);
+            uint32_t wh[RR / 2], wl[RR / 2];
+#pragma unroll
+            for (int m = 0; m < RR / 2; ++m)
+                split2(u[2 * m] * wx[2 * m], u[2 * m + 1] * wx[2 * m + 1], wh[m], wl[m]);
+            store_tokens<RR>(dh + (8 * cg + k) * RH + 4 * rg, wh);
+            store_tokens<RR>(dl + (8 * cg + k) * RH + 4 * rg, wl);
+        }
+    };
+
     if (wave < 4) {
         // ---------------------------------------------------------- producers
         const int hp = wave >> 1;              // the head of this wave's x pieces
         const int head = head0 + hp;
         const float Ah = a.A[head];
-        const int rg = (lane & 7) + 8 * (wave & 1);   // row group: rows 4 rg .. + 3 of a half
-        const int xcg = lane >> 3;                    // x channel group (8 channels)
-        const int bcg = (lane >> 3) + 8 * hp;         // B channel group (of 16)
+        const int xcg = lane >> 3;             // x channel group (8 channels)
         const uint16_t* xcol = static_cast<const uint16_t*>(a.x) + head * a.hs_x + 8 * xcg;
-        const uint16_t* bcol = static_cast<const uint16_t*>(a.B) + grp * a.gs_B + 8 * bcg;
-        const int xch = head * P + 8 * xcg, bch = d_inner + grp * N + 8 * bcg;   // first xBC channels
-        const int xlw = hp * P + 8 * xcg, blw = IPW * P + 8 * bcg;               // their weights in LDS
-        RawBuf bx0, bx1, bb0, bb1;   // the pieces of each half, refilled a chunk ahead
+        const int xch = head * P + 8 * xcg, xlw = hp * P + 8 * xcg;   // first xBC channel, its weights in LDS
+        RawBuf bx0, bx1;             // the pieces of each half
         float d0, d1;                // dt of the next chunk to start (rows 2 lane, 2 lane + 1)
         double lrun = 0.0;           // log decay from the segment's start
-        auto load_half = [&](RawBuf& bx, RawBuf& bb, int c, int h) __attribute__((always_inline)) {
-            c = c < cend ? c : cend - 1;
-            const int lo = (int)(-(int64_t)c * Q), hi = (int)(L - 1 - (int64_t)c * Q);
-            load_raw_piece(xcol + (s0 + (int64_t)c * Q) * a.ld_x, (int)a.ld_x, h * QH + 4 * rg, lo, hi,
-                           (lane & 7) == 0, bx.r);
-            load_raw_piece(bcol + (s0 + (int64_t)c * Q) * a.ld_B, (int)a.ld_B, h * QH + 4 * rg, lo, hi,
-                           (lane & 7) == 0, bb.r);
-        };
         auto load_dt = [&](int c) __attribute__((always_inline)) {
             c = c < cend ? c : cend - 1;
             const int64_t r0 = s0 + (int64_t)c * Q;
             const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
             d0 = a.dt[(r0 + (2 * lane < S ? 2 * lane : S - 1)) * a.ld_dt + head];
             d1 = a.dt[(r0 + (2 * lane + 1 < S ? 2 * lane + 1 : S - 1)) * a.ld_dt + head];
-        };
-        // conv + SiLU of one piece of half h of chunk c; x rows are then weighted
-        auto conv_store = [&](RawBuf& b, int c, int h, bool isx) __attribute__((always_inline)) {
-            const int row0 = QH * h + 4 * rg;             // first row of the piece in the chunk
-            const bool start = c == 0 && row0 == 0;       // the piece starts the sequence
-            raw_halo(b.r, lane);
-            float hv[3][8];
-            if (start) load_halo(a.conv_state, a.conv_dim, slot, init, isx ? xch : bch, hv);
-            float wx[RR] = {1.f, 1.f, 1.f, 1.f};
-            if (isx) {
-                const float4 w4 = *reinterpret_cast<const float4*>(&sW[wave][row0]);
-                wx[0] = w4.x; wx[1] = w4.y; wx[2] = w4.z; wx[3] = w4.w;
-            }
-            const ConvW cw = read_convw(sCW, sCB, isx ? xlw : blw);
-            u16* const dh = isx ? sXH[h][hp] : sBTh[h];
-            u16* const dl = isx ? sXL[h][hp] : sBTl[h];
-            const int cg = isx ? xcg : bcg;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float u[RR];
-                conv_piece(b.r, k, start, hv, cw.w(k), cw.b[k], u);
-                uint32_t wh[RR / 2], wl[RR / 2];
-#pragma unroll
-                for (int m = 0; m < RR / 2; ++m)
-                    split2(u[2 * m] * wx[2 * m], u[2 * m + 1] * wx[2 * m + 1], wh[m], wl[m]);
-                store_tokens<RR>(dh + (8 * cg + k) * RH + 4 * rg, wh);
-                store_tokens<RR>(dl + (8 * cg + k) * RH + 4 * rg, wl);
-            }
         };
         // a chunk's start: gamma of this wave's head, the weights w_i = dt_i
         // e(gamma_S - gamma_i) into this wave's table, the decay for the consumers
@@ -2070,46 +2066,56 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
             lrun += gS;
             load_dt(c + 1);
         };
+        auto stage_x = [&](RawBuf& b, int c, int h) __attribute__((always_inline)) {
+            conv_store(b, c, h, xch, xlw, sW[wave], sXH[h][hp], sXL[h][hp], xcg);
+        };
 
         load_dt(cfirst);
         __builtin_amdgcn_sched_barrier(0);
-        load_half(bx0, bb0, cfirst, 0);
+        load_piece(bx0, xcol, a.ld_x, cfirst, 0);
         __builtin_amdgcn_sched_barrier(0);
-        load_half(bx1, bb1, cfirst, 1);
+        load_piece(bx1, xcol, a.ld_x, cfirst, 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();   // conv weights
         start_chunk(cfirst);
-        conv_store(bx0, cfirst, 0, true);
-        conv_store(bb0, cfirst, 0, false);
-        load_half(bx0, bb0, cfirst + 1, 0);
+        stage_x(bx0, cfirst, 0);
+        load_piece(bx0, xcol, a.ld_x, cfirst + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();   // unit (cfirst, 0) staged
         for (int c = cfirst; c < cend; ++c) {
-            conv_store(bx1, c, 1, true);
-            conv_store(bb1, c, 1, false);
-            load_half(bx1, bb1, c + 1, 1);
+            stage_x(bx1, c, 1);
+            load_piece(bx1, xcol, a.ld_x, c + 1, 1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();   // unit (c, 0) multiplied, (c, 1) staged
             if (c + 1 < cend) {
                 start_chunk(c + 1);
-                conv_store(bx0, c + 1, 0, true);
-                conv_store(bb0, c + 1, 0, false);
-                load_half(bx0, bb0, c + 2, 0);
+                stage_x(bx0, c + 1, 0);
+                load_piece(bx0, xcol, a.ld_x, c + 2, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();   // unit (c, 1) multiplied, (c + 1, 0) staged
         }
-        if (!(cend == nch && seg_k == 0) && seg_k > 0 && (wave & 1) == 0 && lane == 0)
-            a.lam[(cbase + cfirst) * a.nheads + head] = lrun;
+        if (seg_k > 0 && (wave & 1) == 0 && lane == 0) a.lam[(cbase + cfirst) * a.nheads + head] = lrun;
     } else {
         // ---------------------------------------------------------- consumers
         const int cw = wave - 4;   // n tile of both heads' states
+        const int bcg = (lane >> 3) + 8 * (cw >> 1);   // B channel group (of 16) of this thread's pieces
+        const uint16_t* bcol = static_cast<const uint16_t*>(a.B) + grp * a.gs_B + 8 * bcg;
+        const int bch = d_inner + grp * N + 8 * bcg, blw = IPW * P + 8 * bcg;
+        RawBuf bb0, bb1;
+        auto stage_b = [&](RawBuf& b, int c, int h) __attribute__((always_inline)) {
+            conv_store(b, c, h, bch, blw, nullptr, sBTh[h], sBTl[h], bcg);
+        };
         // acc[hh][pt]: head hh, p tile pt; lane l has p = 32 pt + l % 32 and, in
         // registers 4m .. 4m + 3, n = 32 cw + 8m + 4 (l / 32) + 0..3
         f32x16_t acc[IPW][2];
         auto soff = [&](int pt, int m) { return (32 * pt + l32) * N + 32 * cw + 8 * m + 4 * g32; };
         // entry states in accumulator order: float4 ((tile * 4 + m) * 64 + lane), tile = 2 cw + pt
         auto eoff = [&](int pt, int m) { return 4 * (((2 * cw + pt) * 4 + m) * 64 + lane); };
+        load_piece(bb0, bcol, a.ld_B, cfirst, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_piece(bb1, bcol, a.ld_B, cfirst, 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int hh = 0; hh < IPW; ++hh) {
             const float* st = a.ssm_state + ((int64_t)slot * a.nheads + head0 + hh) * (int64_t)(P * N);
@@ -2123,30 +2129,33 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
                     acc[hh][pt][4 * m + 2] = v.z; acc[hh][pt][4 * m + 3] = v.w;
                 }
         }
-        // h^T += B^T (w x) over the 16-row K blocks of a staged half
-        auto multiply = [&](int nkb, int h) __attribute__((always_inline)) {
+        // h^T += B^T (w x) over the 16-row K blocks of a staged half.  Rows past
+        // the sequence's end have weight 0 (their (w x) is 0) and finite B
+        // rows, so every block is multiplied: no branch splits the products
+        // from the conv beside them.
+        auto multiply = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
             for (int k = 0; k < QH / 16; ++k) {
-                if (k < nkb) {
-                    const int bo = (32 * cw + l32) * RH + 16 * k + 8 * g32;
-                    const bf16x8_t bh = as_bf16x8(lds128(sBTh[h] + bo));
-                    const bf16x8_t bl = as_bf16x8(lds128(sBTl[h] + bo));
+                const int bo = (32 * cw + l32) * RH + 16 * k + 8 * g32;
+                const bf16x8_t bh = as_bf16x8(lds128(sBTh[h] + bo));
+                const bf16x8_t bl = as_bf16x8(lds128(sBTl[h] + bo));
 #pragma unroll
-                    for (int hh = 0; hh < IPW; ++hh)
+                for (int hh = 0; hh < IPW; ++hh)
 #pragma unroll
-                        for (int pt = 0; pt < 2; ++pt) {
-                            const int xo = (32 * pt + l32) * RH + 16 * k + 8 * g32;
-                            const bf16x8_t xh = as_bf16x8(lds128(sXH[h][hh] + xo));
-                            const bf16x8_t xl = as_bf16x8(lds128(sXL[h][hh] + xo));
-                            mma32<true, true>(acc[hh][pt], bh, bl, xh, xl);
-                        }
-                }
+                    for (int pt = 0; pt < 2; ++pt) {
+                        const int xo = (32 * pt + l32) * RH + 16 * k + 8 * g32;
+                        const bf16x8_t xh = as_bf16x8(lds128(sXH[h][hh] + xo));
+                        const bf16x8_t xl = as_bf16x8(lds128(sXL[h][hh] + xo));
+                        mma32<true, true>(acc[hh][pt], bh, bl, xh, xl);
+                    }
             }
         };
         __syncthreads();   // conv weights
+        stage_b(bb0, cfirst, 0);
+        load_piece(bb0, bcol, a.ld_B, cfirst + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();   // unit (cfirst, 0) staged
         for (int c = cfirst; c < cend; ++c) {
-            const int S = (int)((L - (int64_t)c * Q) < Q ? (L - (int64_t)c * Q) : Q);
             // entry state of this chunk, then h <- e(gamma_S) h
             const bool store = seg_k == 0 || c > cfirst;
 #pragma unroll
@@ -2165,11 +2174,19 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
                     acc[hh][pt] *= decay;
                 }
             }
-            const int S0 = S < QH ? S : QH;
-            multiply((S0 + 15) >> 4, 0);
+            // unit (c, 0): its products beside the conv of (c, 1)'s B
+            multiply(0);
+            stage_b(bb1, c, 1);
+            load_piece(bb1, bcol, a.ld_B, c + 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
-            const int S1 = S - QH;
-            multiply(S1 > 0 ? (S1 + 15) >> 4 : 0, 1);
+            // unit (c, 1): its products beside the conv of (c + 1, 0)'s B
+            multiply(1);
+            if (c + 1 < cend) {
+                stage_b(bb0, c + 1, 0);
+                load_piece(bb0, bcol, a.ld_B, c + 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             __syncthreads();
         }
         // The end state: the sequence's final state when this is its only segment;
