@@ -324,6 +324,36 @@ __device__ __forceinline__ void conv_piece_start(const uint4 (&r)[RW], int k, co
     }
 }
 
+// conv + SiLU of a whole piece, all 8 channels x RR rows at once (the same
+// operations in the same order per output as conv_piece, laid out breadth
+// first so that a single wave has 32 independent chains to interleave):
+// u[k][t] = SiLU(b_k + w_k0 v[t] + w_k1 v[t+1] + w_k2 v[t+2] + w_k3 v[t+3]).
+__device__ __forceinline__ void conv_piece8(const uint4 (&r)[RW], bool start, const float (&hv)[3][8],
+                                            const float4 (&w)[8], const float (&b)[8], float (&u)[8][RR]) {
+    float acc[8][RR];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int t = 0; t < RR; ++t) acc[k][t] = b[k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int t = 0; t < RR; ++t) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float v = bf16_lane(r[t + j], k);
+                if (start && t + j < 3) v = hv[t + j][k];
+                const float wj = j == 0 ? w[k].x : j == 1 ? w[k].y : j == 2 ? w[k].z : w[k].w;
+                acc[k][t] = fmaf(wj, v, acc[k][t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int t = 0; t < RR; ++t) u[k][t] = silu(acc[k][t]);
+}
+
 // acc += a b over (hi, lo) operands: the lo x lo term (~2^-18 relative) is dropped,
 // and a lo part that is known to be zero (SA / SB false) is skipped.
 template <bool SA, bool SB>
@@ -2017,14 +2047,17 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
             wx[0] = w4.x; wx[1] = w4.y; wx[2] = w4.z; wx[3] = w4.w;
         }
         const ConvW cw = read_convw(sCW, sCB, lw);
+        float4 wv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) wv[k] = cw.w(k);
+        float u[8][RR];
+        conv_piece8(b.r, start, hv, wv, cw.b, u);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            float u[RR];
-            conv_piece(b.r, k, start, hv, cw.w(k), cw.b[k], u);
             uint32_t wh[RR / 2], wl[RR / 2];
 #pragma unroll
             for (int m = 0; m < RR / 2; ++m)
-                split2(u[2 * m] * wx[2 * m], u[2 * m + 1] * wx[2 * m + 1], wh[m], wl[m]);
+                split2(u[k][2 * m] * wx[2 * m], u[k][2 * m + 1] * wx[2 * m + 1], wh[m], wl[m]);
             store_tokens<RR>(dh + (8 * cg + k) * RH + 4 * rg, wh);
             store_tokens<RR>(dl + (8 * cg + k) * RH + 4 * rg, wl);
         }
