@@ -104,7 +104,7 @@ def cpu_baseline(inp, w, seqs=tuple(range(8)), tokens=1536):
 
 # ---------------------------------------------------------------- algorithmic work per kernel
 
-def kernel_bytes(w, T, nseq, raw=True):
+def kernel_bytes(w, T, nseq, raw=True, fused=False):
     """Method bytes of one launch of each prefill kernel: the layer's own inputs and
     outputs a kernel reads or writes, each counted once at its storage width (bf16
     x|B|C and z, fp32 dt, y and states), plus the stage boundaries the separate
@@ -120,6 +120,9 @@ def kernel_bytes(w, T, nseq, raw=True):
       scan_pass    read raw x, B and dt; read the initial, write the final SSM state
       scan_out     read raw x, B, C and dt; write y_pre
       norm         read y_pre and z, write y
+    raw + fused (each chunk-output workgroup holds whole norm groups: it applies
+    the norm itself and the norm kernel does not run)
+      scan_out     read raw x, B, C, dt and z; write y
     chain (M2SSD_PREFILL_CHAIN=1, fp32 inputs)
       conv         read x|B|C, write the post-conv activations (fp32; fp64 for fp32 inputs)
       scan_pass    read post-conv x, B and dt; states as above (fp32 inputs: the
@@ -136,6 +139,10 @@ def kernel_bytes(w, T, nseq, raw=True):
     if w.act != "bf16":
         return {"conv": T * (cd * 4 + cd * 8), "conv_state": conv_state,
                 "scan_pass": T * (cd * 8 + H * 4 + di * 4) + states, "scan_out": 0, "norm": norm}
+    if raw and fused:
+        return {"conv": 0, "conv_state": conv_state,
+                "scan_pass": T * ((di + gn) * act + H * 4) + states,
+                "scan_out": T * (cd * act + H * 4 + di * act + di * 4), "norm": 0}
     if raw:
         return {"conv": 0, "conv_state": conv_state,
                 "scan_pass": T * ((di + gn) * act + H * 4) + states,
@@ -158,7 +165,7 @@ def design_extra_bytes(w, T, nseq):
 
 # The device sources each measured kernel set is built from: a traffic record holds
 # their sha1 and counts only while the sources are unchanged.
-CHAIN_SOURCES = ("conv_rows.hip", "ssd_chunked.hip", "ssd_scan.hip", "gated_norm.hip",
+CHAIN_SOURCES = ("conv_rows.hip", "ssd_chunked.hip", "ssd_scan.hip", "gated_norm.hip", "norm_row.h",
                  "device_common.h")
 DECODE_SOURCES = ("decode_step.hip", "step_size.h", "device_common.h")
 
@@ -357,8 +364,10 @@ def main():
         log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
         del src, dst
 
-    raw = m2.get_counters()["conv_launches"] == 0   # the scan kernels convolved the raw rows
-    kb = kernel_bytes(w, T, nseq, raw)
+    cnt = m2.get_counters()
+    raw = cnt["conv_launches"] == 0      # the scan kernels convolved the raw rows
+    fused = cnt["norm_launches"] == 0    # the chunk output applied the norm
+    kb = kernel_bytes(w, T, nseq, raw, fused)
     extra = design_extra_bytes(w, T, nseq)
     dom = max(kms, key=kms.get)
     step_b = fused_bytes(w, T, nseq)
@@ -376,7 +385,9 @@ def main():
                 "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP64_PEAK_TFLOPS, 4),
                 "traffic": None}
         dom = "scan_pass"
-    roof.update({"kernel": dom, "path": "raw rows convolved in the scan" if raw else "four-kernel chain",
+    path = ("four-kernel chain" if not raw else
+            "raw rows convolved in the scan, norm in the chunk output" if fused else "raw rows convolved in the scan")
+    roof.update({"kernel": dom, "path": path,
             "kernel_ms": round(kms[dom], 4), "kernel_bytes": kb[dom],
             "step_bytes": step_b,
             "scan_tflops_alg": round(scan_flops(w, T) / ((kms["scan_pass"] + kms["scan_out"]) * 1e-3) / 1e12, 2),
@@ -556,7 +567,8 @@ def run_other_mode(args):
         kms = {k: kt[k + "_ms"] / max(1, kt["calls"]) for k in stages}
         from workloads import Workload
         wl = Workload("x", s, tuple(lens[nd:]), "bf16", "pool")
-        kb = kernel_bytes(wl, T - nd, nseq - nd, raw=m2.get_counters()["conv_launches"] == 0)
+        cnt = m2.get_counters()
+        kb = kernel_bytes(wl, T - nd, nseq - nd, raw=cnt["conv_launches"] == 0, fused=cnt["norm_launches"] == 0)
         if mode == "mixed":
             # the decode rows run on a second stream beside the prefill chain, so
             # the chain's kernel times overlap them: the whole step is the unit
