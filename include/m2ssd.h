@@ -238,10 +238,16 @@ int gated_rmsnorm_group(const float* y, int64_t ld_y, const void* z, int64_t ld_
 
 /*
  * Bytes of device workspace mamba2_prefill needs for these sizes and this
- * activation dtype (0 on bad arguments).  The workspace holds the post-conv
- * activations of the batch (fp32 for bf16 inputs, fp64 for fp32 inputs; on the
- * chunk-parallel scan path blocked per head and per group), the fp32 pre-norm
- * output and the scan's own workspace (ssd_chunk_scan_workspace_size()).
+ * activation dtype (0 on bad arguments).  The workspace holds the fp32
+ * pre-norm output (used when y is not fp32) and the scan's own workspace
+ * (ssd_chunk_scan_workspace_size()), and, when the prefill runs as the
+ * four-kernel chain, the post-conv activations of the batch before them (fp32
+ * for bf16 inputs, fp64 for fp32 inputs; on the chunk-parallel scan path
+ * blocked per head and per group).  bf16 inputs at headdim 64, dstate 64 or
+ * 128 (an even number of heads per group at 128) and chunk 128 have the scan
+ * kernels convolve the raw rows themselves, so no post-conv activations are
+ * stored; M2SSD_PREFILL_CHAIN=1 in the environment (read at every call, here
+ * and in mamba2_prefill alike) selects the chain instead.
  */
 size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_seqlen,
                                      int nheads, int headdim, int dstate, int ngroups,
@@ -263,7 +269,11 @@ size_t mamba2_prefill_workspace_size(int64_t total_tokens, int batch, int max_se
  *     a bf16 output alone carries a relative rounding of 2^-9);
  *   workspace: device memory of at least mamba2_prefill_workspace_size() bytes,
  *     16-byte aligned (NULL allowed when that size is 0).
- * Both states are advanced in place.
+ * Both states are advanced in place.  The kernels that run depend on the
+ * shape (the counters tell): on the raw-row path the chunk output applies the
+ * norm itself when each of its workgroups holds whole norm groups and every
+ * row is 16-byte aligned, and the norm kernel runs otherwise; the results do
+ * not depend on which ran.
  */
 int mamba2_prefill(const void* x, int64_t ld_x, const void* B, int64_t ld_B,
                    const void* C, int64_t ld_C, const void* z, int64_t ld_z, int act_dtype,
