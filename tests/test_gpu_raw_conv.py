@@ -26,7 +26,7 @@ import torch
 import mamba_ssd_selective_amd as m2
 from oracle import recurrence as R
 from workloads import LayerShape, small_shape_inputs
-from parity_util import TOL, rel_err
+from parity_util import TOL, rel_err, split_views, to_device
 from test_gpu_parity import gpu_prefill
 
 pytestmark = pytest.mark.gpu
@@ -90,3 +90,30 @@ def test_raw_conv_scan_equals_chain_and_oracle(case, monkeypatch):
         assert worst <= 0.0
     assert rel_err(cs, ref["conv_state"], "conv_state") == 0.0
     assert rel_err(ss, ref["ssm_state"], "ssm_state") <= tol
+
+
+@pytest.mark.parametrize("chain", [False, True])
+def test_sequence_longer_than_planned_levels(chain, monkeypatch):
+    """max_seqlen is an upper bound the caller states; the segment plan is made
+    from it.  A sequence longer than that bound (2000 tokens against 1024 here,
+    still within batch * max_seqlen) has more chunks than the planned segment
+    levels: the state pass's last level runs to the sequence's end and the
+    carry and chunk-output kernels cap the segment index, so every chunk is
+    still computed and the results match the oracle."""
+    m2.load()
+    shape = LayerShape(16, 64, 128, 2)
+    lens = [2000, 100, 100, 100]
+    inp = small_shape_inputs(shape, lens, seed=301, act="bf16", init="random", n_slots=6)
+    if chain:
+        monkeypatch.setenv("M2SSD_PREFILL_CHAIN", "1")
+    d = to_device(inp, "bf16")
+    x, B, C = split_views(d["xbc"], shape)
+    y = m2.mamba2_prefill(x, B, C, d["z"], d["dt"], d["A"], d["D"], d["conv_w"], d["conv_b"], d["norm_w"],
+                          d["conv_state"], d["ssm_state"], d["cu_seqlens"], 1024, shape.nheads, shape.headdim,
+                          shape.dstate, shape.ngroups, 128, d["state_idx"], d["has_init"], 1e-5, True)
+    torch.cuda.synchronize()
+    ref = R.prefill(inp, shape.nheads, shape.headdim, shape.dstate, shape.ngroups)
+    tol = TOL["bf16"]
+    assert rel_err(y, ref["y"], "y", sum(lens) * shape.d_inner) <= tol
+    assert rel_err(d["conv_state"], ref["conv_state"], "conv_state") == 0.0
+    assert rel_err(d["ssm_state"], ref["ssm_state"], "ssm_state") <= tol
