@@ -31,6 +31,8 @@ from test_gpu_parity import gpu_prefill
 
 pytestmark = pytest.mark.gpu
 
+SHORT_LENS = [1 + (7 * b) % 24 for b in range(130)]
+
 CASES = [
     # (shape, lengths, init, norm_before_gate, output dtype, norm fused into the chunk output)
     (LayerShape(16, 64, 128, 2), [300, 1, 2, 3, 129, 0, 257], "random", True, torch.float32, False),
@@ -42,6 +44,11 @@ CASES = [
     (LayerShape(64, 64, 128, 8), [1500, 700, 3, 0, 129], "pool", True, torch.bfloat16, True),
     (LayerShape(64, 64, 128, 8), [1500, 700, 3, 0, 129], "random", False, torch.float32, True),
     (LayerShape(8, 64, 64, 4), [4200, 100], "random", True, torch.float32, True),
+    # norm groups of 2048 and 1024 channels (4 and 2 eight-channel blocks per
+    # lane in the fused norm), over 130 short sequences so that the chunk
+    # output has enough (chunk, group) items to keep whole groups per workgroup
+    (LayerShape(32, 64, 64, 1), SHORT_LENS, "pool", False, torch.float32, True),
+    (LayerShape(16, 64, 128, 1), SHORT_LENS, "random", True, torch.bfloat16, True),
 ]
 
 
