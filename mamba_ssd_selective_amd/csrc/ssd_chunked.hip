@@ -1942,12 +1942,16 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
         // still in cache.  (The norm's barrier sits inside chunk_norm_rows.)
         const int gs = hpg * P;
         const int nbl = (gs / 8 + 63) / 64;
+        // (one block per lane: 16 rows per wave in flight, a chunk's 128 rows in
+        // one batch, as the norm is bound by the rows it has in flight; wider
+        // groups keep fewer rows for their registers: 6 rows at two blocks ran
+        // slower than 4)
         if (a.out_dtype == kBF16) {
-            if (nbl == 1) chunk_norm_rows<uint16_t, 1, 8>(a, r0, S, grp * gs, gs, wave, lane);
+            if (nbl == 1) chunk_norm_rows<uint16_t, 1, 16>(a, r0, S, grp * gs, gs, wave, lane);
             else if (nbl == 2) chunk_norm_rows<uint16_t, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
             else chunk_norm_rows<uint16_t, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
         } else {
-            if (nbl == 1) chunk_norm_rows<float, 1, 8>(a, r0, S, grp * gs, gs, wave, lane);
+            if (nbl == 1) chunk_norm_rows<float, 1, 16>(a, r0, S, grp * gs, gs, wave, lane);
             else if (nbl == 2) chunk_norm_rows<float, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
             else chunk_norm_rows<float, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
         }
