@@ -32,6 +32,7 @@ from test_gpu_parity import gpu_prefill
 pytestmark = pytest.mark.gpu
 
 SHORT_LENS = [1 + (7 * b) % 24 for b in range(130)]
+MANY_LENS = [1 + (5 * b) % 9 for b in range(1500)]
 
 CASES = [
     # (shape, lengths, init, norm_before_gate, output dtype, norm fused into the chunk output)
@@ -49,6 +50,9 @@ CASES = [
     # output has enough (chunk, group) items to keep whole groups per workgroup
     (LayerShape(32, 64, 64, 1), SHORT_LENS, "pool", False, torch.float32, True),
     (LayerShape(16, 64, 128, 1), SHORT_LENS, "random", True, torch.bfloat16, True),
+    # more sequences than the length ranking stages at once (1024), each a
+    # few tokens, every one from its own slot of the pool
+    (LayerShape(8, 64, 64, 2), MANY_LENS, "pool", True, torch.float32, True),
 ]
 
 
@@ -60,7 +64,8 @@ def test_raw_conv_scan_equals_chain_and_oracle(case, monkeypatch):
                              n_slots=len(lens) + 2)
     if init == "pool":
         inp["has_init"] = np.array([(b + 1) % 3 != 0 for b in range(len(lens))], dtype=np.uint8)
-    print(f" shape={shape} lens={lens} init={init} nbg={nbg} y={ydt} fused norm={fused}", flush=True)
+    shown = lens if len(lens) <= 16 else f"{len(lens)} sequences, {sum(lens)} tokens"
+    print(f" shape={shape} lens={shown} init={init} nbg={nbg} y={ydt} fused norm={fused}", flush=True)
     m2.reset_counters()
     y, cs, ss = gpu_prefill(inp, shape, "bf16", nbg=nbg, y_dtype=ydt)
     c = m2.get_counters()
