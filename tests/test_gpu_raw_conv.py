@@ -53,6 +53,9 @@ CASES = [
     # more sequences than the length ranking stages at once (1024), each a
     # few tokens, every one from its own slot of the pool
     (LayerShape(8, 64, 64, 2), MANY_LENS, "pool", True, torch.float32, True),
+    # odd heads per group (3) and one head per group, at dstate 64
+    (LayerShape(12, 64, 64, 4), [300, 130, 5], "random", True, torch.float32, True),
+    (LayerShape(4, 64, 64, 4), [257, 1, 64], "random", False, torch.float32, True),
 ]
 
 
