@@ -393,7 +393,10 @@ int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, con
     a.order = a.states ? m2::chunked_scan_order(a.states, total_tokens, batch, nheads, headdim, dstate) : nullptr;
     if (a.states) m2::chunked_scan_plan(a, total_tokens, max_seqlen);
     else m2::one_pass_plan(a, max_seqlen, need > 0 ? workspace : nullptr);
-    if (batch == 1) a.order = nullptr;  // one sequence: no order to compute
+    // one sequence, or all of one length (batch * max_seqlen tokens): the
+    // identity order is already longest first (the order only sets the state
+    // pass's dispatch; a sequence past max_seqlen would only be dealt later)
+    if (batch == 1 || total_tokens == (int64_t)batch * max_seqlen) a.order = nullptr;
     if ((st = launch_scan(a, total_tokens, static_cast<hipStream_t>(stream), nullptr))) return st;
     return ok();
 }
@@ -566,7 +569,8 @@ int prefill_run(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const 
     sa.order = states_ws ? m2::chunked_scan_order(states_ws, total_tokens, batch, nheads, headdim, dstate) : nullptr;
     if (states_ws) m2::chunked_scan_plan(sa, total_tokens, max_seqlen);
     else m2::one_pass_plan(sa, max_seqlen, seg_ws);
-    if (batch == 1) sa.order = nullptr;  // one sequence: no order to compute
+    // one sequence, or all of one length: no order to compute (see ssd_chunk_scan)
+    if (batch == 1 || total_tokens == (int64_t)batch * max_seqlen) sa.order = nullptr;
     // The raw chunk output applies the norm itself when each of its workgroups
     // holds a whole norm group (out_split 1) and every row is 16-byte aligned.
     {
