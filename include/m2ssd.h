@@ -217,6 +217,24 @@ size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads
                                      int dstate, int ngroups, int chunk_size, int act_dtype);
 
 /*
+ * ssd_chunk_scan_plan -- how ssd_chunk_scan and mamba2_prefill split the
+ * chunk-parallel scan (of page "perf(nemotron_h): prefill single-GPU prompts
+ * in multi-token chunks", section Implementation) for these sizes; host only,
+ * no device work.  *out_split: chunk-output workgroups per (chunk, group) (a
+ * small grid splits a group's heads over several; the norm then runs as its
+ * own kernel).  *seg: chunks per segment when long sequences are split so
+ * that their state walks fill the CUs (0 = not split); *seg_levels: segments
+ * of a max_seqlen-long sequence, the last of which takes every chunk from its
+ * start to the sequence's end (a sequence longer than max_seqlen is still
+ * covered).  Returns M2_OK, or an error (M2_ERR_SHAPE for sizes that take the
+ * one-pass scan, which has no chunk plan); the outputs are written on M2_OK
+ * only.
+ */
+int ssd_chunk_scan_plan(int64_t total_tokens, int batch, int max_seqlen, int nheads, int headdim,
+                        int dstate, int ngroups, int chunk_size, int act_dtype, int* out_split,
+                        int* seg, int* seg_levels);
+
+/*
  * gated_rmsnorm_group -- grouped RMSNorm with the SiLU(z) gate.  (Page
  * "Nemotron-H", section 4.1: the scan output is normalised per group with the
  * ssm_norm weight and multiplied by the SiLU(z) gate; page "NemotronH decodes

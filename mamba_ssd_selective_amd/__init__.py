@@ -9,7 +9,8 @@ from ._lib import (M2_BF16, M2_F32, M2Error, cu_seqlens_of, gated_rmsnorm_group,
                    mamba2_prefill_noalloc, mamba2_prefill_noalloc_scratch_bytes,
                    mamba2_prefill_inproj, mamba2_prefill_inproj_workspace_size,
                    mamba2_decode_inproj, mamba2_mixed_inproj, mamba2_mixed_inproj_workspace_size,
-                   reset_counters, ssd_chunk_scan, ssd_chunk_scan_workspace_size, timing_enable,
+                   reset_counters, ssd_chunk_scan, ssd_chunk_scan_plan, ssd_chunk_scan_workspace_size,
+                   timing_enable,
                    timing_read, version, LIB_PATH)
 
 __all__ = ["M2_BF16", "M2_F32", "M2Error", "cu_seqlens_of", "gated_rmsnorm_group",
@@ -18,6 +19,6 @@ __all__ = ["M2_BF16", "M2_F32", "M2Error", "cu_seqlens_of", "gated_rmsnorm_group
            "mamba2_prefill_noalloc_scratch_bytes", "mamba2_prefill_inproj",
            "mamba2_prefill_inproj_workspace_size", "mamba2_decode_inproj", "mamba2_mixed_inproj",
            "mamba2_mixed_inproj_workspace_size", "reset_counters", "ssd_chunk_scan",
-           "ssd_chunk_scan_workspace_size", "timing_enable",
+           "ssd_chunk_scan_plan", "ssd_chunk_scan_workspace_size", "timing_enable",
            "timing_read", "version",
            "LIB_PATH"]

@@ -63,6 +63,8 @@ _SIGS = {
                             _P, _I, _L, _I, _P, _P, _I, _I, _I, _I, _I, _P, _L, _P,
                             ctypes.c_size_t, _P]),
     "ssd_chunk_scan_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I]),
+    "ssd_chunk_scan_plan": (_I, [_L, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
+                                 ctypes.POINTER(_I)]),
     "gated_rmsnorm_group": (_I, [_P, _L, _P, _L, _I, _P, _F, _I, _I, _L, _I, _P, _L, _I, _P]),
     "mamba2_prefill_workspace_size": (ctypes.c_size_t, [_L, _I, _I, _I, _I, _I, _I, _I, _I]),
     "mamba2_prefill": (_I, [_P, _L, _P, _L, _P, _L, _P, _L, _I, _P, _L, _P, _P, _P, _P, _P,
@@ -216,6 +218,16 @@ def ssd_chunk_scan_workspace_size(total_tokens, batch, nheads, headdim, dstate, 
     code = M2_BF16 if act_dtype == torch.bfloat16 else M2_F32
     return int(load().ssd_chunk_scan_workspace_size(total_tokens, batch, nheads, headdim, dstate,
                                                     ngroups, chunk_size, code))
+
+
+def ssd_chunk_scan_plan(total_tokens, batch, max_seqlen, nheads, headdim, dstate, ngroups,
+                        chunk_size=128, act_dtype=torch.bfloat16):
+    """The chunk-parallel scan's work split for these sizes: (out_split, seg, seg_levels)."""
+    code = M2_BF16 if act_dtype == torch.bfloat16 else M2_F32
+    o, sg, lv = _I(0), _I(0), _I(0)
+    _check(load().ssd_chunk_scan_plan(total_tokens, batch, max_seqlen, nheads, headdim, dstate, ngroups,
+                                      chunk_size, code, ctypes.byref(o), ctypes.byref(sg), ctypes.byref(lv)))
+    return o.value, sg.value, lv.value
 
 
 def ssd_chunk_scan(x, B, C, dt, A, D, ssm_state, cu_seqlens, max_seqlen, nheads, headdim,

@@ -188,8 +188,16 @@ bool chunked_raw_supported(int nheads, int ngroups, int headdim, int dstate, int
 size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, int headdim, int dstate);
 int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
                             int dstate);
-// Sets a.seg (and the buffers behind it) from the longest sequence: long
-// sequences are split when the (sequence, head) walks alone would leave CUs idle.
+// The chunk-parallel scan's split of the work (host only): chunk-output
+// workgroups per (chunk, group), and the segments long sequences are split
+// into when the (sequence, head) walks alone would leave CUs idle (seg chunks
+// each, 0 = not split; seg_levels segments cover max_seqlen, the last level
+// runs to a sequence's end).
+struct ScanSplit {
+    int out_split, seg, seg_levels;
+};
+ScanSplit chunked_scan_split(int64_t total_tokens, int batch, int nheads, int ngroups, int dstate, int max_seqlen);
+// Sets out_split, seg, seg_levels (chunked_scan_split) and the buffers behind them.
 void chunked_scan_plan(ScanArgs& a, int64_t total_tokens, int max_seqlen);
 hipError_t launch_ssd_state_pass(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_ssd_chunk_out(const ScanArgs& a, int64_t total_tokens, hipStream_t stream);

@@ -363,6 +363,25 @@ size_t ssd_chunk_scan_workspace_size(int64_t total_tokens, int batch, int nheads
     return scan_ws_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype);
 }
 
+int ssd_chunk_scan_plan(int64_t total_tokens, int batch, int max_seqlen, int nheads, int headdim, int dstate,
+                        int ngroups, int chunk_size, int act_dtype, int* out_split, int* seg, int* seg_levels) {
+    if (!out_split || !seg || !seg_levels) return fail(M2_ERR_NULL, "scan plan: out_split, seg and seg_levels are required");
+    int st = validate_scan_dims(nheads, headdim, dstate, ngroups, chunk_size);
+    if (st) return st;
+    if (!valid_dtype(act_dtype)) return fail(M2_ERR_DTYPE, "scan plan: act_dtype must be M2_F32 or M2_BF16");
+    if (total_tokens < 0 || batch <= 0 || max_seqlen < 0)
+        return fail(M2_ERR_SHAPE, "scan plan: batch must be > 0, total_tokens and max_seqlen >= 0");
+    if ((int64_t)max_seqlen * batch < total_tokens)
+        return fail(M2_ERR_SHAPE, "scan plan: total_tokens %lld exceeds batch * max_seqlen", (long long)total_tokens);
+    if (scan_states_bytes(total_tokens, batch, nheads, headdim, dstate, ngroups, chunk_size, act_dtype) == 0)
+        return fail(M2_ERR_SHAPE, "scan plan: these sizes take the one-pass scan, which has no chunk plan");
+    const m2::ScanSplit sp = m2::chunked_scan_split(total_tokens, batch, nheads, ngroups, dstate, max_seqlen);
+    *out_split = sp.out_split;
+    *seg = sp.seg;
+    *seg_levels = sp.seg_levels;
+    return ok();
+}
+
 int ssd_chunk_scan(const void* x, int64_t ld_x, const void* B, int64_t ld_B, const void* C,
                    int64_t ld_C, int act_dtype, const float* dt, int64_t ld_dt, const float* A,
                    const float* D, float* ssm_state, int n_slots, const int32_t* cu_seqlens,

@@ -2339,34 +2339,40 @@ size_t chunked_scan_states_bytes(int64_t total_tokens, int batch, int nheads, in
            2 * r256(slots * sizeof(double));
 }
 
-void chunked_scan_plan(ScanArgs& a, int64_t total_tokens, int max_seqlen) {
+ScanSplit chunked_scan_split(int64_t total_tokens, int batch, int nheads, int ngroups, int dstate, int max_seqlen) {
+    ScanSplit sp{1, 0, 1};
+    const int hpg = nheads / ngroups;
     // chunk output: fewer (chunk, group) workgroups than CUs split the group's
     // heads over up to hpg workgroups (a 137-token prompt has 16 such pairs)
     {
-        const int hpg = a.nheads / a.ngroups;
-        const int64_t wgs = (total_tokens / Q + a.batch) * (int64_t)a.ngroups;
+        const int64_t wgs = (total_tokens / Q + batch) * (int64_t)ngroups;
         int split = 1;
         while (hpg % (2 * split) == 0 && wgs * 2 * split <= 256) split *= 2;
-        a.out_split = split;
+        sp.out_split = split;
     }
-    a.seg = 0;
-    a.seg_levels = 1;
+    const int ipw = (dstate == 128 && hpg % 2 == 0) ? 2 : 1;
+    const int64_t level = (int64_t)nheads * batch / ipw;
+    const int nch = (int)(((int64_t)max_seqlen + Q - 1) / Q);
+    if (level >= SEG_TARGET || (int64_t)batch * nheads > SEG_END_MAX) return sp;
+    int nseg = (int)((SEG_TARGET + level - 1) / level);
+    if (nseg > nch / SEG_MIN) nseg = nch / SEG_MIN;
+    if (nseg < 2) return sp;
+    sp.seg = (nch + nseg - 1) / nseg;
+    sp.seg_levels = (nch + sp.seg - 1) / sp.seg;
+    return sp;
+}
+
+void chunked_scan_plan(ScanArgs& a, int64_t total_tokens, int max_seqlen) {
+    const ScanSplit sp = chunked_scan_split(total_tokens, a.batch, a.nheads, a.ngroups, a.dstate, max_seqlen);
+    a.out_split = sp.out_split;
+    a.seg = sp.seg;
+    a.seg_levels = sp.seg_levels;
     char* p = reinterpret_cast<char*>(a.order) + r256((size_t)a.batch * sizeof(int32_t));
     a.seg_end = reinterpret_cast<float*>(p);
     p += seg_end_bytes(a.batch, a.nheads, a.headdim, a.dstate);
     const size_t slots = (size_t)(total_tokens / Q + a.batch) * (size_t)a.nheads;
     a.lam = reinterpret_cast<double*>(p);
     a.cum = reinterpret_cast<double*>(p + r256(slots * sizeof(double)));
-    const int hpg = a.nheads / a.ngroups;
-    const int ipw = (a.dstate == 128 && hpg % 2 == 0) ? 2 : 1;
-    const int64_t level = (int64_t)a.nheads * a.batch / ipw;
-    const int nch = (int)(((int64_t)max_seqlen + Q - 1) / Q);
-    if (level >= SEG_TARGET || (int64_t)a.batch * a.nheads > SEG_END_MAX) return;
-    int nseg = (int)((SEG_TARGET + level - 1) / level);
-    if (nseg > nch / SEG_MIN) nseg = nch / SEG_MIN;
-    if (nseg < 2) return;
-    a.seg = (nch + nseg - 1) / nseg;
-    a.seg_levels = (nch + a.seg - 1) / a.seg;
 }
 
 int32_t* chunked_scan_order(float* states, int64_t total_tokens, int batch, int nheads, int headdim,
