@@ -53,9 +53,22 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def round_fp16_block(v: np.ndarray) -> np.ndarray:
+    """fp16 of the whole block v scaled by one power of two 2^k, chosen so the
+    block's largest magnitude lands in [2^14, 2^15): the scaling is exact, so
+    only fp16's rounding (11 significant bits) and its subnormal floor remain,
+    with the range set by the block instead of by fp16's 65504."""
+    v = np.asarray(v, dtype=np.float64)
+    m = float(np.max(np.abs(v))) if v.size else 0.0
+    if m == 0.0 or not np.isfinite(m):
+        return round_fp16(v)
+    k = 14 - int(np.floor(np.log2(m)))
+    return np.ldexp(round_fp16(np.ldexp(v, k)), -k)
+
+
 FORMATS: Dict[str, Callable[[np.ndarray], np.ndarray]] = {
     "fp64": lambda v: np.asarray(v, dtype=np.float64), "fp32": round_fp32,
-    "fp16": round_fp16, "bf16": round_bf16}
+    "fp16": round_fp16, "bf16": round_bf16, "fp16_block": round_fp16_block}
 
 
 def rel_max(got: np.ndarray, ref: np.ndarray) -> float:
