@@ -152,14 +152,17 @@ def kernel_bytes(w, T, nseq, raw=True, fused=False):
             "scan_out": T * (cd * 4 + H * 4 + di * 4), "norm": norm}
 
 
-def design_extra_bytes(w, T, nseq):
+def design_extra_bytes(w, T, nseq, q16=False):
     """Bytes a kernel moves beyond its method bytes because of this design's
-    decomposition: the fp32 state entering every chunk slot, written by the state
-    pass and read by the chunk output (the staged carry)."""
+    decomposition: the state entering every chunk slot, written by the state
+    pass and read by the chunk output (the staged carry).  fp32, or with q16
+    (the raw-row kernels at dstate 128 when no sequence is split) 16-bit
+    values plus one fp32 scale per row of 32 values."""
     s = w.shape
     if w.act != "bf16":
         return {}
-    entry = (T // w.chunk_size + nseq) * s.nheads * s.headdim * s.dstate * 4
+    per_state = s.headdim * s.dstate * (2 + 4 / 32) if q16 else s.headdim * s.dstate * 4
+    entry = int((T // w.chunk_size + nseq) * s.nheads * per_state)
     return {"scan_pass": entry, "scan_out": entry}
 
 
@@ -368,7 +371,13 @@ def main():
     raw = cnt["conv_launches"] == 0      # the scan kernels convolved the raw rows
     fused = cnt["norm_launches"] == 0    # the chunk output applied the norm
     kb = kernel_bytes(w, T, nseq, raw, fused)
-    extra = design_extra_bytes(w, T, nseq)
+    q16 = False
+    if raw and w.act == "bf16" and w.shape.dstate == 128:
+        # 16-bit entry states unless the plan splits sequences into segments
+        _, seg, _ = m2.ssd_chunk_scan_plan(T, nseq, maxlen, w.shape.nheads, w.shape.headdim,
+                                           w.shape.dstate, w.shape.ngroups, w.chunk_size)
+        q16 = seg == 0
+    extra = design_extra_bytes(w, T, nseq, q16)
     dom = max(kms, key=kms.get)
     step_b = fused_bytes(w, T, nseq)
     step_frac = round(step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)

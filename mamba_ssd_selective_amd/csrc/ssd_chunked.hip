@@ -13,7 +13,9 @@
 //  state pass  walks the chunks of a (sequence, head) in order and keeps h^T
 //              [N x P] in matrix-core accumulators (two heads of one group per
 //              workgroup when they can share the staged B tile).  Per chunk it
-//              writes h_in to the entry-state buffer, scales the accumulators by
+//              writes h_in to the entry-state buffer (fp32; 16-bit rows with a
+//              scale each for the raw-row kernels at dstate 128 when no sequence
+//              is split, see store_entry_q16), scales the accumulators by
 //              e(gamma_S) and adds B^T (dt e(gamma_S - gamma_i) x) with the
 //              accumulators as the running sum.  Only B, x and dt are read.
 //  chunk out   one workgroup per (chunk, group), all chunks at once.  It forms
@@ -403,6 +405,60 @@ __device__ __forceinline__ void state_pn(int f, int& p, int& n) {
     const int lane = f & 63, m = (f >> 6) & 3, tile = f >> 8;
     p = 32 * (tile & 1) + (lane & 31);
     n = 32 * (tile >> 1) + 8 * m + 4 * (lane >> 5);
+}
+
+// 16-bit entry states (the raw-row kernels at dstate 128 when no sequence is
+// split): the state's values enter the chunk output only through its read-out
+// C h_in, so each row of 32 values (one p, one n tile) is stored as 16-bit
+// fixed point on its own scale s = max |v| of the row: q = round-half-even(v /
+// s * 32767) (the hardware's pack to signed normalized 16-bit), read back as q
+// * s / 32767.  The absolute error is at most s / 65534 per value.  A block
+// then moves 17 KB instead of 32 KB, in 5 store instructions per consumer lane
+// and head instead of 8.  Within a (chunk slot, head) block (the fp32 block's
+// place, P * N floats):
+//   uint4 u = ((tile * 2 + m2) * 64 + lane) holds the 16-bit values of float4s
+//     f = (tile * 4 + 2 m2) * 64 + lane and f + 64 (in the fp32 order above),
+//     four each;
+//   float P * N / 2 + r * NTQ + tile, r = p % 32, holds s / 32767 of row
+//     (p = 32 (tile & 1) + r, n tile tile >> 1).
+constexpr int NTQ = (P / 32) * (128 / 32);   // 32 x 32 tiles of a dstate-128 state
+
+// Store one head's entry state, held by a consumer of the raw state pass as the
+// two 32 x 32 accumulator tiles 2 cw and 2 cw + 1 (lane l: p = 32 pt + l % 32,
+// n = 32 cw + 8 m + 4 (l / 32) + e in register 4 m + e).
+__device__ __forceinline__ void store_entry_q16(float* he, const f32x16_t (&h)[2], int cw, int lane) {
+    uint4* dq = reinterpret_cast<uint4*>(he);
+    float dec[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(h[pt][e]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));   // lanes l and l ^ 32 share the row
+        const float enc = mx > 0.f ? __builtin_amdgcn_rcpf(mx) : 0.f;
+        dec[pt] = mx * (1.f / 32767.f);
+        const int tile = 2 * cw + pt;
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(h[pt][8 * m2 + 2 * j] * enc,
+                                                                                   h[pt][8 * m2 + 2 * j + 1] * enc));
+            dq[(tile * 2 + m2) * 64 + lane] = uint4{w[0], w[1], w[2], w[3]};
+        }
+    }
+    if (lane < 32)
+        *reinterpret_cast<float2*>(he + P * 128 / 2 + lane * NTQ + 2 * cw) = float2{dec[0], dec[1]};
+}
+
+// The two float4s of a 16-bit uint4, scaled: lo = values of float4 f, hi of f + 64.
+__device__ __forceinline__ void q16_values(uint4 u, float d, float4& lo, float4& hi) {
+    auto v = [&](uint32_t w, int half) {
+        return (float)(int16_t)(uint16_t)(half ? (w >> 16) : (w & 0xffffu)) * d;
+    };
+    lo = float4{v(u.x, 0), v(u.x, 1), v(u.y, 0), v(u.y, 1)};
+    hi = float4{v(u.z, 0), v(u.z, 1), v(u.w, 0), v(u.w, 1)};
 }
 
 // ------------------------------------------------------------------ state pass
@@ -1450,7 +1506,8 @@ __device__ __forceinline__ void chunk_norm_rows(const ScanArgs& a, int64_t r0, i
 // The chunk output for raw bf16 rows, with the waves split by role.  Waves 0-3
 // (producers) convolve and stage the next head into one head buffer: its x
 // rows (conv + SiLU of the raw rows, as hi / lo planes), its entry state h_in
-// (hi / lo planes) and its decay factors.  Waves 4-7 (consumers) multiply the
+// (hi / lo planes; Q16: read as 16-bit rows and their scales, the format
+// store_entry_q16 writes) and its decay factors.  Waves 4-7 (consumers) multiply the
 // current head out of the other buffer.  A producer and a consumer share each
 // SIMD, so the conv's vector work runs beside the matrix products instead of
 // before them, and each role keeps only its own registers (the two roles run
@@ -1458,8 +1515,9 @@ __device__ __forceinline__ void chunk_norm_rows(const ScanArgs& a, int64_t r0, i
 // T = w and 7 - w of the chunk: every consumer then issues the same number of
 // causal products, and each h_in or x operand read from LDS serves both tiles.
 // All 8 waves convolve the group's B and C for G^T at the start.
-template <int N>
+template <int N, bool Q16>
 __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
+    static_assert(!Q16 || N == 128, "16-bit entry states at dstate 128");
     constexpr int NT = 512;
     constexpr int NKB = N / 32;        // K blocks over n
     constexpr int NPASS = N / 64;      // B, C staged 64 n at a time
@@ -1599,7 +1657,9 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
         // ---------------------------------------------------------- producers
         const int x_cg = lane >> 3, x_rg = (lane & 7) + 8 * wave;
         uint4 xraw[RW];           // the x piece of the head being prefetched: 8 channels x RR rows
-        float4 hr[NHP];           // its h_in
+        float4 hr[Q16 ? 1 : NHP]; // its h_in (fp32 entry states)
+        uint4 hq[Q16 ? NHP / 2 : 1];   // or its 16-bit values
+        float4 hd0, hd1;               // and their row scales (tiles 0-3, 4-7 of row tid % 32)
         uint4 wreg = uint4{0u, 0u, 0u, 0u};   // the conv weights (threads < P) or biases of the head after it
         float dr0 = 0.f, dr1 = 0.f;           // wave 0: its dt of rows 2 lane, 2 lane + 1
         auto prefetch = [&](int head) __attribute__((always_inline)) {
@@ -1612,8 +1672,16 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                 else if (a.conv_b) wreg = *reinterpret_cast<const uint4*>(a.conv_b + hn * P + 4 * (tid - P));
             }
             const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
+            if constexpr (Q16) {
 #pragma unroll
-            for (int k = 0; k < NHP; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + 256 * k));
+                for (int k = 0; k < NHP / 2; ++k) hq[k] = reinterpret_cast<const uint4*>(he)[tid + 256 * k];
+                const float4* hs = reinterpret_cast<const float4*>(he + P * N / 2 + (tid & 31) * NTQ);
+                hd0 = hs[0];
+                hd1 = hs[1];
+            } else {
+#pragma unroll
+                for (int k = 0; k < NHP; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + 256 * k));
+            }
             if (wave == 0) {
                 dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
                 dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
@@ -1699,8 +1767,9 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                 }
             }
             // a later segment's local entry state: its true part is added here (the
-            // loads wait in place; only split sequences take this path)
-            if (fix) {
+            // loads wait in place; only split sequences take this path, and they
+            // keep fp32 entry states)
+            if constexpr (!Q16) if (fix) {
                 const float* hf = a.states + (cslot0 * a.nheads + head) * (int64_t)(P * N);
                 const float fcum = expc(a.cum[(int64_t)cslot * a.nheads + head]);
 #pragma unroll
@@ -1710,16 +1779,33 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                                    fmaf(fcum, hs.z, hr[k].z), fmaf(fcum, hs.w, hr[k].w)};
                 }
             }
-            // h_in split planes: float4 k of the entry state covers (p, n .. n + 3)
-#pragma unroll
-            for (int k = 0; k < NHP; ++k) {
+            // h_in split planes: float4 f of the entry state covers (p, n .. n + 3)
+            auto put_h = [&](int f, float4 v) __attribute__((always_inline)) {
                 int p, n;
-                state_pn(tid + 256 * k, p, n);
+                state_pn(f, p, n);
                 uint32_t hb[2], lb[2];
-                split2(hr[k].x, hr[k].y, hb[0], lb[0]);
-                split2(hr[k].z, hr[k].w, hb[1], lb[1]);
+                split2(v.x, v.y, hb[0], lb[0]);
+                split2(v.z, v.w, hb[1], lb[1]);
                 *reinterpret_cast<uint2*>(HH + p * NRS + n) = uint2{hb[0], hb[1]};
                 *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0], lb[1]};
+            };
+            if constexpr (Q16) {
+                // uint4 tid + 256 k: tile 2 k + tid / 128, float4s f and f + 64 with
+                // f = (tile * 4 + 2 ((tid / 64) % 2)) * 64 + tid % 64
+                const bool hb2 = tid >= 128;
+                const float dk[4] = {hb2 ? hd0.y : hd0.x, hb2 ? hd0.w : hd0.z, hb2 ? hd1.y : hd1.x,
+                                     hb2 ? hd1.w : hd1.z};
+#pragma unroll
+                for (int k = 0; k < NHP / 2; ++k) {
+                    const int f = ((2 * k + (tid >> 7)) * 4 + 2 * ((tid >> 6) & 1)) * 64 + (tid & 63);
+                    float4 lo, hi;
+                    q16_values(hq[k], dk[k], lo, hi);
+                    put_h(f, lo);
+                    put_h(f + 64, hi);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < NHP; ++k) put_h(tid + 256 * k, hr[k]);
             }
             if (wave == 0) {
                 gam[bf][2 * lane] = ga0;
@@ -1971,10 +2057,11 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
 // tiles; they convolve the next unit's B (16 row groups x 16 channel groups
 // over their 256 threads) in the same stretch of code as the current unit's
 // products, so the conv's vector work fills the gaps between matrix
-// instructions, and at a chunk's start they store the entry state and scale
-// by the decay.  Every SIMD then holds one producer and one consumer, both
-// convolving.
-template <int N>
+// instructions, and at a chunk's start they store the entry state (Q16: as
+// 16-bit rows, store_entry_q16; for split sequences fp32, which the segment
+// carry reads) and scale by the decay.  Every SIMD then holds one producer and
+// one consumer, both convolving.
+template <int N, bool Q16>
 __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
     static_assert(N == 128, "two heads of 64 B channels each");
     constexpr int IPW = 2;
@@ -2199,9 +2286,12 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
             for (int hh = 0; hh < IPW; ++hh) {
                 float* he = a.states + ((cbase + c) * a.nheads + head0 + hh) * (int64_t)(P * N);
                 const float decay = sDecay[hh];
+                if constexpr (Q16) {
+                    if (store) store_entry_q16(he, acc[hh], cw, lane);
+                }
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) {
-                    if (store) {
+                    if (!Q16 && store) {
 #pragma unroll
                         for (int m = 0; m < 4; ++m)
                             *reinterpret_cast<float4*>(he + eoff(pt, m)) =
@@ -2262,9 +2352,16 @@ hipError_t launch_pass(const ScanArgs& a, hipStream_t stream) {
     const unsigned levels = a.seg > 0 ? (unsigned)a.seg_levels : 1u;
     if constexpr (N == 128) {
         if ((a.nheads / a.ngroups) % 2 == 0) {
-            if constexpr (is_raw<Tin>())
-                hipLaunchKernelGGL(ssd_state_pass_raw_kernel<N>, dim3(a.nheads * a.batch / 2 * levels), dim3(512),
-                                   0, stream, a);
+            if constexpr (is_raw<Tin>()) {
+                // 16-bit entry states unless sequences are split into segments
+                // (the segment carry joins fp32 states)
+                if (a.seg == 0)
+                    hipLaunchKernelGGL((ssd_state_pass_raw_kernel<N, true>), dim3(a.nheads * a.batch / 2 * levels),
+                                       dim3(512), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((ssd_state_pass_raw_kernel<N, false>), dim3(a.nheads * a.batch / 2 * levels),
+                                       dim3(512), 0, stream, a);
+            }
             else
                 hipLaunchKernelGGL((ssd_state_pass_kernel<N, 2, Tin>), dim3(a.nheads * a.batch / 2 * levels),
                                    dim3(512), 0, stream, a);
@@ -2291,8 +2388,14 @@ hipError_t launch_out(const ScanArgs& a, int64_t total_tokens, hipStream_t strea
     const int64_t slots = total_tokens / Q + a.batch;
     const int split = a.out_split > 1 ? a.out_split : 1;
     const dim3 grid((unsigned)(slots * a.ngroups * split));
-    if constexpr (is_raw<Tin>())
-        hipLaunchKernelGGL(ssd_chunk_out_raw_kernel<N>, grid, dim3(512), 0, stream, a);
+    if constexpr (is_raw<Tin>()) {
+        // the entry-state format the raw state pass wrote: 16-bit at dstate 128
+        // unless sequences are split into segments
+        if (N == 128 && a.seg == 0)
+            hipLaunchKernelGGL((ssd_chunk_out_raw_kernel<N, N == 128>), grid, dim3(512), 0, stream, a);
+        else
+            hipLaunchKernelGGL((ssd_chunk_out_raw_kernel<N, false>), grid, dim3(512), 0, stream, a);
+    }
     else
         hipLaunchKernelGGL((ssd_chunk_out_kernel<N, Tin>), grid, dim3(512), 0, stream, a);
     return hipGetLastError();

@@ -66,9 +66,27 @@ def round_fp16_block(v: np.ndarray) -> np.ndarray:
     return np.ldexp(round_fp16(np.ldexp(v, k)), -k)
 
 
+def round_q16_rows(v: np.ndarray, run: int = 32) -> np.ndarray:
+    """16-bit fixed point with one scale per run of `run` values along the last
+    axis (for a P x N state: per p and n tile of 32): s = fp32(max |v| of the
+    run), q = round-half-even(clip(v / s, -1, 1) * 32767), read back as
+    q * (s / 32767).  Absolute error at most s / 65534 per value: each run
+    keeps 15 bits below its largest magnitude, whatever the exponent spread."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    for n0 in range(0, v.shape[-1], run):
+        r = v[..., n0:n0 + run]
+        sc = np.max(np.abs(r), axis=-1, keepdims=True).astype(np.float32).astype(np.float64)
+        safe = np.where(sc > 0.0, sc, 1.0)
+        q = np.round(np.clip(r / safe, -1.0, 1.0) * 32767.0)
+        out[..., n0:n0 + run] = np.where(sc > 0.0, q * (sc / 32767.0), 0.0)
+    return out
+
+
 FORMATS: Dict[str, Callable[[np.ndarray], np.ndarray]] = {
     "fp64": lambda v: np.asarray(v, dtype=np.float64), "fp32": round_fp32,
-    "fp16": round_fp16, "bf16": round_bf16, "fp16_block": round_fp16_block}
+    "fp16": round_fp16, "bf16": round_bf16, "fp16_block": round_fp16_block,
+    "q16_rows": round_q16_rows}
 
 
 def rel_max(got: np.ndarray, ref: np.ndarray) -> float:
