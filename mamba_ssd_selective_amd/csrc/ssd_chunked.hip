@@ -1573,474 +1573,490 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
     const int64_t L = a.cu_seqlens[seq + 1] - s0;
     const int64_t c = cslot - (s0 / Q + seq);
     if (c * Q >= L) return;
-    const int S = (int)((L - c * Q) < Q ? (L - c * Q) : Q);
-    const int64_t r0 = s0 + c * Q;
-    const int slot = a.state_idx ? a.state_idx[seq] : seq;
-    const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
-    const int d_inner = a.nheads * P;
-    // In a split sequence, a chunk after the first of a later segment holds a
-    // local entry state: the true one adds e(log decay since the segment's start)
-    // times the segment's true entry state (its first chunk's slot).
-    // (the last segment takes every chunk from its start on)
-    const int kseg = a.seg > 0 ? min((int)(c / a.seg), a.seg_levels - 1) : 0;
-    const bool fix = kseg >= 1 && c != (int64_t)kseg * a.seg;
-    const int64_t cslot0 = cslot - (fix ? c - (int64_t)kseg * a.seg : 0);
+    const int S_ = (int)((L - c * Q) < Q ? (L - c * Q) : Q);
+    // At dstate 128 the rest of the kernel is compiled twice: for a full chunk
+    // (every chunk but a sequence's last), with its row count a constant, so
+    // every row test and bound folds away (the copy also needs 29 fewer vector
+    // registers), and for a partial one.  The LDS arrays above serve both.
+    auto body = [&](auto sqc) __attribute__((always_inline)) {
+        constexpr int SQ = decltype(sqc)::value;
+        const int S = SQ ? SQ : S_;
+        const int64_t r0 = s0 + c * Q;
+        const int slot = a.state_idx ? a.state_idx[seq] : seq;
+        const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
+        const int d_inner = a.nheads * P;
+        // In a split sequence, a chunk after the first of a later segment holds a
+        // local entry state: the true one adds e(log decay since the segment's start)
+        // times the segment's true entry state (its first chunk's slot).
+        // (the last segment takes every chunk from its start on)
+        const int kseg = a.seg > 0 ? min((int)(c / a.seg), a.seg_levels - 1) : 0;
+        const bool fix = kseg >= 1 && c != (int64_t)kseg * a.seg;
+        const int64_t cslot0 = cslot - (fix ? c - (int64_t)kseg * a.seg : 0);
 
-    // LDS tables: A and D of the group's heads, the G-phase conv weights (B
-    // channels, then C channels), the first head's x conv weights
-    for (int e = tid; e < hpg; e += NT) {
-        sA[e] = a.A[grp * hpg + e];
-        sD[e] = a.D ? a.D[grp * hpg + e] : 0.f;
-    }
-    for (int e = tid; e < 2 * N; e += NT) {
-        const int ch = d_inner + (e < N ? grp * N + e : G * N + grp * N + (e - N));
-        gW[wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
-        gBias[e] = a.conv_b ? a.conv_b[ch] : 0.f;
-    }
-    for (int e = tid; e < P; e += NT) {
-        const int ch = (grp * hpg + j0) * P + e;
-        sXW[0][wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
-        sXB[0][e] = a.conv_b ? a.conv_b[ch] : 0.f;
-    }
-
-    // G phase: each thread convolves one piece (RR rows x 8 channels) of each
-    // 64-n slice, of B (producers) or C (consumers), into the slice planes.
-    const bool gIsB = wave < 4;
-    const int g_cg = lane >> 3, g_rg = (lane & 7) + 8 * (wave & 3);
-    auto g_load = [&](uint4 (&graw)[NPASS][RW]) __attribute__((always_inline)) {
-        const int64_t gld = gIsB ? a.ld_B : a.ld_C;
-        const uint16_t* gcol = gIsB ? static_cast<const uint16_t*>(a.B) + r0 * a.ld_B + grp * a.gs_B
-                                  : static_cast<const uint16_t*>(a.C) + r0 * a.ld_C + grp * a.gs_C;
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps)
-            load_raw_piece(gcol + 64 * ps + 8 * g_cg, (int)gld, 4 * g_rg, (int)(-c * Q), (int)(L - 1 - c * Q),
-                           (lane & 7) == 0, graw[ps]);
-    };
-    auto g_conv = [&](int ps, uint4 (&gr)[RW]) __attribute__((always_inline)) {
-        raw_halo(gr, lane);
-        const int row0 = 4 * g_rg;
-        const bool start = c == 0 && row0 == 0;
-        const int wi = (gIsB ? 0 : N) + 64 * ps + 8 * g_cg;
-        const int ch0 = d_inner + (gIsB ? 0 : G * N) + grp * N + 64 * ps + 8 * g_cg;
-        u16* const dh = gIsB ? Bh : Ch;
-        u16* const dl = gIsB ? Bl : Cl;
-        const ConvW cw = read_convw(gW, gBias, wi);
-        // one output row (8 channels) at a time; window row j of output row tt
-        // is raw row tt + j, or for a piece that starts the sequence and
-        // tt + j < 3, carried row tt + j of the conv state
-#pragma unroll
-        for (int tt = 0; tt < RR; ++tt) {
-            float v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float4 w4 = cw.w(k);
-                const float wk[4] = {w4.x, w4.y, w4.z, w4.w};
-                float acc = cw.b[k];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float xv = bf16_lane(gr[tt + j], k);
-                    if (tt + j < 3 && start)
-                        xv = init ? a.conv_state[((int64_t)slot * 3 + tt + j) * a.conv_dim + ch0 + k] : 0.f;
-                    acc = fmaf(wk[j], xv, acc);
-                }
-                v[k] = silu(acc);
-            }
-            uint4 h4, l4;
-            split8(v, h4, l4);
-            const int off = (row0 + tt) * HR + 8 * g_cg;
-            *reinterpret_cast<uint4*>(dh + off) = h4;
-            *reinterpret_cast<uint4*>(dl + off) = l4;
+        // LDS tables: A and D of the group's heads, the G-phase conv weights (B
+        // channels, then C channels), the first head's x conv weights
+        for (int e = tid; e < hpg; e += NT) {
+            sA[e] = a.A[grp * hpg + e];
+            sD[e] = a.D ? a.D[grp * hpg + e] : 0.f;
         }
-    };
+        for (int e = tid; e < 2 * N; e += NT) {
+            const int ch = d_inner + (e < N ? grp * N + e : G * N + grp * N + (e - N));
+            gW[wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
+            gBias[e] = a.conv_b ? a.conv_b[ch] : 0.f;
+        }
+        for (int e = tid; e < P; e += NT) {
+            const int ch = (grp * hpg + j0) * P + e;
+            sXW[0][wsw(e)] = *reinterpret_cast<const float4*>(a.conv_w + (int64_t)ch * 4);
+            sXB[0][e] = a.conv_b ? a.conv_b[ch] : 0.f;
+        }
 
-    if (wave < 4) {
-        // ---------------------------------------------------------- producers
-        const int x_cg = lane >> 3, x_rg = (lane & 7) + 8 * wave;
-        uint4 xraw[RW];           // the x piece of the head being prefetched: 8 channels x RR rows
-        float4 hr[Q16 ? 1 : NHP]; // its h_in (fp32 entry states)
-        uint4 hq[Q16 ? NHP / 2 : 1];   // or its 16-bit values
-        float4 hd0, hd1;               // and their row scales (tiles 0-3, 4-7 of row tid % 32)
-        uint4 wreg = uint4{0u, 0u, 0u, 0u};   // the conv weights (threads < P) or biases of the head after it
-        float dr0 = 0.f, dr1 = 0.f;           // wave 0: its dt of rows 2 lane, 2 lane + 1
-        auto prefetch = [&](int head) __attribute__((always_inline)) {
-            load_raw_piece(static_cast<const uint16_t*>(a.x) + r0 * a.ld_x + head * a.hs_x + 8 * x_cg, (int)a.ld_x,
-                           4 * x_rg, (int)(-c * Q), (int)(L - 1 - c * Q), (lane & 7) == 0, xraw);
-            if (tid < P + P / 4) {
-                const int hn = head + 1 < grp * hpg + j1 ? head + 1 : head;
-                wreg = uint4{0u, 0u, 0u, 0u};
-                if (tid < P) wreg = *reinterpret_cast<const uint4*>(a.conv_w + ((int64_t)hn * P + tid) * 4);
-                else if (a.conv_b) wreg = *reinterpret_cast<const uint4*>(a.conv_b + hn * P + 4 * (tid - P));
-            }
-            const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
-            if constexpr (Q16) {
+        // G phase: each thread convolves one piece (RR rows x 8 channels) of each
+        // 64-n slice, of B (producers) or C (consumers), into the slice planes.
+        const bool gIsB = wave < 4;
+        const int g_cg = lane >> 3, g_rg = (lane & 7) + 8 * (wave & 3);
+        auto g_load = [&](uint4 (&graw)[NPASS][RW]) __attribute__((always_inline)) {
+            const int64_t gld = gIsB ? a.ld_B : a.ld_C;
+            const uint16_t* gcol = gIsB ? static_cast<const uint16_t*>(a.B) + r0 * a.ld_B + grp * a.gs_B
+                                      : static_cast<const uint16_t*>(a.C) + r0 * a.ld_C + grp * a.gs_C;
 #pragma unroll
-                for (int k = 0; k < NHP / 2; ++k) hq[k] = reinterpret_cast<const uint4*>(he)[tid + 256 * k];
-                const float4* hs = reinterpret_cast<const float4*>(he + P * N / 2 + (tid & 31) * NTQ);
-                hd0 = hs[0];
-                hd1 = hs[1];
-            } else {
+            for (int ps = 0; ps < NPASS; ++ps)
+                load_raw_piece(gcol + 64 * ps + 8 * g_cg, (int)gld, 4 * g_rg, (int)(-c * Q), (int)(L - 1 - c * Q),
+                               (lane & 7) == 0, graw[ps]);
+        };
+        auto g_conv = [&](int ps, uint4 (&gr)[RW]) __attribute__((always_inline)) {
+            raw_halo(gr, lane);
+            const int row0 = 4 * g_rg;
+            const bool start = c == 0 && row0 == 0;
+            const int wi = (gIsB ? 0 : N) + 64 * ps + 8 * g_cg;
+            const int ch0 = d_inner + (gIsB ? 0 : G * N) + grp * N + 64 * ps + 8 * g_cg;
+            u16* const dh = gIsB ? Bh : Ch;
+            u16* const dl = gIsB ? Bl : Cl;
+            const ConvW cw = read_convw(gW, gBias, wi);
+            // one output row (8 channels) at a time; window row j of output row tt
+            // is raw row tt + j, or for a piece that starts the sequence and
+            // tt + j < 3, carried row tt + j of the conv state
 #pragma unroll
-                for (int k = 0; k < NHP; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + 256 * k));
-            }
-            if (wave == 0) {
-                dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
-                dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
+            for (int tt = 0; tt < RR; ++tt) {
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 w4 = cw.w(k);
+                    const float wk[4] = {w4.x, w4.y, w4.z, w4.w};
+                    float acc = cw.b[k];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float xv = bf16_lane(gr[tt + j], k);
+                        if (tt + j < 3 && start)
+                            xv = init ? a.conv_state[((int64_t)slot * 3 + tt + j) * a.conv_dim + ch0 + k] : 0.f;
+                        acc = fmaf(wk[j], xv, acc);
+                    }
+                    v[k] = silu(acc);
+                }
+                uint4 h4, l4;
+                split8(v, h4, l4);
+                const int off = (row0 + tt) * HR + 8 * g_cg;
+                *reinterpret_cast<uint4*>(dh + off) = h4;
+                *reinterpret_cast<uint4*>(dl + off) = l4;
             }
         };
-        // Stage head j (whose loads are in xraw / hr / dr / wreg) into head buffer bf.
-        auto stage = [&](int bf, int j) __attribute__((always_inline)) {
-            u16* Xh = smem + bf * HBUF;
-            u16* Xl = Xh + P * RS;
-            u16* HH = Xh + HX;
-            u16* HL = HH + P * NRS;
-            const int head = grp * hpg + j;
-            // wave 0: gamma and the decay factors of this head, from the prefetched dt
-            double ga0 = 0.0, ga1 = 0.0;
-            float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
-            if (wave == 0) {
-                gamma_scan(dr0, dr1, sA[j], ga0, ga1);
-                // rows 2 lane, 2 lane + 1 lie in tile lane / 8, whose last row 16 (lane / 8) + 15
-                // is held (as ga1) by lane 8 (lane / 8) + 7
-                double gri[8];
-#pragma unroll
-                for (int it = 0; it < 8; ++it) gri[it] = readlane_f64(ga1, 8 * it + 7);
-                double gr = gri[0];
-#pragma unroll
-                for (int it = 1; it < 8; ++it) gr = (lane >> 3) == it ? gri[it] : gr;
-                rf0 = dr0 * expc(gr - ga0);
-                rf1 = dr1 * expc(gr - ga1);
-#pragma unroll
-                for (int it = 0; it < 8; ++it) {
-                    cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri[it]) : 0.f;
-                    cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri[it]) : 0.f;
+
+        if (wave < 4) {
+            // ---------------------------------------------------------- producers
+            const int x_cg = lane >> 3, x_rg = (lane & 7) + 8 * wave;
+            uint4 xraw[RW];           // the x piece of the head being prefetched: 8 channels x RR rows
+            float4 hr[Q16 ? 1 : NHP]; // its h_in (fp32 entry states)
+            uint4 hq[Q16 ? NHP / 2 : 1];   // or its 16-bit values
+            float4 hd0, hd1;               // and their row scales (tiles 0-3, 4-7 of row tid % 32)
+            uint4 wreg = uint4{0u, 0u, 0u, 0u};   // the conv weights (threads < P) or biases of the head after it
+            float dr0 = 0.f, dr1 = 0.f;           // wave 0: its dt of rows 2 lane, 2 lane + 1
+            auto prefetch = [&](int head) __attribute__((always_inline)) {
+                load_raw_piece(static_cast<const uint16_t*>(a.x) + r0 * a.ld_x + head * a.hs_x + 8 * x_cg, (int)a.ld_x,
+                               4 * x_rg, (int)(-c * Q), (int)(L - 1 - c * Q), (lane & 7) == 0, xraw);
+                if (tid < P + P / 4) {
+                    const int hn = head + 1 < grp * hpg + j1 ? head + 1 : head;
+                    wreg = uint4{0u, 0u, 0u, 0u};
+                    if (tid < P) wreg = *reinterpret_cast<const uint4*>(a.conv_w + ((int64_t)hn * P + tid) * 4);
+                    else if (a.conv_b) wreg = *reinterpret_cast<const uint4*>(a.conv_b + hn * P + 4 * (tid - P));
                 }
-            }
-            // the next head's conv weights into the other buffer (read one phase later)
-            if (tid < P) {
-                sXW[bf ^ 1][wsw(tid)] = __builtin_bit_cast(float4, wreg);
-            } else if (tid < P + P / 4) {
-                *reinterpret_cast<float4*>(&sXB[bf ^ 1][4 * (tid - P)]) = __builtin_bit_cast(float4, wreg);
-            }
-            // conv + SiLU of the x piece: rows 4 x_rg .. + 3 of the chunk, placed at
-            // their positions in the K-slot order of the x^T planes (row i sits at
-            // 8 (4 (i / 32) + (i / 4) % 4) + 4 ((i / 16) % 2) + i % 4), the 32-row
-            // block i / 32 swizzled by plane row (xsw)
-            {
-                raw_halo(xraw, lane);
-                const int row0 = 4 * x_rg;
-                const bool start = c == 0 && row0 == 0;
-                const int pos = 8 * ((row0 >> 2) & 3) + 4 * ((row0 >> 4) & 1);
-                auto put = [&](int k, float (&u)[RR]) __attribute__((always_inline)) {
-                    if (S < Q) {
+                const float* he = a.states + ((s0 / Q + seq + c) * a.nheads + head) * (int64_t)(P * N);
+                if constexpr (Q16) {
 #pragma unroll
-                        for (int tt = 0; tt < RR; ++tt)
-                            if (row0 + tt >= S) u[tt] = 0.f;
+                    for (int k = 0; k < NHP / 2; ++k) hq[k] = reinterpret_cast<const uint4*>(he)[tid + 256 * k];
+                    const float4* hs = reinterpret_cast<const float4*>(he + P * N / 2 + (tid & 31) * NTQ);
+                    hd0 = hs[0];
+                    hd1 = hs[1];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NHP; ++k) hr[k] = *reinterpret_cast<const float4*>(he + 4 * (tid + 256 * k));
+                }
+                if (wave == 0) {
+                    dr0 = (2 * lane < S) ? a.dt[(r0 + 2 * lane) * a.ld_dt + head] : 0.f;
+                    dr1 = (2 * lane + 1 < S) ? a.dt[(r0 + 2 * lane + 1) * a.ld_dt + head] : 0.f;
+                }
+            };
+            // Stage head j (whose loads are in xraw / hr / dr / wreg) into head buffer bf.
+            auto stage = [&](int bf, int j) __attribute__((always_inline)) {
+                u16* Xh = smem + bf * HBUF;
+                u16* Xl = Xh + P * RS;
+                u16* HH = Xh + HX;
+                u16* HL = HH + P * NRS;
+                const int head = grp * hpg + j;
+                // wave 0: gamma and the decay factors of this head, from the prefetched dt
+                double ga0 = 0.0, ga1 = 0.0;
+                float rf0 = 0.f, rf1 = 0.f, cf0[8], cf1[8];
+                if (wave == 0) {
+                    gamma_scan(dr0, dr1, sA[j], ga0, ga1);
+                    // rows 2 lane, 2 lane + 1 lie in tile lane / 8, whose last row 16 (lane / 8) + 15
+                    // is held (as ga1) by lane 8 (lane / 8) + 7
+                    double gri[8];
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) gri[it] = readlane_f64(ga1, 8 * it + 7);
+                    double gr = gri[0];
+#pragma unroll
+                    for (int it = 1; it < 8; ++it) gr = (lane >> 3) == it ? gri[it] : gr;
+                    rf0 = dr0 * expc(gr - ga0);
+                    rf1 = dr1 * expc(gr - ga1);
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
+                        cf0[it] = (it < (lane >> 3)) ? expc(ga0 - gri[it]) : 0.f;
+                        cf1[it] = (it < (lane >> 3)) ? expc(ga1 - gri[it]) : 0.f;
                     }
+                }
+                // the next head's conv weights into the other buffer (read one phase later)
+                if (tid < P) {
+                    sXW[bf ^ 1][wsw(tid)] = __builtin_bit_cast(float4, wreg);
+                } else if (tid < P + P / 4) {
+                    *reinterpret_cast<float4*>(&sXB[bf ^ 1][4 * (tid - P)]) = __builtin_bit_cast(float4, wreg);
+                }
+                // conv + SiLU of the x piece: rows 4 x_rg .. + 3 of the chunk, placed at
+                // their positions in the K-slot order of the x^T planes (row i sits at
+                // 8 (4 (i / 32) + (i / 4) % 4) + 4 ((i / 16) % 2) + i % 4), the 32-row
+                // block i / 32 swizzled by plane row (xsw)
+                {
+                    raw_halo(xraw, lane);
+                    const int row0 = 4 * x_rg;
+                    const bool start = c == 0 && row0 == 0;
+                    const int pos = 8 * ((row0 >> 2) & 3) + 4 * ((row0 >> 4) & 1);
+                    auto put = [&](int k, float (&u)[RR]) __attribute__((always_inline)) {
+                        if (S < Q) {
+#pragma unroll
+                            for (int tt = 0; tt < RR; ++tt)
+                                if (row0 + tt >= S) u[tt] = 0.f;
+                        }
+                        uint32_t hb[2], lb[2];
+                        split2(u[0], u[1], hb[0], lb[0]);
+                        split2(u[2], u[3], hb[1], lb[1]);
+                        const int off = (8 * x_cg + k) * RS + 32 * xsw(row0 >> 5, 8 * x_cg + k) + pos;
+                        *reinterpret_cast<uint2*>(Xh + off) = uint2{hb[0], hb[1]};
+                        *reinterpret_cast<uint2*>(Xl + off) = uint2{lb[0], lb[1]};
+                    };
+                    // (the producers have the registers to hold all 8 channels' weights)
+                    const ConvW cw = read_convw(sXW[bf], sXB[bf], 8 * x_cg);
+                    float4 wv[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) wv[k] = cw.w(k);
+                    if (start) {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            float u[RR];
+                            conv_piece_start(xraw, k, a.conv_state, a.conv_dim, slot, init, head * P + 8 * x_cg,
+                                             wv[k], cw.b[k], u);
+                            put(k, u);
+                        }
+                    } else {
+                        const float hv[3][8] = {};
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            float u[RR];
+                            conv_piece(xraw, k, false, hv, wv[k], cw.b[k], u);
+                            put(k, u);
+                        }
+                    }
+                }
+                // a later segment's local entry state: its true part is added here (the
+                // loads wait in place; only split sequences take this path, and they
+                // keep fp32 entry states)
+                if constexpr (!Q16) if (fix) {
+                    const float* hf = a.states + (cslot0 * a.nheads + head) * (int64_t)(P * N);
+                    const float fcum = expc(a.cum[(int64_t)cslot * a.nheads + head]);
+#pragma unroll
+                    for (int k = 0; k < NHP; ++k) {
+                        const float4 hs = *reinterpret_cast<const float4*>(hf + 4 * (tid + 256 * k));
+                        hr[k] = float4{fmaf(fcum, hs.x, hr[k].x), fmaf(fcum, hs.y, hr[k].y),
+                                       fmaf(fcum, hs.z, hr[k].z), fmaf(fcum, hs.w, hr[k].w)};
+                    }
+                }
+                // h_in split planes: float4 f of the entry state covers (p, n .. n + 3)
+                auto put_h = [&](int f, float4 v) __attribute__((always_inline)) {
+                    int p, n;
+                    state_pn(f, p, n);
                     uint32_t hb[2], lb[2];
-                    split2(u[0], u[1], hb[0], lb[0]);
-                    split2(u[2], u[3], hb[1], lb[1]);
-                    const int off = (8 * x_cg + k) * RS + 32 * xsw(row0 >> 5, 8 * x_cg + k) + pos;
-                    *reinterpret_cast<uint2*>(Xh + off) = uint2{hb[0], hb[1]};
-                    *reinterpret_cast<uint2*>(Xl + off) = uint2{lb[0], lb[1]};
+                    split2(v.x, v.y, hb[0], lb[0]);
+                    split2(v.z, v.w, hb[1], lb[1]);
+                    *reinterpret_cast<uint2*>(HH + p * NRS + n) = uint2{hb[0], hb[1]};
+                    *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0], lb[1]};
                 };
-                // (the producers have the registers to hold all 8 channels' weights)
-                const ConvW cw = read_convw(sXW[bf], sXB[bf], 8 * x_cg);
-                float4 wv[8];
+                if constexpr (Q16) {
+                    // uint4 tid + 256 k: tile 2 k + tid / 128, float4s f and f + 64 with
+                    // f = (tile * 4 + 2 ((tid / 64) % 2)) * 64 + tid % 64
+                    const bool hb2 = tid >= 128;
+                    const float dk[4] = {hb2 ? hd0.y : hd0.x, hb2 ? hd0.w : hd0.z, hb2 ? hd1.y : hd1.x,
+                                         hb2 ? hd1.w : hd1.z};
 #pragma unroll
-                for (int k = 0; k < 8; ++k) wv[k] = cw.w(k);
-                if (start) {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        float u[RR];
-                        conv_piece_start(xraw, k, a.conv_state, a.conv_dim, slot, init, head * P + 8 * x_cg,
-                                         wv[k], cw.b[k], u);
-                        put(k, u);
+                    for (int k = 0; k < NHP / 2; ++k) {
+                        const int f = ((2 * k + (tid >> 7)) * 4 + 2 * ((tid >> 6) & 1)) * 64 + (tid & 63);
+                        float4 lo, hi;
+                        q16_values(hq[k], dk[k], lo, hi);
+                        put_h(f, lo);
+                        put_h(f + 64, hi);
                     }
                 } else {
-                    const float hv[3][8] = {};
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        float u[RR];
-                        conv_piece(xraw, k, false, hv, wv[k], cw.b[k], u);
-                        put(k, u);
-                    }
+                    for (int k = 0; k < NHP; ++k) put_h(tid + 256 * k, hr[k]);
                 }
-            }
-            // a later segment's local entry state: its true part is added here (the
-            // loads wait in place; only split sequences take this path, and they
-            // keep fp32 entry states)
-            if constexpr (!Q16) if (fix) {
-                const float* hf = a.states + (cslot0 * a.nheads + head) * (int64_t)(P * N);
-                const float fcum = expc(a.cum[(int64_t)cslot * a.nheads + head]);
-#pragma unroll
-                for (int k = 0; k < NHP; ++k) {
-                    const float4 hs = *reinterpret_cast<const float4*>(hf + 4 * (tid + 256 * k));
-                    hr[k] = float4{fmaf(fcum, hs.x, hr[k].x), fmaf(fcum, hs.y, hr[k].y),
-                                   fmaf(fcum, hs.z, hr[k].z), fmaf(fcum, hs.w, hr[k].w)};
+                if (wave == 0) {
+                    gam[bf][2 * lane] = ga0;
+                    gam[bf][2 * lane + 1] = ga1;
+                    dts[bf][2 * lane] = dr0;
+                    dts[bf][2 * lane + 1] = dr1;
+                    din[bf][2 * lane] = expc(ga0);
+                    din[bf][2 * lane + 1] = expc(ga1);
+                    rowf[bf][2 * lane] = rf0;
+                    rowf[bf][2 * lane + 1] = rf1;
+                    *reinterpret_cast<float4*>(colf[bf] + 16 * lane) = float4{cf0[0], cf0[1], cf0[2], cf0[3]};
+                    *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 4) = float4{cf0[4], cf0[5], cf0[6], cf0[7]};
+                    *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 8) = float4{cf1[0], cf1[1], cf1[2], cf1[3]};
+                    *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 12) = float4{cf1[4], cf1[5], cf1[6], cf1[7]};
                 }
-            }
-            // h_in split planes: float4 f of the entry state covers (p, n .. n + 3)
-            auto put_h = [&](int f, float4 v) __attribute__((always_inline)) {
-                int p, n;
-                state_pn(f, p, n);
-                uint32_t hb[2], lb[2];
-                split2(v.x, v.y, hb[0], lb[0]);
-                split2(v.z, v.w, hb[1], lb[1]);
-                *reinterpret_cast<uint2*>(HH + p * NRS + n) = uint2{hb[0], hb[1]};
-                *reinterpret_cast<uint2*>(HL + p * NRS + n) = uint2{lb[0], lb[1]};
             };
-            if constexpr (Q16) {
-                // uint4 tid + 256 k: tile 2 k + tid / 128, float4s f and f + 64 with
-                // f = (tile * 4 + 2 ((tid / 64) % 2)) * 64 + tid % 64
-                const bool hb2 = tid >= 128;
-                const float dk[4] = {hb2 ? hd0.y : hd0.x, hb2 ? hd0.w : hd0.z, hb2 ? hd1.y : hd1.x,
-                                     hb2 ? hd1.w : hd1.z};
-#pragma unroll
-                for (int k = 0; k < NHP / 2; ++k) {
-                    const int f = ((2 * k + (tid >> 7)) * 4 + 2 * ((tid >> 6) & 1)) * 64 + (tid & 63);
-                    float4 lo, hi;
-                    q16_values(hq[k], dk[k], lo, hi);
-                    put_h(f, lo);
-                    put_h(f + 64, hi);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < NHP; ++k) put_h(tid + 256 * k, hr[k]);
-            }
-            if (wave == 0) {
-                gam[bf][2 * lane] = ga0;
-                gam[bf][2 * lane + 1] = ga1;
-                dts[bf][2 * lane] = dr0;
-                dts[bf][2 * lane + 1] = dr1;
-                din[bf][2 * lane] = expc(ga0);
-                din[bf][2 * lane + 1] = expc(ga1);
-                rowf[bf][2 * lane] = rf0;
-                rowf[bf][2 * lane + 1] = rf1;
-                *reinterpret_cast<float4*>(colf[bf] + 16 * lane) = float4{cf0[0], cf0[1], cf0[2], cf0[3]};
-                *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 4) = float4{cf0[4], cf0[5], cf0[6], cf0[7]};
-                *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 8) = float4{cf1[0], cf1[1], cf1[2], cf1[3]};
-                *reinterpret_cast<float4*>(colf[bf] + 16 * lane + 12) = float4{cf1[4], cf1[5], cf1[6], cf1[7]};
-            }
-        };
 
-        uint4 graw[NPASS][RW];
-        g_load(graw);
-        prefetch(grp * hpg + j0);
-        __syncthreads();   // LDS tables
+            uint4 graw[NPASS][RW];
+            g_load(graw);
+            prefetch(grp * hpg + j0);
+            __syncthreads();   // LDS tables
 #pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-            if (ps > 0) __syncthreads();   // the previous slice's products are done
-            g_conv(ps, graw[ps]);
+            for (int ps = 0; ps < NPASS; ++ps) {
+                if (ps > 0) __syncthreads();   // the previous slice's products are done
+                g_conv(ps, graw[ps]);
+                __syncthreads();
+            }
+            stage(0, j0);   // (buffer 0: no G slice there, and the G-phase weights are read)
+            if (j0 + 1 < j1) prefetch(grp * hpg + j0 + 1);
             __syncthreads();
-        }
-        stage(0, j0);   // (buffer 0: no G slice there, and the G-phase weights are read)
-        if (j0 + 1 < j1) prefetch(grp * hpg + j0 + 1);
-        __syncthreads();
-        for (int j = j0; j < j1; ++j) {
-            if (j + 1 < j1) {
-                stage((j - j0 + 1) & 1, j + 1);
-                if (j + 2 < j1) prefetch(grp * hpg + j + 2);
-            }
-            __syncthreads();
-        }
-    } else {
-        // ---------------------------------------------------------- consumers
-        auto consumer = [&](auto TAc) __attribute__((always_inline)) {
-            constexpr int TA = decltype(TAc)::value;
-            constexpr int TB = 7 - TA;
-            // this lane's output rows.  Tiles past a short chunk's end are
-            // multiplied all the same (their rows are finite: B and C rows are
-            // clamped into the sequence, x rows and dt are 0 there) and not
-            // stored: the products stay free of branches.
-            const int tA = 16 * TA + l16, tB = 16 * TB + l16;
-            // C operands of the two tiles (column t, K = n), kept for every head
-            bf16x8_t chA[NKB], clA[NKB], chB[NKB], clB[NKB];
-            // G^T[i, t] = B_i . C_t for the i tiles it <= T of each tile
-            f32x4_t gtA[TA + 1], gtB[TB + 1];
-#pragma unroll
-            for (int it = 0; it <= TA; ++it) gtA[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int it = 0; it <= TB; ++it) gtB[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-            {
-                uint4 graw[NPASS][RW];
-                g_load(graw);
-                __syncthreads();   // LDS tables
-#pragma unroll
-                for (int ps = 0; ps < NPASS; ++ps) {
-                    if (ps > 0) __syncthreads();
-                    g_conv(ps, graw[ps]);
-                    __syncthreads();
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        const int k = 2 * ps + k2;
-                        chA[k] = as_bf16x8(lds128(Ch + tA * HR + 32 * k2 + 8 * q));
-                        clA[k] = as_bf16x8(lds128(Cl + tA * HR + 32 * k2 + 8 * q));
-                        chB[k] = as_bf16x8(lds128(Ch + tB * HR + 32 * k2 + 8 * q));
-                        clB[k] = as_bf16x8(lds128(Cl + tB * HR + 32 * k2 + 8 * q));
-#pragma unroll
-                        for (int it = 0; it <= TB; ++it) {
-                            const int row = (16 * it + l16) * HR + 32 * k2 + 8 * q;
-                            const bf16x8_t bh = as_bf16x8(lds128(Bh + row));
-                            const bf16x8_t bl = as_bf16x8(lds128(Bl + row));
-                            mma2<true, true>(gtB[it], bh, bl, chB[k], clB[k]);
-                            if (it <= TA) mma2<true, true>(gtA[it], bh, bl, chA[k], clA[k]);
-                        }
-                    }
-                }
-            }
-            __syncthreads();   // the first head is staged
-
             for (int j = j0; j < j1; ++j) {
-                const int bf = (j - j0) & 1;
-                const int head = grp * hpg + j;
-                const float Dh = sD[j];
-                const u16* Xh = smem + bf * HBUF;
-                const u16* Xl = Xh + P * RS;
-                const u16* HH = Xh + HX;
-                const u16* HL = HH + P * NRS;
-                const float* rowfb = rowf[bf];
-                const float* dtsb = dts[bf];
-                const double* gamb = gam[bf];
-                // y^T[p, t] tiles: lane has t, p = 16 pt + 4q + r
-                f32x4_t yA[4], yB[4];
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    yA[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    yB[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                }
-                // inter-chunk term: h_in C^T (A = h_in rows p, B = C columns t, K = n)
-#pragma unroll
-                for (int k = 0; k < NKB; ++k) {
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const bf16x8_t ah = as_bf16x8(lds128(HH + (16 * pt + l16) * NRS + 32 * k + 8 * q));
-                        const bf16x8_t al = as_bf16x8(lds128(HL + (16 * pt + l16) * NRS + 32 * k + 8 * q));
-                        mma2<true, true>(yA[pt], ah, al, chA[k], clA[k]);
-                        mma2<true, true>(yB[pt], ah, al, chB[k], clB[k]);
-                    }
-                }
-                {
-                    const float sa = din[bf][tA], sb = din[bf][tB];
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        yA[pt] *= sa;
-                        yB[pt] *= sb;
-                    }
-                }
-                // intra-chunk term: X^T M^T over i tile pairs (2kb, 2kb+1); the M^T
-                // operand slot s < 4 is row 4q + s of tile 2kb, s >= 4 row 4q + s - 4
-                // of tile 2kb + 1 (the rows this lane's accumulators hold); the x^T
-                // planes hold the rows in that order (8 per (kb, q) group).
-                float cfA[8], cfB[8];
-                {
-                    const float4* ca = reinterpret_cast<const float4*>(colf[bf] + 8 * tA);
-                    const float4* cb = reinterpret_cast<const float4*>(colf[bf] + 8 * tB);
-                    const float4 a0 = ca[0], a1 = ca[1], b0 = cb[0], b1 = cb[1];
-                    cfA[0] = a0.x; cfA[1] = a0.y; cfA[2] = a0.z; cfA[3] = a0.w;
-                    cfA[4] = a1.x; cfA[5] = a1.y; cfA[6] = a1.z; cfA[7] = a1.w;
-                    cfB[0] = b0.x; cfB[1] = b0.y; cfB[2] = b0.z; cfB[3] = b0.w;
-                    cfB[4] = b1.x; cfB[5] = b1.y; cfB[6] = b1.z; cfB[7] = b1.w;
-                }
-                // M^T slots of tile TT (column t) for i tiles 2kb, 2kb + 1
-                auto mslots = [&](auto TTc, int kb, const f32x4_t* gT, const float (&cfv)[8], int t,
-                                  bf16x8_t& mh, bf16x8_t& ml) __attribute__((always_inline)) {
-                    constexpr int TT = decltype(TTc)::value;
-                    float m[8];
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int it = 2 * kb + h2;
-                        const int i0 = 16 * it + 4 * q;
-                        if (it < TT) {
-                            const float4 rf = *reinterpret_cast<const float4*>(rowfb + i0);
-                            const float cv = cfv[it];
-                            m[4 * h2 + 0] = gT[it][0] * rf.x * cv;
-                            m[4 * h2 + 1] = gT[it][1] * rf.y * cv;
-                            m[4 * h2 + 2] = gT[it][2] * rf.z * cv;
-                            m[4 * h2 + 3] = gT[it][3] * rf.w * cv;
-                        } else if (it == TT) {
-                            // the diagonal tile, branch-free: for i > t the clamped
-                            // exponent gives a finite factor that the select drops
-                            const double gt = gamb[t];
-                            const float4 d4 = *reinterpret_cast<const float4*>(dtsb + i0);
-                            const double2 ga = *reinterpret_cast<const double2*>(gamb + i0);
-                            const double2 gb = *reinterpret_cast<const double2*>(gamb + i0 + 2);
-                            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-                            const double gv[4] = {ga.x, ga.y, gb.x, gb.y};
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int i = i0 + r;
-                                float v = gT[it][r] * dv[r] * expc(gt - gv[r]);
-                                v = (i == t) ? v + Dh : v;
-                                m[4 * h2 + r] = (i <= t) ? v : 0.f;
-                            }
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) m[4 * h2 + r] = 0.f;
-                        }
-                    }
-                    uint4 mh4, ml4;
-                    split8(m, mh4, ml4);
-                    mh = as_bf16x8(mh4);
-                    ml = as_bf16x8(ml4);
-                };
-#pragma unroll
-                for (int kb = 0; kb <= TB / 2; ++kb) {
-                    bf16x8_t mhB, mlB, mhA, mlA;
-                    mslots(std::integral_constant<int, TB>{}, kb, gtB, cfB, tB, mhB, mlB);
-                    if (kb <= TA / 2) mslots(std::integral_constant<int, TA>{}, kb, gtA, cfA, tA, mhA, mlA);
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const int xo = (16 * pt + l16) * RS + 32 * xsw(kb, 16 * pt) + 8 * q;
-                        const bf16x8_t xh = as_bf16x8(lds128(Xh + xo));
-                        const bf16x8_t xl = as_bf16x8(lds128(Xl + xo));
-                        mma2<true, true>(yB[pt], xh, xl, mhB, mlB);
-                        if (kb <= TA / 2) mma2<true, true>(yA[pt], xh, xl, mhA, mlA);
-                    }
-                }
-                // store y rows tA, tB of the chunk: lane has y[t][16 pt + 4q .. +3]
-                if (tA < S) {
-                    float* dst = a.y + (r0 + tA) * a.ld_y + (int64_t)head * P + 4 * q;
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt)
-                        *reinterpret_cast<float4*>(dst + 16 * pt) = float4{yA[pt][0], yA[pt][1], yA[pt][2], yA[pt][3]};
-                }
-                if (tB < S) {
-                    float* dst = a.y + (r0 + tB) * a.ld_y + (int64_t)head * P + 4 * q;
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt)
-                        *reinterpret_cast<float4*>(dst + 16 * pt) = float4{yB[pt][0], yB[pt][1], yB[pt][2], yB[pt][3]};
+                if (j + 1 < j1) {
+                    stage((j - j0 + 1) & 1, j + 1);
+                    if (j + 2 < j1) prefetch(grp * hpg + j + 2);
                 }
                 __syncthreads();
             }
-        };
-        switch (wave) {
-            case 4: consumer(std::integral_constant<int, 0>{}); break;
-            case 5: consumer(std::integral_constant<int, 1>{}); break;
-            case 6: consumer(std::integral_constant<int, 2>{}); break;
-            default: consumer(std::integral_constant<int, 3>{}); break;
-        }
-    }
-
-    if (a.fuse_norm) {
-        // The grouped gated RMSNorm of this chunk's rows over this group's
-        // channels, wave w the rows w, w + 8, ..., read back while they are
-        // still in cache.  (The norm's barrier sits inside chunk_norm_rows.)
-        const int gs = hpg * P;
-        const int nbl = (gs / 8 + 63) / 64;
-        // (one block per lane: 16 rows per wave in flight, a chunk's 128 rows in
-        // one batch, as the norm is bound by the rows it has in flight; wider
-        // groups keep fewer rows for their registers: 6 rows at two blocks ran
-        // slower than 4)
-        if (a.out_dtype == kBF16) {
-            if (nbl == 1) chunk_norm_rows<uint16_t, 1, 16>(a, r0, S, grp * gs, gs, wave, lane);
-            else if (nbl == 2) chunk_norm_rows<uint16_t, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
-            else chunk_norm_rows<uint16_t, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
         } else {
-            if (nbl == 1) chunk_norm_rows<float, 1, 16>(a, r0, S, grp * gs, gs, wave, lane);
-            else if (nbl == 2) chunk_norm_rows<float, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
-            else chunk_norm_rows<float, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
+            // ---------------------------------------------------------- consumers
+            auto consumer = [&](auto TAc) __attribute__((always_inline)) {
+                constexpr int TA = decltype(TAc)::value;
+                constexpr int TB = 7 - TA;
+                // this lane's output rows.  Tiles past a short chunk's end are
+                // multiplied all the same (their rows are finite: B and C rows are
+                // clamped into the sequence, x rows and dt are 0 there) and not
+                // stored: the products stay free of branches.
+                const int tA = 16 * TA + l16, tB = 16 * TB + l16;
+                // C operands of the two tiles (column t, K = n), kept for every head
+                bf16x8_t chA[NKB], clA[NKB], chB[NKB], clB[NKB];
+                // G^T[i, t] = B_i . C_t for the i tiles it <= T of each tile
+                f32x4_t gtA[TA + 1], gtB[TB + 1];
+#pragma unroll
+                for (int it = 0; it <= TA; ++it) gtA[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int it = 0; it <= TB; ++it) gtB[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+                {
+                    uint4 graw[NPASS][RW];
+                    g_load(graw);
+                    __syncthreads();   // LDS tables
+#pragma unroll
+                    for (int ps = 0; ps < NPASS; ++ps) {
+                        if (ps > 0) __syncthreads();
+                        g_conv(ps, graw[ps]);
+                        __syncthreads();
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2) {
+                            const int k = 2 * ps + k2;
+                            chA[k] = as_bf16x8(lds128(Ch + tA * HR + 32 * k2 + 8 * q));
+                            clA[k] = as_bf16x8(lds128(Cl + tA * HR + 32 * k2 + 8 * q));
+                            chB[k] = as_bf16x8(lds128(Ch + tB * HR + 32 * k2 + 8 * q));
+                            clB[k] = as_bf16x8(lds128(Cl + tB * HR + 32 * k2 + 8 * q));
+#pragma unroll
+                            for (int it = 0; it <= TB; ++it) {
+                                const int row = (16 * it + l16) * HR + 32 * k2 + 8 * q;
+                                const bf16x8_t bh = as_bf16x8(lds128(Bh + row));
+                                const bf16x8_t bl = as_bf16x8(lds128(Bl + row));
+                                mma2<true, true>(gtB[it], bh, bl, chB[k], clB[k]);
+                                if (it <= TA) mma2<true, true>(gtA[it], bh, bl, chA[k], clA[k]);
+                            }
+                        }
+                    }
+                }
+                __syncthreads();   // the first head is staged
+
+                for (int j = j0; j < j1; ++j) {
+                    const int bf = (j - j0) & 1;
+                    const int head = grp * hpg + j;
+                    const float Dh = sD[j];
+                    const u16* Xh = smem + bf * HBUF;
+                    const u16* Xl = Xh + P * RS;
+                    const u16* HH = Xh + HX;
+                    const u16* HL = HH + P * NRS;
+                    const float* rowfb = rowf[bf];
+                    const float* dtsb = dts[bf];
+                    const double* gamb = gam[bf];
+                    // y^T[p, t] tiles: lane has t, p = 16 pt + 4q + r
+                    f32x4_t yA[4], yB[4];
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        yA[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        yB[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+                    // inter-chunk term: h_in C^T (A = h_in rows p, B = C columns t, K = n)
+#pragma unroll
+                    for (int k = 0; k < NKB; ++k) {
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt) {
+                            const bf16x8_t ah = as_bf16x8(lds128(HH + (16 * pt + l16) * NRS + 32 * k + 8 * q));
+                            const bf16x8_t al = as_bf16x8(lds128(HL + (16 * pt + l16) * NRS + 32 * k + 8 * q));
+                            mma2<true, true>(yA[pt], ah, al, chA[k], clA[k]);
+                            mma2<true, true>(yB[pt], ah, al, chB[k], clB[k]);
+                        }
+                    }
+                    {
+                        const float sa = din[bf][tA], sb = din[bf][tB];
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt) {
+                            yA[pt] *= sa;
+                            yB[pt] *= sb;
+                        }
+                    }
+                    // intra-chunk term: X^T M^T over i tile pairs (2kb, 2kb+1); the M^T
+                    // operand slot s < 4 is row 4q + s of tile 2kb, s >= 4 row 4q + s - 4
+                    // of tile 2kb + 1 (the rows this lane's accumulators hold); the x^T
+                    // planes hold the rows in that order (8 per (kb, q) group).
+                    float cfA[8], cfB[8];
+                    {
+                        const float4* ca = reinterpret_cast<const float4*>(colf[bf] + 8 * tA);
+                        const float4* cb = reinterpret_cast<const float4*>(colf[bf] + 8 * tB);
+                        const float4 a0 = ca[0], a1 = ca[1], b0 = cb[0], b1 = cb[1];
+                        cfA[0] = a0.x; cfA[1] = a0.y; cfA[2] = a0.z; cfA[3] = a0.w;
+                        cfA[4] = a1.x; cfA[5] = a1.y; cfA[6] = a1.z; cfA[7] = a1.w;
+                        cfB[0] = b0.x; cfB[1] = b0.y; cfB[2] = b0.z; cfB[3] = b0.w;
+                        cfB[4] = b1.x; cfB[5] = b1.y; cfB[6] = b1.z; cfB[7] = b1.w;
+                    }
+                    // M^T slots of tile TT (column t) for i tiles 2kb, 2kb + 1
+                    auto mslots = [&](auto TTc, int kb, const f32x4_t* gT, const float (&cfv)[8], int t,
+                                      bf16x8_t& mh, bf16x8_t& ml) __attribute__((always_inline)) {
+                        constexpr int TT = decltype(TTc)::value;
+                        float m[8];
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const int it = 2 * kb + h2;
+                            const int i0 = 16 * it + 4 * q;
+                            if (it < TT) {
+                                const float4 rf = *reinterpret_cast<const float4*>(rowfb + i0);
+                                const float cv = cfv[it];
+                                m[4 * h2 + 0] = gT[it][0] * rf.x * cv;
+                                m[4 * h2 + 1] = gT[it][1] * rf.y * cv;
+                                m[4 * h2 + 2] = gT[it][2] * rf.z * cv;
+                                m[4 * h2 + 3] = gT[it][3] * rf.w * cv;
+                            } else if (it == TT) {
+                                // the diagonal tile, branch-free: for i > t the clamped
+                                // exponent gives a finite factor that the select drops
+                                const double gt = gamb[t];
+                                const float4 d4 = *reinterpret_cast<const float4*>(dtsb + i0);
+                                const double2 ga = *reinterpret_cast<const double2*>(gamb + i0);
+                                const double2 gb = *reinterpret_cast<const double2*>(gamb + i0 + 2);
+                                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+                                const double gv[4] = {ga.x, ga.y, gb.x, gb.y};
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int i = i0 + r;
+                                    float v = gT[it][r] * dv[r] * expc(gt - gv[r]);
+                                    v = (i == t) ? v + Dh : v;
+                                    m[4 * h2 + r] = (i <= t) ? v : 0.f;
+                                }
+                            } else {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) m[4 * h2 + r] = 0.f;
+                            }
+                        }
+                        uint4 mh4, ml4;
+                        split8(m, mh4, ml4);
+                        mh = as_bf16x8(mh4);
+                        ml = as_bf16x8(ml4);
+                    };
+#pragma unroll
+                    for (int kb = 0; kb <= TB / 2; ++kb) {
+                        bf16x8_t mhB, mlB, mhA, mlA;
+                        mslots(std::integral_constant<int, TB>{}, kb, gtB, cfB, tB, mhB, mlB);
+                        if (kb <= TA / 2) mslots(std::integral_constant<int, TA>{}, kb, gtA, cfA, tA, mhA, mlA);
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt) {
+                            const int xo = (16 * pt + l16) * RS + 32 * xsw(kb, 16 * pt) + 8 * q;
+                            const bf16x8_t xh = as_bf16x8(lds128(Xh + xo));
+                            const bf16x8_t xl = as_bf16x8(lds128(Xl + xo));
+                            mma2<true, true>(yB[pt], xh, xl, mhB, mlB);
+                            if (kb <= TA / 2) mma2<true, true>(yA[pt], xh, xl, mhA, mlA);
+                        }
+                    }
+                    // store y rows tA, tB of the chunk: lane has y[t][16 pt + 4q .. +3]
+                    if (tA < S) {
+                        float* dst = a.y + (r0 + tA) * a.ld_y + (int64_t)head * P + 4 * q;
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt)
+                            *reinterpret_cast<float4*>(dst + 16 * pt) =
+                                float4{yA[pt][0], yA[pt][1], yA[pt][2], yA[pt][3]};
+                    }
+                    if (tB < S) {
+                        float* dst = a.y + (r0 + tB) * a.ld_y + (int64_t)head * P + 4 * q;
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt)
+                            *reinterpret_cast<float4*>(dst + 16 * pt) =
+                                float4{yB[pt][0], yB[pt][1], yB[pt][2], yB[pt][3]};
+                    }
+                    __syncthreads();
+                }
+            };
+            switch (wave) {
+                case 4: consumer(std::integral_constant<int, 0>{}); break;
+                case 5: consumer(std::integral_constant<int, 1>{}); break;
+                case 6: consumer(std::integral_constant<int, 2>{}); break;
+                default: consumer(std::integral_constant<int, 3>{}); break;
+            }
         }
+
+        if (a.fuse_norm) {
+            // The grouped gated RMSNorm of this chunk's rows over this group's
+            // channels, wave w the rows w, w + 8, ..., read back while they are
+            // still in cache.  (The norm's barrier sits inside chunk_norm_rows.)
+            const int gs = hpg * P;
+            const int nbl = (gs / 8 + 63) / 64;
+            // (one block per lane: 16 rows per wave in flight, a chunk's 128 rows in
+            // one batch, as the norm is bound by the rows it has in flight; wider
+            // groups keep fewer rows for their registers: 6 rows at two blocks ran
+            // slower than 4)
+            if (a.out_dtype == kBF16) {
+                if (nbl == 1) chunk_norm_rows<uint16_t, 1, 16>(a, r0, S, grp * gs, gs, wave, lane);
+                else if (nbl == 2) chunk_norm_rows<uint16_t, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
+                else chunk_norm_rows<uint16_t, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
+            } else {
+                if (nbl == 1) chunk_norm_rows<float, 1, 16>(a, r0, S, grp * gs, gs, wave, lane);
+                else if (nbl == 2) chunk_norm_rows<float, 2, 4>(a, r0, S, grp * gs, gs, wave, lane);
+                else chunk_norm_rows<float, 4, 2>(a, r0, S, grp * gs, gs, wave, lane);
+            }
+        }
+    };
+    if constexpr (N == 128) {
+        if (S_ == Q) body(std::integral_constant<int, Q>{});
+        else body(std::integral_constant<int, 0>{});
+    } else {
+        body(std::integral_constant<int, 0>{});   // (at dstate 64 the second copy spilled)
     }
 }
 
