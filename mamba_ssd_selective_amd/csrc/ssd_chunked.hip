@@ -1575,12 +1575,14 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
     if (c * Q >= L) return;
     const int S_ = (int)((L - c * Q) < Q ? (L - c * Q) : Q);
     // At dstate 128 the rest of the kernel is compiled twice: for a full chunk
-    // (every chunk but a sequence's last), with its row count a constant, so
-    // every row test and bound folds away (the copy also needs 29 fewer vector
-    // registers), and for a partial one.  The LDS arrays above serve both.
+    // that is not its sequence's first (every chunk but a sequence's first and
+    // last), with its row count a constant and no rows from the carried conv
+    // state, so every row test, bound and start-of-sequence path folds away,
+    // and for any chunk.  The LDS arrays above serve both.
     auto body = [&](auto sqc) __attribute__((always_inline)) {
         constexpr int SQ = decltype(sqc)::value;
         const int S = SQ ? SQ : S_;
+        const bool c0 = !SQ && c == 0;   // the sequence's first chunk
         const int64_t r0 = s0 + c * Q;
         const int slot = a.state_idx ? a.state_idx[seq] : seq;
         const bool init = a.has_init ? (a.has_init[seq] != 0) : true;
@@ -1626,7 +1628,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
         auto g_conv = [&](int ps, uint4 (&gr)[RW]) __attribute__((always_inline)) {
             raw_halo(gr, lane);
             const int row0 = 4 * g_rg;
-            const bool start = c == 0 && row0 == 0;
+            const bool start = c0 && row0 == 0;
             const int wi = (gIsB ? 0 : N) + 64 * ps + 8 * g_cg;
             const int ch0 = d_inner + (gIsB ? 0 : G * N) + grp * N + 64 * ps + 8 * g_cg;
             u16* const dh = gIsB ? Bh : Ch;
@@ -1735,7 +1737,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
                 {
                     raw_halo(xraw, lane);
                     const int row0 = 4 * x_rg;
-                    const bool start = c == 0 && row0 == 0;
+                    const bool start = c0 && row0 == 0;
                     const int pos = 8 * ((row0 >> 2) & 3) + 4 * ((row0 >> 4) & 1);
                     auto put = [&](int k, float (&u)[RR]) __attribute__((always_inline)) {
                         if (S < Q) {
@@ -2053,7 +2055,7 @@ __global__ __launch_bounds__(512) void ssd_chunk_out_raw_kernel(ScanArgs a) {
         }
     };
     if constexpr (N == 128) {
-        if (S_ == Q) body(std::integral_constant<int, Q>{});
+        if (S_ == Q && c > 0) body(std::integral_constant<int, Q>{});
         else body(std::integral_constant<int, 0>{});
     } else {
         body(std::integral_constant<int, 0>{});   // (at dstate 64 the second copy spilled)
