@@ -2136,17 +2136,20 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
 
     // One raw piece (4 rows x 8 channels, rows 4 rg .. of half h) of chunk c,
     // refilled a chunk ahead; and its conv + SiLU into the unit's LDS planes,
-    // times the rows' weights when wt is given (x) or not (B).
+    // times the rows' weights when wt is given (x) or not (B).  Only the
+    // workgroup's first unit can hold a sequence's first row: the staging
+    // calls after it pass first = false, which folds the carried-halo path
+    // (its loads, its 24 registers and the window's selects) out of the loop.
     const int rg = (lane & 7) + 8 * (wave & 1);   // row group of both roles' pieces
     auto load_piece = [&](RawBuf& b, const uint16_t* col, int64_t ld, int c, int h) __attribute__((always_inline)) {
         c = c < cend ? c : cend - 1;
         load_raw_piece(col + (s0 + (int64_t)c * Q) * ld, (int)ld, h * QH + 4 * rg, (int)(-(int64_t)c * Q),
                        (int)(L - 1 - (int64_t)c * Q), (lane & 7) == 0, b.r);
     };
-    auto conv_store = [&](RawBuf& b, int c, int h, int ch, int lw, const float* wt, u16* dh, u16* dl, int cg)
-        __attribute__((always_inline)) {
-        const int row0 = QH * h + 4 * rg;             // first row of the piece in the chunk
-        const bool start = c == 0 && row0 == 0;       // the piece starts the sequence
+    auto conv_store = [&](RawBuf& b, int c, int h, int ch, int lw, const float* wt, u16* dh, u16* dl, int cg,
+                          bool first) __attribute__((always_inline)) {
+        const int row0 = QH * h + 4 * rg;                    // first row of the piece in the chunk
+        const bool start = first && c == 0 && row0 == 0;    // the piece starts the sequence
         raw_halo(b.r, lane);
         float hv[3][8];
         if (start) load_halo(a.conv_state, a.conv_dim, slot, init, ch, hv);
@@ -2208,8 +2211,8 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
             lrun += gS;
             load_dt(c + 1);
         };
-        auto stage_x = [&](RawBuf& b, int c, int h) __attribute__((always_inline)) {
-            conv_store(b, c, h, xch, xlw, sW[wave], sXH[h][hp], sXL[h][hp], xcg);
+        auto stage_x = [&](RawBuf& b, int c, int h, bool first) __attribute__((always_inline)) {
+            conv_store(b, c, h, xch, xlw, sW[wave], sXH[h][hp], sXL[h][hp], xcg, first);
         };
 
         load_dt(cfirst);
@@ -2220,18 +2223,18 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();   // conv weights
         start_chunk(cfirst);
-        stage_x(bx0, cfirst, 0);
+        stage_x(bx0, cfirst, 0, true);
         load_piece(bx0, xcol, a.ld_x, cfirst + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();   // unit (cfirst, 0) staged
         for (int c = cfirst; c < cend; ++c) {
-            stage_x(bx1, c, 1);
+            stage_x(bx1, c, 1, false);
             load_piece(bx1, xcol, a.ld_x, c + 1, 1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();   // unit (c, 0) multiplied, (c, 1) staged
             if (c + 1 < cend) {
                 start_chunk(c + 1);
-                stage_x(bx0, c + 1, 0);
+                stage_x(bx0, c + 1, 0, false);
                 load_piece(bx0, xcol, a.ld_x, c + 2, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -2245,8 +2248,8 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
         const uint16_t* bcol = static_cast<const uint16_t*>(a.B) + grp * a.gs_B + 8 * bcg;
         const int bch = d_inner + grp * N + 8 * bcg, blw = IPW * P + 8 * bcg;
         RawBuf bb0, bb1;
-        auto stage_b = [&](RawBuf& b, int c, int h) __attribute__((always_inline)) {
-            conv_store(b, c, h, bch, blw, nullptr, sBTh[h], sBTl[h], bcg);
+        auto stage_b = [&](RawBuf& b, int c, int h, bool first) __attribute__((always_inline)) {
+            conv_store(b, c, h, bch, blw, nullptr, sBTh[h], sBTl[h], bcg, first);
         };
         // acc[hh][pt]: head hh, p tile pt; lane l has p = 32 pt + l % 32 and, in
         // registers 4m .. 4m + 3, n = 32 cw + 8m + 4 (l / 32) + 0..3
@@ -2293,7 +2296,7 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
             }
         };
         __syncthreads();   // conv weights
-        stage_b(bb0, cfirst, 0);
+        stage_b(bb0, cfirst, 0, true);
         load_piece(bb0, bcol, a.ld_B, cfirst + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();   // unit (cfirst, 0) staged
@@ -2321,14 +2324,14 @@ __global__ __launch_bounds__(512) void ssd_state_pass_raw_kernel(ScanArgs a) {
             }
             // unit (c, 0): its products beside the conv of (c, 1)'s B
             multiply(0);
-            stage_b(bb1, c, 1);
+            stage_b(bb1, c, 1, false);
             load_piece(bb1, bcol, a.ld_B, c + 1, 1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             // unit (c, 1): its products beside the conv of (c + 1, 0)'s B
             multiply(1);
             if (c + 1 < cend) {
-                stage_b(bb0, c + 1, 0);
+                stage_b(bb0, c + 1, 0, false);
                 load_piece(bb0, bcol, a.ld_B, c + 2, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
