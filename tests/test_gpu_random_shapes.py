@@ -49,7 +49,7 @@ def draw_case(seed):
     return act, LayerShape(nheads, headdim, dstate, ngroups), lens, init, nbg, y_dtype, r
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_shape_against_oracle(seed):
     act, shape, lens, init, nbg, y_dtype, r = draw_case(seed)
     print(f" act={act} shape={shape} lens={lens} init={init} nbg={nbg} y={y_dtype}", flush=True)
@@ -91,7 +91,7 @@ def draw_decode_case(seed):
     return act, LayerShape(ngroups * hpg, headdim, dstate, ngroups), batch, n_slots, nbg, y_dtype, r
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_decode_batch_against_oracle(seed):
     """mamba2_decode on a seeded random shape and batch (1 to 300 rows at
     permuted pool slots, some fresh), against the oracle's one-token prefill."""
